@@ -1,0 +1,60 @@
+"""Brute-force pair enumeration for tiny cases (n <= 64), pure Python.
+
+TEST INFRASTRUCTURE ONLY. Written independently of ``oracle.c``: every
+(i, j) pair is tested with the pages' own description of the pattern --
+nearby tokens always see each other (|i - j| <= w), far tokens only when they
+share a group, and never a later token (Korean page "Why Attend to
+Everything? Focus is the Key", technical summary §2.1; Japanese page "Focus:
+Learning Which Attention Pairs Matter", technical summary §2.1-§2.2) -- and
+the softmax is taken over exactly the kept pairs (exact softmax, §2.1 of the
+Korean page).
+"""
+import math
+
+
+def bf16_to_float(bits: int) -> float:
+    """Value of a bf16 bit pattern, decoded from sign, exponent and mantissa."""
+    sign = -1.0 if bits & 0x8000 else 1.0
+    exp = (bits >> 7) & 0xFF
+    man = bits & 0x7F
+    if exp == 0:
+        return sign * man * 2.0 ** (-133)          # subnormal: man/2^7 * 2^-126
+    if exp == 0xFF:
+        return sign * math.inf if man == 0 else math.nan
+    return sign * (1.0 + man / 128.0) * 2.0 ** (exp - 127)
+
+
+def keeps(i: int, j: int, w: int, gi: int, gj: int) -> bool:
+    if j > i:                      # causal
+        return False
+    near = abs(i - j) <= w         # local window, any group
+    return near or gi == gj        # far: same group only
+
+
+def attention(q, k, v, ids, w, scale):
+    """q: [Hq][n][d], k/v: [Hkv][n][d] nested lists of bf16 bit patterns
+    (one batch element); ids: [n]. Returns (out [Hq][n][d], weights [Hq][n][n])."""
+    Hq, Hkv = len(q), len(k)
+    n, d = len(q[0]), len(q[0][0])
+    share = Hq // Hkv
+    out, weights = [], []
+    for h in range(Hq):
+        kv = h // share
+        Kf = [[bf16_to_float(x) for x in row] for row in k[kv]]
+        Vf = [[bf16_to_float(x) for x in row] for row in v[kv]]
+        oh, wh = [], []
+        for i in range(n):
+            qi = [bf16_to_float(x) for x in q[h][i]]
+            scores = {}
+            for j in range(n):
+                if keeps(i, j, w, ids[i], ids[j]):
+                    scores[j] = scale * math.fsum(a * b for a, b in zip(qi, Kf[j]))
+            top = max(scores.values())
+            ex = {j: math.exp(s - top) for j, s in scores.items()}
+            tot = math.fsum(ex.values())
+            row_w = [ex.get(j, 0.0) / tot for j in range(n)]
+            oh.append([math.fsum(row_w[j] * Vf[j][c] for j in scores) for c in range(d)])
+            wh.append(row_w)
+        out.append(oh)
+        weights.append(wh)
+    return out, weights
