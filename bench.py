@@ -1,0 +1,245 @@
+"""Benchmark of the Focus forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--skip-cpu-baseline] [--skip-dense]
+
+One step = the whole hot path on one batch of seeded synthetic input already
+resident in HBM: focus_assign -> focus_group_sort -> focus_attn_long_range
+-> focus_attn_window_merge (the two passes of focus_attn_fwd), all through
+the C ABI on one stream. W untimed warm-up steps, then K timed steps between
+two device synchronisations. Per-kernel times come from HIP events recorded
+on the same stream around each call inside the timed loop.
+
+Prints ONE JSON line. value = visited-pair TFLOP/s of the whole step
+(4*d flops per allowed (query head, i, j) pair / step time). Also reported:
+attention-only TFLOP/s, the dense causal baseline (dense_causal_attn_fwd) and
+the speedups over it, the roofline of the dominant kernel, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Focus attn visited-pair TFLOP/s + speedup vs dense causal, n=32K, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="70b_gqa_n32768")
+    ap.add_argument("--dense-iters", type=int, default=5)
+    ap.add_argument("--skip-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-dense", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle attention sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(x, wl, target_s):
+    """The oracle as it stands, on the host cores: full assignment and group
+    sort, attention on a random row sample extrapolated per visited pair."""
+    import oracle
+    from group_gated_sparse_amd import metrics
+    cores = oracle.max_threads()
+    t0 = time.perf_counter()
+    ids, _ = oracle.assign(x["hidden"], x["P"], x["C"], x["bias"])
+    t_assign = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.group_sort(ids, wl.K)
+    t_sort = time.perf_counter() - t0
+    rng = np.random.default_rng(7)
+    total_rows = wl.B * wl.Hq * wl.n
+    rows_done = 0
+    pairs_done = 0
+    t_attn = 0.0
+    batch = 2048
+    while t_attn < target_s and rows_done < total_rows:
+        rows = rng.integers(0, total_rows, size=batch)
+        t0 = time.perf_counter()
+        _, _, vis = oracle.attn(x["q"], x["k"], x["v"], ids, wl.w, wl.softmax_scale, rows=rows)
+        t_attn += time.perf_counter() - t0
+        rows_done += batch
+        pairs_done += int(vis.sum())
+        if t_attn > 0:
+            batch = int(min(max(batch, batch * (target_s - t_attn) / t_attn), 262144))
+            batch = max(batch, 256)
+    win, lr = metrics.pair_counts(ids, wl.w)
+    pairs_all = (win + lr) * wl.Hq
+    t_attn_all = t_attn * pairs_all / max(pairs_done, 1)
+    step_s = t_assign + t_sort + t_attn_all
+    flops = metrics.attn_flops(win + lr, wl.Hq, wl.d)
+    return {
+        "value": flops / step_s / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"full fp32 assignment ({wl.B * wl.n} tokens, {t_assign:.2f} s) and group sort "
+                   f"({t_sort:.3f} s); fp64 attention on {rows_done} random query rows "
+                   f"({pairs_done} visited pairs, {t_attn:.2f} s) extrapolated per visited pair "
+                   f"to all {pairs_all} pairs ({t_attn_all:.1f} s); step estimate {step_s:.1f} s"),
+        "step_s": step_s,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the design notes describe how the work would shard). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from group_gated_sparse_amd import focus, metrics, synth, workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = workloads.BY_NAME[args.workload]
+    log(f"workload {wl.name}: generating seeded inputs")
+    t0 = time.perf_counter()
+    x = synth.make_inputs(wl)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f} s; uploading")
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    hidden, P, C = dev(x["hidden"]), dev(x["P"]), dev(x["C"])
+    bias = None if x["bias"] is None else dev(x["bias"])
+    q, k, v = dev16(x["q"]), dev16(x["k"]), dev16(x["v"])
+    B, n, K, w, d, Hq, Hkv = wl.B, wl.n, wl.K, wl.w, wl.d, wl.Hq, wl.Hkv
+    scale = wl.softmax_scale
+    dv = q.device
+    ids = torch.empty((B, n), dtype=torch.int32, device=dv)
+    perm = torch.empty((B, n), dtype=torch.int32, device=dv)
+    offs = torch.empty((B, K + 1), dtype=torch.int32, device=dv)
+    out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=dv)
+    ws_a = torch.empty(focus.focus_assign_workspace_bytes(wl.d_model, K), dtype=torch.uint8,
+                       device=dv)
+    ws_n = focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w)
+    ws_t = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dv)
+    stream = torch.cuda.current_stream()
+
+    names = ["assign", "sort", "long_range", "window_merge"]
+
+    def step(evs=None):
+        def mark(i):
+            if evs is not None:
+                evs[i].record(stream)
+        mark(0)
+        focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False, workspace=ws_a)
+        mark(1)
+        focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs)
+        mark(2)
+        focus.focus_attn_long_range(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t, out=out)
+        mark(3)
+        focus.focus_attn_window_merge(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t,
+                                      out=out)
+        mark(4)
+
+    log(f"warm-up {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    phase = {nm: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+             for i, nm in enumerate(names)}
+    ev_step = float(np.mean([evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps)]))
+    ms_step = max(wall_ms, ev_step)
+    log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
+
+    gids = ids.cpu().numpy()
+    win, lr = metrics.pair_counts(gids, w)
+    pairs = win + lr
+    flops = metrics.attn_flops(pairs, Hq, d)
+    attn_ms = phase["long_range"] + phase["window_merge"]
+    res = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "n": n, "d_head": d,
+                   "d_model": wl.d_model, "d_proj": wl.d_proj, "K": K, "window": w,
+                   "out_dtype": "bf16"},
+        "visited_pairs_per_head": pairs,
+        "window_pairs_per_head": win,
+        "long_range_pairs_per_head": lr,
+        "phase_ms": phase,
+        "attn_ms": attn_ms,
+        "attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
+        "attn_frac_of_bf16_peak": flops / (attn_ms * 1e-3) / 1e12 / metrics.MI355X_BF16_DENSE_TFLOPS,
+        "assign_GBps": (B * n * wl.d_model * 4) / (phase["assign"] * 1e-3) / 1e9,
+    }
+
+    # The dominant kernel of the step and its roofline (bf16 MFMA bound).
+    kern = max(("long_range", "window_merge"), key=lambda nm: phase[nm])
+    kflops = metrics.attn_flops(lr if kern == "long_range" else win, Hq, d)
+    ach = kflops / (phase[kern] * 1e-3) / 1e12
+    res["roofline"] = {"kernel": "attn_kernel<128,1> (long-range pass)" if kern == "long_range"
+                       else "attn_kernel<128,0> (window pass + merge)",
+                       "bound": "mfma", "achieved": ach,
+                       "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                       "frac": ach / metrics.MI355X_BF16_DENSE_TFLOPS, "traffic": None,
+                       "flops_per_launch": kflops, "avg_launch_ms": phase[kern]}
+
+    if not args.skip_dense:
+        log(f"dense causal baseline x{args.dense_iters}")
+        focus.dense_causal_attn_fwd(q, k, v, scale, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.dense_iters):
+            focus.dense_causal_attn_fwd(q, k, v, scale, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_iters
+        dflops = metrics.attn_flops(B * (n * (n + 1) // 2), Hq, d)
+        res["dense_ms"] = dense_ms
+        res["dense_tflops"] = dflops / (dense_ms * 1e-3) / 1e12
+        res["speedup_attn_vs_dense"] = dense_ms / attn_ms
+        res["speedup_step_vs_dense"] = dense_ms / ms_step
+        log(f"dense {dense_ms:.3f} ms ({res['dense_tflops']:.1f} TFLOP/s)")
+
+    del hidden, q, k, v, out, ws_t
+    torch.cuda.empty_cache()
+    if not args.skip_cpu_baseline:
+        log("CPU oracle baseline")
+        res["cpu_baseline"] = cpu_baseline(x, wl, args.cpu_seconds)
+        log(f"cpu baseline {res['cpu_baseline']['value']:.3e} TFLOP/s")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

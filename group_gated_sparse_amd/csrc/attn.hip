@@ -1,0 +1,460 @@
+// Exact-softmax attention over the Focus pattern, and the dense causal
+// baseline, as bf16 MFMA flash-style kernels for gfx950.
+//
+// The pattern (Korean page "Why Attend to Everything? Focus is the Key",
+// technical summary §2.1 and §2.3; Japanese page "Focus: Learning Which
+// Attention Pairs Matter", §2.1-§2.2): row i keeps every key of the causal
+// window 0 <= i-j <= w, and beyond the window only keys of its own group;
+// the softmax is exact over the kept keys. The Korean page §2.3 splits the
+// work into a local-window attention and an intra-group long-range
+// attention; here those are two kernels joined by a log-sum-exp merge:
+//
+//   long-range pass (group-sorted order): for each tile of 128//G sorted
+//     tokens x G query heads that share one kv head, visit only the key
+//     tiles of the groups present in the tile, and inside a group only keys
+//     whose position is below (largest query position) - w. Keys are
+//     gathered through perm, so every visited tile is dense in one group.
+//     Writes the normalised partial output and its log2-sum-exp per row.
+//   window pass (sequence order): for each tile of tokens, the key band
+//     [q0 - w, q0 + TT - 1]; its epilogue merges the long-range partial.
+//   dense causal: the window pass with the band widened to [0, q0 + TT - 1].
+//
+// The two key sets {i-j <= w} and {i-j > w, same group} are disjoint, so
+// every allowed pair is counted exactly once.
+//
+// Per workgroup: 4 waves x 32 query rows. Per 64-key tile:
+//   S^T (keys x rows) = K Q^T   : A = K from LDS, B = Q^T held in registers
+//   online softmax per row in registers (one row per lane pair, exp2 domain)
+//   O^T (d x rows)  += V^T P^T  : A = V^T via LDS transposing reads
+//                                 (ds_read_b64_tr_b16), B = P^T in registers
+// with v_mfma_f32_32x32x16_bf16 and fp32 accumulation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "focus_internal.h"
+
+namespace focus {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BN = 64;      // keys per tile
+constexpr int NT = 256;     // threads per workgroup
+constexpr int ROWS = 128;   // query rows per workgroup (4 waves x 32)
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.69314718055994530942f;
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* ids;
+    const int32_t* perm;
+    const int32_t* offsets;
+    float* og;     // long-range partial output [B][Hq][n][D] (normalised)
+    float* lseg;   // long-range partial log2-sum-exp [B][Hq][n] (-inf: no key)
+    void* out;
+    float* lse;
+    int B, Hq, Hkv, n, K, w;
+    int hpk;       // Hq / Hkv
+    int G;         // query heads packed per workgroup
+    int TT;        // tokens per workgroup tile (ROWS / G)
+    int nslices;   // hpk / G
+    int ntiles;    // ceil(n / TT)
+    int total;     // workgroups
+    float sl2;     // scale * log2(e)
+    int out_f32;
+    int merge;
+    int dense;
+};
+
+template <int D>
+struct Geom {
+    static constexpr int NCH = D / 8;                    // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;                   // bytes per row
+    static constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;  // rows per 256-byte bank line
+    static constexpr int TILEB = BN * ROWB;
+    static constexpr int KS = D / 16;                    // k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;                    // 32-wide blocks of O^T
+};
+
+// Byte offset of 16-byte chunk `ch` of tile row `row` in LDS. The chunk index
+// is XOR-swizzled per 256-byte bank line so that (a) 16 consecutive rows
+// reading the same logical chunk (the K operand) land on 16 distinct chunk
+// slots, and (b) the 4 rows x 2 chunks of a transposing V read are distinct.
+template <int D>
+__device__ __forceinline__ int lds_off(int row, int ch) {
+    constexpr int NCH = Geom<D>::NCH, RPL = Geom<D>::RPL;
+    const int u = row / RPL;
+    const int f = ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
+    return row * Geom<D>::ROWB + ((ch ^ f) << 4);
+}
+
+__device__ __forceinline__ float other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
+// works through one contiguous range of work items (neighbouring tiles of one
+// head share keys in that XCD's L2).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+    const int per = total / 8, rem = total % 8;
+    const int x = bid % 8, local = bid / 8;
+    return x * per + (x < rem ? x : rem) + local;
+}
+
+template <int D, int PHASE>  // PHASE 0: window / dense (sequence order); 1: long-range (sorted)
+__global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
+    using G = Geom<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * G::TILEB];
+    __shared__ int kpos_s[BN];
+    unsigned char* Ks = smem;
+    unsigned char* Vs = smem + G::TILEB;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rl = lane & 31, hh = lane >> 5;
+
+    const int L = xcd_remap(blockIdx.x, a.total);
+    int tile = L % a.ntiles;
+    int rest = L / a.ntiles;
+    const int slice = rest % a.nslices;
+    rest /= a.nslices;
+    const int kvh = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    if (PHASE == 1) tile = a.ntiles - 1 - tile;  // heavier sorted tiles first
+
+    const int R = wave * 32 + rl;
+    const int hslot = R / a.TT, tok = R % a.TT;
+    const int h = kvh * a.hpk + slice * a.G + hslot;
+    const int64_t bn = (int64_t)b * a.n;
+    const int s_row = tile * a.TT + tok;
+    const bool rvalid = s_row < a.n;
+    int pos_i = rvalid ? s_row : 0;
+    int g_i = 0;
+    if (PHASE == 1 && rvalid) {
+        pos_i = clampi(a.perm[bn + s_row], 0, a.n - 1);
+        g_i = clampi(a.ids[bn + pos_i], 0, a.K - 1);
+    }
+
+    // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
+    const int64_t qrow_off = (((int64_t)b * a.Hq + h) * a.n + pos_i) * D;
+    bf16x8 qf[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        if (rvalid) {
+            qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qrow_off + 16 * ks + 8 * hh);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) qf[ks][t] = (__bf16)0.0f;
+        }
+    }
+
+    f32x16 acc[G::DB];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
+    float m_run = kNegInf, l_run = 0.0f;
+
+    const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * a.n * D;
+    const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * a.n * D;
+
+    // One 64-key tile: keys kt0 .. kt0+63 (sequence positions in PHASE 0,
+    // sorted slots in PHASE 1); keys at or beyond kend are padding.
+    auto do_tile = [&](int kt0, int kend, bool full, int seg_g) {
+        __syncthreads();
+        if (PHASE == 1) {
+            if (tid < BN) {
+                const int s = kt0 + tid;
+                kpos_s[tid] = (s < kend) ? clampi(a.perm[bn + s], 0, a.n - 1) : -1;
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int it = 0; it < BN * G::NCH / NT; ++it) {
+            const int idx = it * NT + tid;
+            const int row = idx / G::NCH, ch = idx % G::NCH;
+            const int key = kt0 + row;
+            u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+            if (key < kend) {
+                const int pos = (PHASE == 0) ? key : kpos_s[row];
+                kx = *reinterpret_cast<const u32x4*>(kbase + (int64_t)pos * D + ch * 8);
+                vx = *reinterpret_cast<const u32x4*>(vbase + (int64_t)pos * D + ch * 8);
+            }
+            *reinterpret_cast<u32x4*>(Ks + lds_off<D>(row, ch)) = kx;
+            *reinterpret_cast<u32x4*>(Vs + lds_off<D>(row, ch)) = vx;
+        }
+        __syncthreads();
+
+        // S^T = K Q^T for two 32-key blocks.
+        f32x16 st[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < G::KS; ++ks) {
+                const bf16x8 kf =
+                    *reinterpret_cast<const bf16x8*>(Ks + lds_off<D>(kb * 32 + rl, 2 * ks + hh));
+                st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[kb], 0, 0, 0);
+            }
+        }
+
+        // Mask: lane holds keys kidx = kb*32 + 8*(e>>2) + 4*hh + (e&3) of its row.
+        if (!full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int kidx = kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    const int key = kt0 + kidx;
+                    bool ok;
+                    if (PHASE == 0) {
+                        ok = key < kend && key <= pos_i && pos_i - key <= a.w;
+                    } else {
+                        const int pj = kpos_s[kidx];
+                        ok = rvalid && g_i == seg_g && key < kend && pos_i - pj > a.w;
+                    }
+                    if (!ok) st[kb][e] = kNegInf;
+                }
+        }
+
+        float tmax = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, st[kb][e]);
+        tmax = fmaxf(tmax, other_half(tmax));
+        const float m_new = fmaxf(m_run, tmax * a.sl2);
+        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float psum = 0.0f;
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
+                psum += p;
+                pf[kb][e >> 3][e & 7] = (__bf16)p;
+            }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+
+        // O^T += V^T P^T. For k-step (kb, sp) the B slots 0..3 / 4..7 of lane
+        // half hh hold keys kb*32+16*sp+4*hh+{0..3} / +8+{0..3}; the A operand
+        // gets the same keys through two transposing reads, lane m of each
+        // 16-lane group addressing row key0 + m/4, columns 4*(m%4) .. +3 of
+        // its 16-column half.
+        const int m16 = lane & 15;
+        const int colbase = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) {
+                const int key0 = kb * 32 + 16 * sp + 4 * hh + (m16 >> 2);
+#pragma unroll
+                for (int db = 0; db < G::DB; ++db) {
+                    const int col = db * 32 + colbase;
+                    const int o1 = lds_off<D>(key0, col >> 3) + (col & 7) * 2;
+                    const int o2 = lds_off<D>(key0 + 8, col >> 3) + (col & 7) * 2;
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(Vs + o1));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4*)(Vs + o2));
+                    const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][sp], acc[db], 0, 0, 0);
+                }
+            }
+    };
+
+    if (PHASE == 0) {
+        const int q0 = tile * a.TT;
+        const int qlast = min(a.n, q0 + a.TT) - 1;
+        const int kstart = a.dense ? 0 : max(0, q0 - a.w);
+        const int kend = qlast + 1;
+        for (int kt0 = kstart; kt0 < kend; kt0 += BN) {
+            const bool full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
+                              (a.dense || qlast - kt0 <= a.w);
+            do_tile(kt0, kend, full, 0);
+        }
+    } else {
+        const int s0 = tile * a.TT;
+        const int s1 = min(a.n, s0 + a.TT);
+        const int* offb = a.offsets + (int64_t)b * (a.K + 1);
+        const int gf = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
+        const int gl = clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], 0, a.K - 1);
+        for (int g = gf; g <= gl; ++g) {
+            const int ob = clampi(offb[g], 0, a.n);
+            const int oe = clampi(offb[g + 1], ob, a.n);
+            const int qlo = max(s0, ob), qhi = min(s1, oe);
+            if (qlo >= qhi) continue;
+            const int maxpos = clampi(a.perm[bn + qhi - 1], 0, a.n - 1);
+            const int minpos = clampi(a.perm[bn + qlo], 0, a.n - 1);
+            // first slot in [ob, qhi) whose position is >= maxpos - w
+            int lo = ob, hi = qhi;
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (a.perm[bn + mid] < maxpos - a.w) lo = mid + 1; else hi = mid;
+            }
+            const int kend = lo;
+            const bool rows_one_group = (s0 >= ob) && (s1 <= oe);
+            for (int kt0 = ob; kt0 < kend; kt0 += BN) {
+                bool full = false;
+                if (rows_one_group && kt0 + BN <= kend) {
+                    const int last_pos = a.perm[bn + kt0 + BN - 1];
+                    full = (minpos - last_pos > a.w);
+                }
+                do_tile(kt0, kend, full, g);
+            }
+        }
+    }
+
+    // Epilogue. Lane holds rows' O^T entries d = db*32 + 8*i + 4*hh + j at
+    // acc[db][4*i + j]; l_run covers this lane half's keys.
+    const float l_tot = l_run + other_half(l_run);
+    const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
+    if (PHASE == 1) {
+        if (!rvalid) return;
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        float* orow = a.og + row * D;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 o = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv,
+                           acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv};
+                *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i + 4 * hh) = o;
+            }
+        if (hh == 0) a.lseg[row] = l_tot > 0.0f ? m_run + __log2f(l_tot) : kNegInf;
+    } else {
+        if (!rvalid) return;
+        float lse2 = m_run + __log2f(l_tot);
+        float cw = 1.0f / l_tot, cg = 0.0f;
+        const float* grow = nullptr;
+        if (a.merge) {
+            const float lg = a.lseg[row];
+            const float M = fmaxf(lse2, lg);
+            const float aw = __builtin_amdgcn_exp2f(lse2 - M);
+            const float ag = __builtin_amdgcn_exp2f(lg - M);
+            const float den = aw + ag;
+            cw = aw / (den * l_tot);
+            cg = ag / den;
+            lse2 = M + __log2f(den);
+            grow = a.og + row * D;
+        }
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d0 = db * 32 + 8 * i + 4 * hh;
+                f32x4 o = {acc[db][4 * i] * cw, acc[db][4 * i + 1] * cw, acc[db][4 * i + 2] * cw,
+                           acc[db][4 * i + 3] * cw};
+                if (grow) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(grow + d0);
+                    o[0] = __builtin_fmaf(gv[0], cg, o[0]);
+                    o[1] = __builtin_fmaf(gv[1], cg, o[1]);
+                    o[2] = __builtin_fmaf(gv[2], cg, o[2]);
+                    o[3] = __builtin_fmaf(gv[3], cg, o[3]);
+                }
+                if (a.out_f32) {
+                    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = o;
+                } else {
+                    const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + row * D + d0) = ob;
+                }
+            }
+        if (hh == 0 && a.lse) a.lse[row] = lse2 * kLn2;
+    }
+}
+
+// Query heads packed into one workgroup: the largest power of two <= 8 that
+// divides Hq/Hkv. All packed heads share the kv head, the token set and the
+// mask, so each K/V tile staged in LDS serves G*TT = 128 query rows.
+int heads_per_wg(int hpk) {
+    int g = 1;
+    while (g < 8 && hpk % (2 * g) == 0) g *= 2;
+    return g;
+}
+
+AttnArgs make_args(const AttnProblem& p) {
+    AttnArgs a{};
+    a.q = p.q;
+    a.k = p.k;
+    a.v = p.v;
+    a.ids = p.ids;
+    a.perm = p.perm;
+    a.offsets = p.offsets;
+    a.out = p.out;
+    a.lse = p.lse;
+    a.B = p.B;
+    a.Hq = p.Hq;
+    a.Hkv = p.Hkv;
+    a.n = p.n;
+    a.K = p.K;
+    a.w = p.w;
+    a.hpk = p.Hq / p.Hkv;
+    a.G = heads_per_wg(a.hpk);
+    a.TT = ROWS / a.G;
+    a.nslices = a.hpk / a.G;
+    a.ntiles = (p.n + a.TT - 1) / a.TT;
+    a.total = p.B * p.Hkv * a.nslices * a.ntiles;
+    a.sl2 = p.scale * 1.44269504088896340736f;
+    a.out_f32 = p.out_f32;
+    if (p.workspace) {
+        a.og = static_cast<float*>(p.workspace);
+        a.lseg = reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
+                                          align_up((size_t)p.B * p.Hq * p.n * p.d * 4));
+    }
+    return a;
+}
+
+template <int PHASE>
+hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
+    const dim3 grid((unsigned)a.total), block(NT);
+    switch (d) {
+        case 32: hipLaunchKernelGGL((attn_kernel<32, PHASE>), grid, block, 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((attn_kernel<64, PHASE>), grid, block, 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((attn_kernel<128, PHASE>), grid, block, 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
+    if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
+    AttnArgs a = make_args(p);
+    return launch<1>(a, p.d, stream);
+}
+
+hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream) {
+    AttnArgs a = make_args(p);
+    a.merge = merge && attn_has_long_range(p.n, p.w) ? 1 : 0;
+    return launch<0>(a, p.d, stream);
+}
+
+hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream) {
+    AttnArgs a = make_args(p);
+    a.dense = 1;
+    a.merge = 0;
+    a.w = p.n;
+    return launch<0>(a, p.d, stream);
+}
+
+}  // namespace focus

@@ -1,0 +1,55 @@
+// Internal launch interface between the C ABI (api.cpp) and the HIP kernels.
+// Every launcher assumes its arguments were validated by the ABI layer and
+// returns the hipError_t of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace focus {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// ---- assignment -----------------------------------------------------------
+// Padded row length of the split W^T = (P C^T)^T tables: a multiple of 64.
+inline int assign_dpad(int d_model) { return (d_model + 63) / 64 * 64; }
+inline int assign_kpad(int K) { return K <= 32 ? 32 : 64; }
+inline size_t assign_workspace(int d_model, int K) {
+    return 2 * align_up((size_t)assign_kpad(K) * assign_dpad(d_model) * 2);
+}
+hipError_t launch_assign(const float* hidden, const float* P, const float* C, const float* bias,
+                         int B, int n, int d_model, int d_proj, int K, int32_t* ids,
+                         float* margin, void* workspace, hipStream_t stream);
+
+// ---- grouping ---------------------------------------------------------------
+hipError_t launch_group_sort(const int32_t* ids, int B, int n, int K, int32_t* perm,
+                             int32_t* offsets, hipStream_t stream);
+
+// ---- attention --------------------------------------------------------------
+struct AttnProblem {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* ids;
+    const int32_t* perm;
+    const int32_t* offsets;
+    int B, Hq, Hkv, n, d, K, w;
+    float scale;
+    void* out;
+    int out_f32;
+    float* lse;
+    void* workspace;
+};
+
+// True when some pair further apart than the window can exist (n - 1 > w).
+inline bool attn_has_long_range(int n, int w) { return (int64_t)n - 1 > (int64_t)w; }
+inline size_t attn_workspace(int B, int Hq, int n, int d, int w) {
+    if (!attn_has_long_range(n, w)) return 0;
+    return align_up((size_t)B * Hq * n * d * 4) + align_up((size_t)B * Hq * n * 4);
+}
+hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
+hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream);
+hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream);
+
+}  // namespace focus

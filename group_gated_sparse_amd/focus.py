@@ -1,0 +1,255 @@
+"""Thin ctypes binding of libfocus.so (C ABI in include/focus.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, turned into device pointers, and passed with the current HIP
+stream. Every step of the computation runs in the library's HIP kernels; a
+missing library raises instead of falling back to anything else.
+
+q, k, v are torch.bfloat16 CUDA tensors (their bits are the ABI's uint16).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfocus.so")
+
+FOCUS_OK = 0
+FOCUS_BF16 = 0
+FOCUS_F32 = 1
+STATUS_NAMES = {0: "FOCUS_OK", 1: "FOCUS_ERR_INVALID_ARGUMENT", 2: "FOCUS_ERR_UNSUPPORTED",
+                3: "FOCUS_ERR_WORKSPACE", 4: "FOCUS_ERR_DEVICE"}
+
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_sz = ctypes.c_size_t
+_f = ctypes.c_float
+
+_SIGNATURES = {
+    "focus_abi_version": ([], _i),
+    "focus_last_error": ([], ctypes.c_char_p),
+    "focus_assign_workspace_bytes": ([_i, _i], _sz),
+    "focus_assign": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
+    "focus_group_sort_workspace_bytes": ([_i, _i, _i], _sz),
+    "focus_group_sort": ([_p, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
+    "focus_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+    "focus_attn_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p,
+                        _sz, _p], _i),
+    "focus_attn_long_range": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
+                               _p, _p, _sz, _p], _i),
+    "focus_attn_window_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
+                                 _i, _p, _p, _sz, _p], _i),
+    "dense_causal_attn_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p], _i),
+}
+
+_lib = None
+
+
+class FocusError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def lib():
+    """The loaded libfocus.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m group_gated_sparse_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def _check_status(status: int):
+    if status != FOCUS_OK:
+        raise FocusError(status, lib().focus_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+    if nbytes == 0:
+        return given
+    if given is not None:
+        _need(given, "workspace", torch.uint8)
+        return given
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def focus_assign_workspace_bytes(d_model: int, K: int) -> int:
+    return int(lib().focus_assign_workspace_bytes(d_model, K))
+
+
+def focus_assign(hidden: torch.Tensor, P: torch.Tensor, C: torch.Tensor,
+                 bias: Optional[torch.Tensor] = None, *, group_ids=None, margin=None,
+                 want_margin: bool = True, workspace=None, stream=None
+                 ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Group id per token: argmax_k (h P) C_k^T + bias_k. hidden (B, n, d_model) fp32."""
+    B, n, d_model = hidden.shape
+    d_proj = P.shape[1]
+    K = C.shape[0]
+    _need(hidden, "hidden", torch.float32)
+    _need(P, "P", torch.float32, (d_model, d_proj))
+    _need(C, "C", torch.float32, (K, d_proj))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (K,))
+    dev = hidden.device
+    if group_ids is None:
+        group_ids = torch.empty((B, n), dtype=torch.int32, device=dev)
+    _need(group_ids, "group_ids", torch.int32, (B, n))
+    if margin is None and want_margin:
+        margin = torch.empty((B, n), dtype=torch.float32, device=dev)
+    if margin is not None:
+        _need(margin, "margin", torch.float32, (B, n))
+    nbytes = focus_assign_workspace_bytes(d_model, K)
+    ws = _workspace(nbytes, dev, workspace)
+    _check_status(lib().focus_assign(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n, d_model,
+                                     d_proj, K, _ptr(group_ids), _ptr(margin), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream)))
+    return group_ids, margin
+
+
+def focus_group_sort_workspace_bytes(B: int, n: int, K: int) -> int:
+    return int(lib().focus_group_sort_workspace_bytes(B, n, K))
+
+
+def focus_group_sort(group_ids: torch.Tensor, K: int, *, perm=None, group_offsets=None,
+                     workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Stable grouping: (perm (B, n) sorted slot -> position, group_offsets (B, K+1))."""
+    B, n = group_ids.shape
+    _need(group_ids, "group_ids", torch.int32)
+    dev = group_ids.device
+    if perm is None:
+        perm = torch.empty((B, n), dtype=torch.int32, device=dev)
+    if group_offsets is None:
+        group_offsets = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    _need(perm, "perm", torch.int32, (B, n))
+    _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
+    nbytes = focus_group_sort_workspace_bytes(B, n, K)
+    ws = _workspace(nbytes, dev, workspace)
+    _check_status(lib().focus_group_sort(_ptr(group_ids), B, n, K, _ptr(perm),
+                                         _ptr(group_offsets), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _stream(stream)))
+    return perm, group_offsets
+
+
+def focus_attn_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K: int,
+                               window: int) -> int:
+    return int(lib().focus_attn_workspace_bytes(B, Hq, Hkv, n, d_head, K, window))
+
+
+def _attn_call(fn_name, q, k, v, group_ids, perm, group_offsets, K, window, scale, out,
+               out_dtype, lse, want_lse, workspace, stream):
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, Hkv, n, d))
+    _need(v, "v", torch.bfloat16, (B, Hkv, n, d))
+    _need(group_ids, "group_ids", torch.int32, (B, n))
+    _need(perm, "perm", torch.int32, (B, n))
+    _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
+    if out is None:
+        out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _need(out, "out", out.dtype, (B, Hq, n, d))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, n))
+    nbytes = focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, window)
+    ws = _workspace(nbytes, q.device, workspace)
+    dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
+    fn = getattr(lib(), fn_name)
+    _check_status(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(group_ids), _ptr(perm), _ptr(group_offsets),
+                     B, Hq, Hkv, n, d, K, window, float(scale), _ptr(out), dt, _ptr(lse),
+                     _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return out, lse, ws
+
+
+def focus_attn_fwd(q, k, v, group_ids, perm, group_offsets, K: int, window: int, scale: float,
+                   *, out=None, out_dtype=torch.bfloat16, lse=None, want_lse: bool = False,
+                   workspace=None, stream=None):
+    """Focus attention over the local window plus same-group long-range pairs.
+    Returns (out, lse or None)."""
+    out, lse, _ = _attn_call("focus_attn_fwd", q, k, v, group_ids, perm, group_offsets, K,
+                             window, scale, out, out_dtype, lse, want_lse, workspace, stream)
+    return out, lse
+
+
+def focus_attn_long_range(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
+                          scale: float, *, workspace, out=None, out_dtype=torch.bfloat16,
+                          lse=None, want_lse: bool = False, stream=None):
+    """First pass of focus_attn_fwd (writes the long-range partial into workspace)."""
+    return _attn_call("focus_attn_long_range", q, k, v, group_ids, perm, group_offsets, K,
+                      window, scale, out, out_dtype, lse, want_lse, workspace, stream)
+
+
+def focus_attn_window_merge(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
+                            scale: float, *, workspace, out=None, out_dtype=torch.bfloat16,
+                            lse=None, want_lse: bool = False, stream=None):
+    """Second pass of focus_attn_fwd (window attention + merge with the partial)."""
+    return _attn_call("focus_attn_window_merge", q, k, v, group_ids, perm, group_offsets, K,
+                      window, scale, out, out_dtype, lse, want_lse, workspace, stream)
+
+
+def dense_causal_attn_fwd(q, k, v, scale: float, *, out=None, out_dtype=torch.bfloat16,
+                          lse=None, want_lse: bool = False, stream=None):
+    """Plain causal attention baseline. Returns (out, lse or None)."""
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, Hkv, n, d))
+    _need(v, "v", torch.bfloat16, (B, Hkv, n, d))
+    if out is None:
+        out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
+    _need(out, "out", out.dtype, (B, Hq, n, d))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, n))
+    dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
+    _check_status(lib().dense_causal_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, n, d,
+                                              float(scale), _ptr(out), dt, _ptr(lse),
+                                              _stream(stream)))
+    return out, lse
+
+
+def focus_forward(hidden, P, C, bias, q, k, v, window: int, scale: float, *,
+                  out_dtype=torch.bfloat16, want_lse: bool = False, stream=None):
+    """The whole forward pass: assign -> group sort -> attention."""
+    K = C.shape[0]
+    ids, _ = focus_assign(hidden, P, C, bias, want_margin=False, stream=stream)
+    perm, offs = focus_group_sort(ids, K, stream=stream)
+    out, lse = focus_attn_fwd(q, k, v, ids, perm, offs, K, window, scale, out_dtype=out_dtype,
+                              want_lse=want_lse, stream=stream)
+    return out, lse, ids, perm, offs

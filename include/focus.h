@@ -1,0 +1,167 @@
+/*
+ * focus.h -- C ABI of libfocus.so: the Focus group-gated attention forward
+ * pass on AMD Instinct MI355X (gfx950).
+ *
+ * The method (Focus; pages "Why Attend to Everything? Focus is the Key",
+ * Korean technical summary §2.1-§2.3, and "Focus: Learning Which Attention
+ * Pairs Matter", Japanese technical summary §2.1-§2.2): every token is given
+ * one of K groups by comparing its projected hidden state with K learned
+ * centroids; attention then keeps the local window at full resolution and,
+ * beyond it, only pairs whose tokens share a group, with the exact softmax
+ * over the kept pairs. Inference uses a hard assignment, so dropped pairs
+ * are skipped rather than zeroed.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), contiguous, row-major in the layout stated, and 16-byte
+ *     aligned unless stated otherwise. The caller owns every buffer; the
+ *     library never allocates or frees device memory and keeps no pointer
+ *     after the call returns.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; buffers must stay valid until the
+ *     stream has passed the call. No call synchronises the host.
+ *   - Arguments are validated on the host before anything is enqueued: on a
+ *     non-OK status nothing has been launched, and focus_last_error()
+ *     returns a message (thread-local, valid until the next call on that
+ *     thread). A failed launch returns FOCUS_ERR_DEVICE.
+ *   - Device-side data (group ids, perm, offsets) cannot be checked on the
+ *     host. Out-of-range values give undefined results but never an
+ *     out-of-bounds access: kernels clamp every index they read.
+ *   - Workspaces are caller-provided scratch of at least the size the
+ *     matching *_workspace_bytes() function returns; contents are undefined
+ *     between calls, and concurrent calls must not share one.
+ *   - Results are bitwise deterministic for fixed inputs on one device.
+ *   - Nothing is thrown across the ABI; the library never prints or exits.
+ */
+#ifndef FOCUS_H_
+#define FOCUS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* focus_stream_t; /* hipStream_t */
+
+typedef enum {
+    FOCUS_OK = 0,
+    FOCUS_ERR_INVALID_ARGUMENT = 1, /* null / misaligned pointer, bad size, overlap */
+    FOCUS_ERR_UNSUPPORTED = 2,      /* valid request outside the supported range   */
+    FOCUS_ERR_WORKSPACE = 3,        /* workspace missing or too small              */
+    FOCUS_ERR_DEVICE = 4            /* a HIP launch or runtime call failed         */
+} focus_status;
+
+typedef enum { FOCUS_BF16 = 0, FOCUS_F32 = 1 } focus_dtype;
+
+#define FOCUS_ABI_VERSION 1
+#define FOCUS_MAX_GROUPS 64
+
+int focus_abi_version(void);
+const char* focus_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Step 1: hard group assignment (Japanese page §2.1: the hidden state h_t is
+ * projected and compared with the centroids in centroid space; §2.2: a hard
+ * top-k assignment at inference, here k = 1).
+ *
+ *   score[t][k] = (h_t · P) · C_k + bias[k]      computed as h_t · (P C^T)
+ *   group_ids[t] = argmax_k score[t][k]          exact ties -> lowest k
+ *   margin[t]    = top-1 score - top-2 score     (+inf when K == 1)
+ *
+ * hidden    [B][n][d_model] fp32     P [d_model][d_proj] fp32
+ * C         [K][d_proj] fp32         bias [K] fp32 or NULL
+ * group_ids [B][n] int32 (out)       margin [B][n] fp32 (out) or NULL
+ * Limits: 1 <= K <= 64; d_model % 4 == 0; d_proj >= 1; B, n >= 1.
+ * The scores are accumulated in fp32 from an exact bf16 hi/lo split of h
+ * and of P C^T, so they agree with plain fp32 arithmetic to ~1e-6 relative;
+ * tokens whose top-2 margin is below ~1e-3 may resolve either way.
+ * ---------------------------------------------------------------------- */
+size_t focus_assign_workspace_bytes(int d_model, int K);
+focus_status focus_assign(const float* hidden, const float* P, const float* C, const float* bias,
+                          int B, int n, int d_model, int d_proj, int K,
+                          int32_t* group_ids, float* margin,
+                          void* workspace, size_t workspace_bytes, focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Step 2: stable grouping of tokens (counting sort per batch element).
+ *
+ * group_offsets[b][k] = number of tokens of batch b whose id is < k (K+1
+ *                       entries; empty groups repeat an offset)
+ * perm[b][group_offsets[b][g] + r] = t, the r-th token (in increasing t)
+ *                       with id g; so perm maps sorted slot -> position and
+ *                       positions increase inside each group's segment.
+ * group_ids [B][n] int32 in [0, K) (values outside are clamped)
+ * perm [B][n] int32 (out), group_offsets [B][K+1] int32 (out)
+ * Limits: 1 <= K <= 64; B, n >= 1.
+ * ---------------------------------------------------------------------- */
+size_t focus_group_sort_workspace_bytes(int B, int n, int K);
+focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K,
+                              int32_t* perm, int32_t* group_offsets,
+                              void* workspace, size_t workspace_bytes, focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Step 3: exact-softmax attention over the Focus pattern (Korean page §2.1
+ * and §2.3; Japanese page §2.1-§2.2). For query row (b, h, i), with kv head
+ * h / (Hq / Hkv) and groups shared by all heads of a token:
+ *
+ *   A_i = { j : 0 <= i - j <= window }  U  { j : j < i - window,
+ *                                             group_ids[b][j] == group_ids[b][i] }
+ *   out[b][h][i] = sum_{j in A_i} softmax_j(scale * q_i . k_j) v_j
+ *   lse[b][h][i] = log sum_{j in A_i} exp(scale * q_i . k_j)   (natural log)
+ *
+ * Each allowed pair is counted once (the two sets are disjoint). The work is
+ * done in two passes, as the Korean page §2.3 splits the pattern: an
+ * intra-group long-range pass in group-sorted order (tiles of keys from
+ * other groups are never visited) and a local-window pass in sequence order
+ * that merges both parts by log-sum-exp.
+ *
+ * q [B][Hq][n][d_head] bf16 bits; k, v [B][Hkv][n][d_head] bf16 bits
+ * group_ids [B][n], perm [B][n], group_offsets [B][K+1]: as produced by
+ *   focus_group_sort from the same ids
+ * out [B][Hq][n][d_head], bf16 (round to nearest even) or fp32 per out_dtype;
+ *   must not overlap q, k or v
+ * lse [B][Hq][n] fp32 or NULL
+ * Limits: d_head in {32, 64, 128}; 1 <= K <= 64; Hq % Hkv == 0; window >= 0;
+ *   scale finite and > 0; B, n >= 1.
+ * ---------------------------------------------------------------------- */
+size_t focus_attn_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int window);
+focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const int32_t* group_ids, const int32_t* perm,
+                            const int32_t* group_offsets,
+                            int B, int Hq, int Hkv, int n, int d_head, int K, int window,
+                            float scale, void* out, focus_dtype out_dtype, float* lse,
+                            void* workspace, size_t workspace_bytes, focus_stream_t stream);
+
+/* The two passes of focus_attn_fwd as separate calls (same arguments and the
+ * same workspace, which carries the long-range partial result from the first
+ * call to the second). focus_attn_fwd == long_range then window_merge. */
+focus_status focus_attn_long_range(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   const int32_t* group_ids, const int32_t* perm,
+                                   const int32_t* group_offsets,
+                                   int B, int Hq, int Hkv, int n, int d_head, int K, int window,
+                                   float scale, void* out, focus_dtype out_dtype, float* lse,
+                                   void* workspace, size_t workspace_bytes, focus_stream_t stream);
+focus_status focus_attn_window_merge(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                     const int32_t* group_ids, const int32_t* perm,
+                                     const int32_t* group_offsets,
+                                     int B, int Hq, int Hkv, int n, int d_head, int K, int window,
+                                     float scale, void* out, focus_dtype out_dtype, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Baseline: plain causal attention (every pair j <= i), the "full attention"
+ * the Focus pages compare against. Same layouts and limits as above; needs no
+ * workspace.
+ * ---------------------------------------------------------------------- */
+focus_status dense_causal_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   int B, int Hq, int Hkv, int n, int d_head, float scale,
+                                   void* out, focus_dtype out_dtype, float* lse,
+                                   focus_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FOCUS_H_ */

@@ -1,0 +1,190 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects invalid requests on the host before any HIP call
+(no GPU is touched by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from group_gated_sparse_amd import focus
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "focus.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+# Fake device addresses: only ever compared and range-checked on the host.
+A = 0x10000000
+Bp = 0x20000000
+C_ = 0x30000000
+D_ = 0x40000000
+E_ = 0x50000000
+F_ = 0x60000000
+G_ = 0x70000000
+H_ = 0x80000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:focus_status|size_t|int|const char\*)\s+(\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_header_is_plain_c():
+    subprocess.check_call(["gcc", "-std=c99", "-fsyntax-only", "-Wall", "-Werror", "-x", "c",
+                           HEADER])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = focus.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    out = subprocess.check_output(["nm", "-D", "--defined-only", focus.LIB_PATH], text=True)
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    for name in names:
+        assert name in exported, f"{name} is declared but not exported"
+        assert getattr(lib, name) is not None
+    assert lib.focus_abi_version() == 1
+
+
+def _err():
+    return focus.lib().focus_last_error().decode()
+
+
+def _assign(**kw):
+    args = dict(hidden=A, P=Bp, C=C_, bias=None, B=1, n=8, d_model=64, d_proj=16, K=4,
+                ids=D_, margin=None, ws=E_, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return focus.lib().focus_assign(args["hidden"], args["P"], args["C"], args["bias"], args["B"],
+                                    args["n"], args["d_model"], args["d_proj"], args["K"],
+                                    args["ids"], args["margin"], args["ws"], args["wsb"],
+                                    args["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(hidden=None), INVALID, "hidden"),
+    (dict(hidden=A + 4), INVALID, "aligned"),
+    (dict(P=None), INVALID, "P"),
+    (dict(ids=None), INVALID, "group_ids"),
+    (dict(K=0), UNSUPPORTED, "K"),
+    (dict(K=65), UNSUPPORTED, "K"),
+    (dict(B=0), INVALID, "B"),
+    (dict(n=0), INVALID, "n"),
+    (dict(d_model=62), UNSUPPORTED, "multiple of 4"),
+    (dict(d_proj=0), INVALID, "d_proj"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(wsb=16), WORKSPACE, "too small"),
+    (dict(ids=A + 64), INVALID, "overlap"),
+])
+def test_assign_rejects(kw, code, msg):
+    assert _assign(**kw) == code
+    assert msg in _err()
+
+
+def test_workspace_sizes():
+    lib = focus.lib()
+    # two bf16 tables of [32 or 64][d_model rounded up to 64], each 256-byte aligned
+    assert lib.focus_assign_workspace_bytes(64, 4) == 2 * 32 * 64 * 2
+    assert lib.focus_assign_workspace_bytes(100, 40) == 2 * 64 * 128 * 2
+    assert lib.focus_assign_workspace_bytes(64, 0) == 0
+    assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 0
+    # long-range partial: fp32 [B][Hq][n][d] + fp32 [B][Hq][n]
+    assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == 256 * 2 * 32 * 4 + 2048
+    # no pair can be further apart than the window: no partial needed
+    assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
+    assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
+
+
+def _sort(**kw):
+    args = dict(ids=A, B=1, n=16, K=4, perm=Bp, offs=C_, stream=None)
+    args.update(kw)
+    return focus.lib().focus_group_sort(args["ids"], args["B"], args["n"], args["K"],
+                                        args["perm"], args["offs"], None, 0, args["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(ids=None), INVALID, "group_ids"),
+    (dict(perm=None), INVALID, "perm"),
+    (dict(offs=None), INVALID, "group_offsets"),
+    (dict(K=0), UNSUPPORTED, "K"),
+    (dict(K=100), UNSUPPORTED, "K"),
+    (dict(n=0), INVALID, "n"),
+    (dict(perm=A + 8), INVALID, "overlap"),
+])
+def test_group_sort_rejects(kw, code, msg):
+    assert _sort(**kw) == code
+    assert msg in _err()
+
+
+def _attn(fn="focus_attn_fwd", **kw):
+    args = dict(q=A, k=Bp, v=C_, ids=D_, perm=E_, offs=F_, B=1, Hq=4, Hkv=2, n=256, d=64, K=4,
+                w=16, scale=0.125, out=G_, dt=0, lse=None, ws=H_, wsb=1 << 30, stream=None)
+    args.update(kw)
+    f = getattr(focus.lib(), fn)
+    return f(args["q"], args["k"], args["v"], args["ids"], args["perm"], args["offs"], args["B"],
+             args["Hq"], args["Hkv"], args["n"], args["d"], args["K"], args["w"], args["scale"],
+             args["out"], args["dt"], args["lse"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_long_range",
+                                "focus_attn_window_merge"])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), INVALID, "q"),
+    (dict(k=Bp + 8), INVALID, "aligned"),
+    (dict(ids=None), INVALID, "group_ids"),
+    (dict(offs=None), INVALID, "group_offsets"),
+    (dict(out=None), INVALID, "out"),
+    (dict(d=48), UNSUPPORTED, "d_head"),
+    (dict(d=256), UNSUPPORTED, "d_head"),
+    (dict(Hq=3), INVALID, "multiple"),
+    (dict(K=0), UNSUPPORTED, "K"),
+    (dict(K=65), UNSUPPORTED, "K"),
+    (dict(w=-1), INVALID, "window"),
+    (dict(n=0), INVALID, "n"),
+    (dict(B=0), INVALID, "B"),
+    (dict(scale=0.0), INVALID, "scale"),
+    (dict(scale=-1.0), INVALID, "scale"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(dt=7), INVALID, "out_dtype"),
+    (dict(out=A + 1024), INVALID, "overlap"),
+    (dict(lse=G_ + 64), INVALID, "overlap"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(wsb=1024), WORKSPACE, "too small"),
+])
+def test_attn_rejects(fn, kw, code, msg):
+    assert _attn(fn, **kw) == code
+    assert msg in _err()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(q=None), INVALID, "q"),
+    (dict(d=16), UNSUPPORTED, "d_head"),
+    (dict(Hkv=3), INVALID, "multiple"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(out=Bp), INVALID, "overlap"),
+])
+def test_dense_rejects(kw, code, msg):
+    args = dict(q=A, k=Bp, v=C_, B=1, Hq=4, Hkv=2, n=256, d=64, scale=0.125, out=G_, dt=0,
+                lse=None, stream=None)
+    args.update(kw)
+    rc = focus.lib().dense_causal_attn_fwd(args["q"], args["k"], args["v"], args["B"], args["Hq"],
+                                           args["Hkv"], args["n"], args["d"], args["scale"],
+                                           args["out"], args["dt"], args["lse"], args["stream"])
+    assert rc == code
+    assert msg in _err()
+
+
+def test_error_text_is_thread_local():
+    import threading
+    assert _sort(K=0) == UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["text"] = _err()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["text"] == "" and "K must be" in _err()

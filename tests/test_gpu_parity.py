@@ -1,0 +1,215 @@
+"""GPU parity: every entry point of libfocus.so, called through the C ABI
+binding, against the CPU oracle on the same seeded inputs.
+
+Bars: group ids equal except near-ties (oracle top-2 margin < 1e-3, where
+either of the two top groups is accepted); perm and offsets bit-exact against
+the oracle sort of the GPU's own ids; attention within max-abs 1e-2 and
+mean-abs 1e-3 of the fp64 oracle (fp32 output; bf16 output adds its own
+rounding).
+"""
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_gated_sparse_amd import focus, synth, workloads
+from gpu_common import (check_attn, check_ids, dev, dev_bf16, host, sample_rows, say,
+                        visited_pairs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _qkv(rng, B, Hq, Hkv, n, d):
+    q = synth.bf16_bits(rng.standard_normal((B, Hq, n, d), dtype=np.float32))
+    k = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d), dtype=np.float32))
+    v = synth.bf16_bits(rng.standard_normal((B, Hkv, n, d), dtype=np.float32))
+    return q, k, v
+
+
+def _run_attn(q, k, v, ids, K, w, scale, out_dtype=torch.float32, stream=None):
+    tq, tk, tv = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    tid = dev(ids.astype(np.int32))
+    perm, offs = focus.focus_group_sort(tid, K, stream=stream)
+    out, lse = focus.focus_attn_fwd(tq, tk, tv, tid, perm, offs, K, w, scale,
+                                    out_dtype=out_dtype, want_lse=True, stream=stream)
+    torch.cuda.synchronize()
+    return host(out.float()), host(lse), host(perm), host(offs)
+
+
+# ---------------------------------------------------------------- attention
+ATTN_CASES = [
+    # (name, B, Hq, Hkv, n, d, K, w)
+    ("n1", 1, 1, 1, 1, 64, 3, 0),
+    ("ragged_n77_d32", 1, 2, 1, 77, 32, 3, 5),
+    ("w0_d64", 2, 2, 2, 200, 64, 4, 0),
+    ("K_gt_n", 1, 2, 2, 40, 64, 64, 3),
+    ("single_group", 1, 2, 1, 300, 128, 1, 17),
+    ("gqa3_ragged", 1, 6, 2, 333, 128, 5, 40),
+    ("gqa8_d128", 1, 16, 2, 520, 128, 7, 64),
+    ("gqa16", 1, 16, 1, 260, 64, 6, 30),
+    ("wide_window", 1, 2, 2, 150, 32, 4, 149),
+    ("many_tiles", 2, 3, 3, 1100, 64, 9, 100),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=[c[0] for c in ATTN_CASES])
+def test_focus_attn_matches_oracle(case):
+    name, B, Hq, Hkv, n, d, K, w = case
+    say(f"[attn] {name}: B={B} Hq={Hq} Hkv={Hkv} n={n} d={d} K={K} w={w}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    scale = 1.0 / math.sqrt(d)
+    out, lse, perm, offs = _run_attn(q, k, v, ids, K, w, scale)
+    ref, rlse, _ = oracle.attn(q, k, v, ids, w, scale)
+    check_attn(out.reshape(-1, d), ref.reshape(-1, d), name)
+    assert np.max(np.abs(lse - rlse)) < 1e-3
+    rperm, roffs = oracle.group_sort(ids, K)
+    assert np.array_equal(perm, rperm) and np.array_equal(offs, roffs)
+
+
+def test_focus_attn_bf16_output():
+    say("[attn] bf16 output")
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, n, d, K, w = 1, 8, 2, 700, 128, 6, 90
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    out, _, _, _ = _run_attn(q, k, v, ids, K, w, 0.088, out_dtype=torch.bfloat16)
+    ref, _, _ = oracle.attn(q, k, v, ids, w, 0.088)
+    check_attn(out.reshape(-1, d), ref.reshape(-1, d), "bf16 out", bf16_out=True)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+def test_dense_causal_matches_oracle(d):
+    say(f"[dense] d={d}")
+    rng = np.random.default_rng(d)
+    B, Hq, Hkv, n = 2, 4, 2, 517
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    scale = 1.0 / math.sqrt(d)
+    out, lse = focus.dense_causal_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), scale,
+                                           out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    ref, rlse, _ = oracle.attn(q, k, v, np.zeros((B, n), np.int32), 0, scale)
+    check_attn(host(out).reshape(-1, d), ref.reshape(-1, d), f"dense d={d}")
+    assert np.max(np.abs(host(lse) - rlse)) < 1e-3
+
+
+def test_single_group_and_wide_window_equal_dense():
+    """K = 1 and w >= n-1 both reduce the pattern to full causal attention."""
+    say("[attn] K=1 and w>=n-1 against the dense kernel")
+    rng = np.random.default_rng(5)
+    B, Hq, Hkv, n, d = 1, 8, 8, 640, 64
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    dense, _ = focus.dense_causal_attn_fwd(dev_bf16(q), dev_bf16(k), dev_bf16(v), 0.125,
+                                           out_dtype=torch.float32)
+    a, _, _, _ = _run_attn(q, k, v, np.zeros((B, n), np.int32), 1, 37, 0.125)
+    b, _, _, _ = _run_attn(q, k, v, rng.integers(0, 5, size=(B, n), dtype=np.int32), 5, n - 1,
+                           0.125)
+    dn = host(dense)
+    assert np.max(np.abs(a - dn)) < 1e-2 and np.max(np.abs(b - dn)) < 1e-5
+
+
+def test_deterministic_and_stream_independent():
+    say("[attn] determinism / non-default stream")
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, n, d, K, w = 1, 8, 1, 900, 128, 8, 64
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    a = _run_attn(q, k, v, ids, K, w, 0.09)
+    b = _run_attn(q, k, v, ids, K, w, 0.09)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = _run_attn(q, k, v, ids, K, w, 0.09, stream=s)
+    s.synchronize()
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
+
+
+def test_two_calls_equal_one():
+    """focus_attn_long_range then focus_attn_window_merge == focus_attn_fwd."""
+    say("[attn] split calls")
+    rng = np.random.default_rng(10)
+    B, Hq, Hkv, n, d, K, w = 1, 4, 4, 480, 64, 5, 33
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    tq, tk, tv, tid = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(ids)
+    perm, offs = focus.focus_group_sort(tid, K)
+    one, _ = focus.focus_attn_fwd(tq, tk, tv, tid, perm, offs, K, w, 0.125, out_dtype=torch.float32)
+    ws = torch.empty(focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w), dtype=torch.uint8,
+                     device="cuda")
+    two = torch.empty_like(one)
+    focus.focus_attn_long_range(tq, tk, tv, tid, perm, offs, K, w, 0.125, workspace=ws, out=two)
+    focus.focus_attn_window_merge(tq, tk, tv, tid, perm, offs, K, w, 0.125, workspace=ws, out=two)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+
+
+# ---------------------------------------------------------------- sort
+@pytest.mark.parametrize("B,n,K", [(1, 1, 1), (1, 5, 64), (3, 1000, 7), (2, 4097, 64), (1, 65536, 64)])
+def test_group_sort_bit_exact(B, n, K):
+    say(f"[sort] B={B} n={n} K={K}")
+    rng = np.random.default_rng(n + K)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    if n > 100:
+        ids[:, 10:60] = 3 % K
+    perm, offs = focus.focus_group_sort(dev(ids), K)
+    torch.cuda.synchronize()
+    rperm, roffs = oracle.group_sort(ids, K)
+    assert np.array_equal(host(perm), rperm) and np.array_equal(host(offs), roffs)
+
+
+# ---------------------------------------------------------------- assign
+ASSIGN_CASES = [
+    # (name, B, n, d_model, d_proj, K, bias)
+    ("k1", 1, 50, 64, 16, 1, False),
+    ("tiny_k4", 1, 256, 64, 32, 4, False),
+    ("ragged_tokens_k7", 3, 101, 100, 20, 7, True),
+    ("k33", 1, 300, 256, 64, 33, True),
+    ("k64_dproj200", 2, 128, 512, 200, 64, False),
+]
+
+
+@pytest.mark.parametrize("case", ASSIGN_CASES, ids=[c[0] for c in ASSIGN_CASES])
+def test_assign_matches_oracle(case):
+    name, B, n, d_model, d_proj, K, use_bias = case
+    say(f"[assign] {name}")
+    rng = np.random.default_rng(len(name) * 7 + K)
+    h = rng.standard_normal((B, n, d_model), dtype=np.float32)
+    P = (rng.standard_normal((d_model, d_proj), dtype=np.float32) / np.float32(np.sqrt(d_model)))
+    C = rng.standard_normal((K, d_proj), dtype=np.float32)
+    C /= np.linalg.norm(C, axis=1, keepdims=True)
+    bias = (rng.standard_normal(K).astype(np.float32) * np.float32(0.2)) if use_bias else None
+    ids, margin = focus.focus_assign(dev(h), dev(P), dev(C), None if bias is None else dev(bias))
+    torch.cuda.synchronize()
+    rids, rmargin = oracle.assign(h, P, C, bias)
+    check_ids(host(ids).ravel(), rids.ravel(), rmargin.ravel(), h.reshape(-1, d_model), P, C, bias,
+              name)
+    gm, rm = host(margin).ravel(), rmargin.ravel()
+    fin = np.isfinite(rm)
+    assert np.array_equal(np.isfinite(gm), fin)
+    assert np.max(np.abs(gm[fin] - rm[fin]), initial=0.0) < 1e-4
+
+
+# ---------------------------------------------------------------- workloads
+@pytest.mark.parametrize("wl", [workloads.TINY, workloads.GPT2], ids=lambda w: w.name)
+def test_whole_path_small_workloads(wl):
+    """assign -> sort -> attention on the full small workloads, all rows."""
+    say(f"[path] {wl.name}")
+    x = synth.make_inputs(wl)
+    out, lse, ids, perm, offs = focus.focus_forward(
+        dev(x["hidden"]), dev(x["P"]), dev(x["C"]), None if x["bias"] is None else dev(x["bias"]),
+        dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), wl.w, wl.softmax_scale,
+        out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    gids = host(ids)
+    rids, rmargin = oracle.assign(x["hidden"], x["P"], x["C"], x["bias"])
+    check_ids(gids.ravel(), rids.ravel(), rmargin.ravel(), x["hidden"].reshape(-1, wl.d_model),
+              x["P"], x["C"], x["bias"], wl.name)
+    rperm, roffs = oracle.group_sort(gids, wl.K)
+    assert np.array_equal(host(perm), rperm) and np.array_equal(host(offs), roffs)
+    ref, rlse, vis = oracle.attn(x["q"], x["k"], x["v"], gids, wl.w, wl.softmax_scale)
+    check_attn(host(out).reshape(-1, wl.d), ref.reshape(-1, wl.d), wl.name)
+    assert int(vis[:, 0].sum()) == visited_pairs(gids, wl.w)
