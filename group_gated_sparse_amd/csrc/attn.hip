@@ -9,7 +9,7 @@
 // work into a local-window attention and an intra-group long-range
 // attention; here those are two kernels joined by a log-sum-exp merge:
 //
-//   long-range pass (group-sorted order): for each tile of 128//G sorted
+//   long-range pass (group-sorted order): for each tile of 128/G sorted
 //     tokens x G query heads that share one kv head, visit only the key
 //     tiles of the groups present in the tile, and inside a group only keys
 //     whose position is below (largest query position) - w. Keys are
@@ -17,7 +17,7 @@
 //     Writes the normalised partial output and its log2-sum-exp per row.
 //   window pass (sequence order): for each tile of tokens, the key band
 //     [q0 - w, q0 + TT - 1]; its epilogue merges the long-range partial.
-//   dense causal: the window pass with the band widened to [0, q0 + TT - 1].
+//   dense causal (baseline): the window pass with the band [0, q0 + TT - 1].
 //
 // The two key sets {i-j <= w} and {i-j > w, same group} are disjoint, so
 // every allowed pair is counted exactly once.
@@ -27,7 +27,12 @@
 //   online softmax per row in registers (one row per lane pair, exp2 domain)
 //   O^T (d x rows)  += V^T P^T  : A = V^T via LDS transposing reads
 //                                 (ds_read_b64_tr_b16), B = P^T in registers
-// with v_mfma_f32_32x32x16_bf16 and fp32 accumulation.
+// with v_mfma_f32_32x32x16_bf16 and fp32 accumulation. K and V tiles are
+// copied HBM -> LDS by global_load_lds_dwordx4 into two LDS buffers: the copy
+// of tile t+1 runs while tile t is computed, one barrier per tile. The
+// running max is only moved (and the accumulator rescaled) when a row's max
+// grows by more than 2^8, so probabilities stay <= 256 and the rescale is
+// rare; the final normalisation is exact either way.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -41,14 +46,17 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 64;      // keys per tile
-constexpr int NT = 256;     // threads per workgroup
-constexpr int ROWS = 128;   // query rows per workgroup (4 waves x 32)
+constexpr int BN = 64;       // keys per tile
+constexpr int NT = 256;      // threads per workgroup
+constexpr int ROWS = 128;    // query rows per workgroup (4 waves x 32)
+constexpr int MAXSEG = 64;   // groups present in one sorted query tile (K <= 64)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+
+enum { kWindow = 0, kLongRange = 1, kDense = 2 };
 
 struct AttnArgs {
     const uint16_t* q;
@@ -71,29 +79,38 @@ struct AttnArgs {
     float sl2;     // scale * log2(e)
     int out_f32;
     int merge;
-    int dense;
 };
 
 template <int D>
 struct Geom {
-    static constexpr int NCH = D / 8;                    // 16-byte chunks per row
-    static constexpr int ROWB = D * 2;                   // bytes per row
+    static constexpr int NCH = D / 8;                         // 16-byte chunks per row
+    static constexpr int ROWB = D * 2;                        // bytes per row
     static constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;  // rows per 256-byte bank line
-    static constexpr int TILEB = BN * ROWB;
-    static constexpr int KS = D / 16;                    // k-steps of S^T = K Q^T
-    static constexpr int DB = D / 32;                    // 32-wide blocks of O^T
+    static constexpr int TILEB = BN * ROWB;                   // bytes of one K or V tile
+    static constexpr int NI = TILEB / (4 * 1024);             // 1 KB copies per wave per tile
+    static constexpr int KS = D / 16;                         // k-steps of S^T = K Q^T
+    static constexpr int DB = D / 32;                         // 32-wide blocks of O^T
 };
 
 // Byte offset of 16-byte chunk `ch` of tile row `row` in LDS. The chunk index
 // is XOR-swizzled per 256-byte bank line so that (a) 16 consecutive rows
 // reading the same logical chunk (the K operand) land on 16 distinct chunk
 // slots, and (b) the 4 rows x 2 chunks of a transposing V read are distinct.
+// The swizzle depends only on row bits 0-3, so adding 16*r rows is affine.
 template <int D>
 __device__ __forceinline__ int lds_off(int row, int ch) {
     constexpr int NCH = Geom<D>::NCH, RPL = Geom<D>::RPL;
     const int u = row / RPL;
     const int f = ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
     return row * Geom<D>::ROWB + ((ch ^ f) << 4);
+}
+// Inverse for the copy: chunk slot `pc` of row `row` holds logical chunk pc ^ f.
+template <int D>
+__device__ __forceinline__ int logical_chunk(int row, int pc) {
+    constexpr int NCH = Geom<D>::NCH, RPL = Geom<D>::RPL;
+    const int u = row / RPL;
+    const int f = ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
+    return pc ^ f;
 }
 
 __device__ __forceinline__ float other_half(float x) {
@@ -102,6 +119,14 @@ __device__ __forceinline__ float other_half(float x) {
 }
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte global -> LDS copy; lane l lands at lds_base + 16*l.
+__device__ __forceinline__ void copy16(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                     0);
+}
 
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
 // works through one contiguous range of work items (neighbouring tiles of one
@@ -112,13 +137,14 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return x * per + (x < rem ? x : rem) + local;
 }
 
-template <int D, int PHASE>  // PHASE 0: window / dense (sequence order); 1: long-range (sorted)
-__global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
+template <int D, int PHASE>
+__global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     using G = Geom<D>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * G::TILEB];
-    __shared__ int kpos_s[BN];
-    unsigned char* Ks = smem;
-    unsigned char* Vs = smem + G::TILEB;
+    constexpr bool SORTED = PHASE == kLongRange;
+    __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * G::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf1[2 * G::TILEB];
+    __shared__ int kpos0[BN], kpos1[BN];
+    __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 31, hh = lane >> 5;
@@ -130,7 +156,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
     rest /= a.nslices;
     const int kvh = rest % a.Hkv;
     const int b = rest / a.Hkv;
-    if (PHASE == 1) tile = a.ntiles - 1 - tile;  // heavier sorted tiles first
+    if (SORTED) tile = a.ntiles - 1 - tile;  // heavier sorted tiles first
 
     const int R = wave * 32 + rl;
     const int hslot = R / a.TT, tok = R % a.TT;
@@ -139,8 +165,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
     const int s_row = tile * a.TT + tok;
     const bool rvalid = s_row < a.n;
     int pos_i = rvalid ? s_row : 0;
-    int g_i = 0;
-    if (PHASE == 1 && rvalid) {
+    int g_i = -1;
+    if (SORTED && rvalid) {
         pos_i = clampi(a.perm[bn + s_row], 0, a.n - 1);
         g_i = clampi(a.ids[bn + pos_i], 0, a.K - 1);
     }
@@ -158,43 +184,140 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
         }
     }
 
+    const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * a.n * D;
+    const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * a.n * D;
+
+    // ---- the key tiles this workgroup visits: ntl tiles, tile tau at
+    // ---- key slot kt0(tau), valid slots below kend(tau).
+    int ntl = 0;
+    int kstart = 0, kend0 = 0;               // sequence-order passes
+    int gfirst = 0, minpos = 0;              // long-range pass
+    bool rows_one_group = false;
+    if (!SORTED) {
+        const int q0 = tile * a.TT;
+        const int qlast = min(a.n, q0 + a.TT) - 1;
+        kstart = (PHASE == kDense) ? 0 : max(0, q0 - a.w);
+        kend0 = qlast + 1;
+        ntl = (kend0 - kstart + BN - 1) / BN;
+    } else {
+        const int s0 = tile * a.TT;
+        const int s1 = min(a.n, s0 + a.TT);
+        const int* offb = a.offsets + (int64_t)b * (a.K + 1);
+        gfirst = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
+        const int glast = clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1);
+        const int nseg = glast - gfirst + 1;
+        if (tid < nseg) {
+            const int g = gfirst + tid;
+            const int ob = clampi(offb[g], 0, a.n);
+            const int oe = clampi(offb[g + 1], ob, a.n);
+            const int qlo = max(s0, ob), qhi = min(s1, oe);
+            int kend = ob;
+            if (qlo < qhi) {
+                // first slot in [ob, qhi) whose position is >= (largest query position) - w
+                const int maxpos = clampi(a.perm[bn + qhi - 1], 0, a.n - 1);
+                int lo = ob, hi = qhi;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (a.perm[bn + mid] < maxpos - a.w) lo = mid + 1; else hi = mid;
+                }
+                kend = lo;
+            }
+            seg_ob[tid] = ob;
+            seg_kend[tid] = kend;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            int run = 0;
+            for (int t = 0; t < nseg; ++t) {
+                seg_t0[t] = run;
+                run += (seg_kend[t] - seg_ob[t] + BN - 1) / BN;
+            }
+            seg_t0[nseg] = run;
+        }
+        __syncthreads();
+        ntl = seg_t0[nseg];
+        const int ob0 = clampi(offb[gfirst], 0, a.n);
+        const int oe0 = clampi(offb[gfirst + 1], ob0, a.n);
+        rows_one_group = (s0 >= ob0) && (s1 <= oe0);
+        minpos = clampi(a.perm[bn + s0], 0, a.n - 1);
+    }
+
+    // Tile tau -> (segment, first key slot, end of valid slots).
+    int seg_cur = 0;
+    auto locate = [&](int tau, int& seg, int& kt0, int& kend) {
+        if (!SORTED) {
+            seg = 0;
+            kt0 = kstart + tau * BN;
+            kend = kend0;
+        } else {
+            while (seg_t0[seg + 1] <= tau) ++seg;
+            kt0 = seg_ob[seg] + (tau - seg_t0[seg]) * BN;
+            kend = seg_kend[seg];
+        }
+    };
+
+    // This lane's share of a tile copy: NI rows (one per 1 KB copy) and the
+    // logical chunk it fetches from each.
+    int crow[G::NI], cch[G::NI];
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+        const int o = (wave * G::NI + i) * 1024 + 16 * lane;
+        crow[i] = o / G::ROWB;
+        cch[i] = logical_chunk<D>(crow[i], (o % G::ROWB) / 16);
+    }
+    int cpos[G::NI];  // sorted pass: positions of the rows of the next copy
+
+    auto fetch_pos = [&](int tau) {
+        int seg = seg_cur, kt0, kend;
+        locate(tau, seg, kt0, kend);
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i)
+            cpos[i] = a.perm[bn + min(kt0 + crow[i], kend - 1)];
+    };
+    auto issue = [&](int tau, unsigned char* bufp, int* kposp) {
+        int seg = seg_cur, kt0, kend;
+        locate(tau, seg, kt0, kend);
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) {
+            int pos;
+            if (SORTED) {
+                pos = clampi(cpos[i], 0, a.n - 1);
+                if ((16 * lane) % G::ROWB == 0)
+                    kposp[crow[i]] = (kt0 + crow[i] < kend) ? pos : 0x7fffffff;
+            } else {
+                pos = min(kt0 + crow[i], kend - 1);
+            }
+            const int64_t go = (int64_t)pos * D + cch[i] * 8;
+            copy16(kbase + go, bufp + (wave * G::NI + i) * 1024);
+            copy16(vbase + go, bufp + G::TILEB + (wave * G::NI + i) * 1024);
+        }
+    };
+
+    // LDS offsets of this lane's operand reads (tile-relative).
+    int koff[G::KS];
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) koff[ks] = lds_off<D>(rl, 2 * ks + hh);
+    const int m16 = lane & 15;
+    const int colbase = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);
+    int voff[G::DB][2];
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int col = db * 32 + colbase;
+            voff[db][s] = G::TILEB + lds_off<D>(4 * hh + (m16 >> 2) + 8 * s, col >> 3) + (col & 7) * 2;
+        }
+
     f32x16 acc[G::DB];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
-    float m_run = kNegInf, l_run = 0.0f;
+    float m_ref = kNegInf, l_run = 0.0f;
 
-    const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * a.n * D;
-    const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * a.n * D;
-
-    // One 64-key tile: keys kt0 .. kt0+63 (sequence positions in PHASE 0,
-    // sorted slots in PHASE 1); keys at or beyond kend are padding.
-    auto do_tile = [&](int kt0, int kend, bool full, int seg_g) {
-        __syncthreads();
-        if (PHASE == 1) {
-            if (tid < BN) {
-                const int s = kt0 + tid;
-                kpos_s[tid] = (s < kend) ? clampi(a.perm[bn + s], 0, a.n - 1) : -1;
-            }
-            __syncthreads();
-        }
-#pragma unroll
-        for (int it = 0; it < BN * G::NCH / NT; ++it) {
-            const int idx = it * NT + tid;
-            const int row = idx / G::NCH, ch = idx % G::NCH;
-            const int key = kt0 + row;
-            u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-            if (key < kend) {
-                const int pos = (PHASE == 0) ? key : kpos_s[row];
-                kx = *reinterpret_cast<const u32x4*>(kbase + (int64_t)pos * D + ch * 8);
-                vx = *reinterpret_cast<const u32x4*>(vbase + (int64_t)pos * D + ch * 8);
-            }
-            *reinterpret_cast<u32x4*>(Ks + lds_off<D>(row, ch)) = kx;
-            *reinterpret_cast<u32x4*>(Vs + lds_off<D>(row, ch)) = vx;
-        }
-        __syncthreads();
-
+    auto compute = [&](int tau, const unsigned char* bufp, const int* kposp) {
+        int kt0, kend;
+        locate(tau, seg_cur, kt0, kend);
         // S^T = K Q^T for two 32-key blocks.
         f32x16 st[2];
 #pragma unroll
@@ -204,13 +327,25 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
 #pragma unroll
             for (int ks = 0; ks < G::KS; ++ks) {
                 const bf16x8 kf =
-                    *reinterpret_cast<const bf16x8*>(Ks + lds_off<D>(kb * 32 + rl, 2 * ks + hh));
+                    *reinterpret_cast<const bf16x8*>(bufp + kb * 32 * G::ROWB + koff[ks]);
                 st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[kb], 0, 0, 0);
             }
         }
 
-        // Mask: lane holds keys kidx = kb*32 + 8*(e>>2) + 4*hh + (e&3) of its row.
+        // Mask (boundary tiles only). Lane holds keys kidx = kb*32 +
+        // 8*(e>>2) + 4*hh + (e&3) of its row.
+        bool full;
+        if (!SORTED) {
+            const int q0 = tile * a.TT;
+            const int qlast = kend - 1;
+            full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
+                   (PHASE == kDense || qlast - kt0 <= a.w);
+        } else {
+            full = rows_one_group && seg_cur == 0 && (kt0 + BN <= kend) &&
+                   (minpos - kposp[BN - 1] > a.w);
+        }
         if (!full) {
+            const int seg_g = gfirst + seg_cur;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -218,25 +353,36 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
                     const int kidx = kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
                     const int key = kt0 + kidx;
                     bool ok;
-                    if (PHASE == 0) {
+                    if (!SORTED) {
                         ok = key < kend && key <= pos_i && pos_i - key <= a.w;
                     } else {
-                        const int pj = kpos_s[kidx];
-                        ok = rvalid && g_i == seg_g && key < kend && pos_i - pj > a.w;
+                        ok = g_i == seg_g && key < kend && pos_i - kposp[kidx] > a.w;
                     }
                     if (!ok) st[kb][e] = kNegInf;
                 }
         }
 
+        // Online softmax with a lagging reference max.
         float tmax = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, st[kb][e]);
-        tmax = fmaxf(tmax, other_half(tmax));
-        const float m_new = fmaxf(m_run, tmax * a.sl2);
-        const float m_use = (m_new == kNegInf) ? 0.0f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        tmax = fmaxf(tmax, other_half(tmax)) * a.sl2;
+        const bool grow = tmax > m_ref + kRescaleSlack;
+        if (__any(grow)) {
+            // growing rows: alpha = 2^(m_ref - tmax) (0 when m_ref = -inf);
+            // the other rows of the wave keep their reference (alpha = 1).
+            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.0f;
+            const float m_new = grow ? tmax : m_ref;
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+            m_ref = m_new;
+        }
+        const float m_use = (m_ref == kNegInf) ? 0.0f : m_ref;
         float psum = 0.0f;
         bf16x8 pf[2][2];
 #pragma unroll
@@ -247,80 +393,56 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
                 psum += p;
                 pf[kb][e >> 3][e & 7] = (__bf16)p;
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+        l_run += psum;
 
         // O^T += V^T P^T. For k-step (kb, sp) the B slots 0..3 / 4..7 of lane
         // half hh hold keys kb*32+16*sp+4*hh+{0..3} / +8+{0..3}; the A operand
         // gets the same keys through two transposing reads, lane m of each
         // 16-lane group addressing row key0 + m/4, columns 4*(m%4) .. +3 of
         // its 16-column half.
-        const int m16 = lane & 15;
-        const int colbase = 16 * ((lane >> 4) & 1) + 4 * (m16 & 3);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
-                const int key0 = kb * 32 + 16 * sp + 4 * hh + (m16 >> 2);
+                const unsigned char* vb = bufp + (kb * 32 + 16 * sp) * G::ROWB;
 #pragma unroll
                 for (int db = 0; db < G::DB; ++db) {
-                    const int col = db * 32 + colbase;
-                    const int o1 = lds_off<D>(key0, col >> 3) + (col & 7) * 2;
-                    const int o2 = lds_off<D>(key0 + 8, col >> 3) + (col & 7) * 2;
                     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(Vs + o1));
+                        (__attribute__((address_space(3))) s16x4*)(vb + voff[db][0]));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (__attribute__((address_space(3))) s16x4*)(Vs + o2));
+                        (__attribute__((address_space(3))) s16x4*)(vb + voff[db][1]));
                     const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    const bf16x8 vf = __builtin_bit_cast(bf16x8, vv);
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[kb][sp], acc[db], 0, 0, 0);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        __builtin_bit_cast(bf16x8, vv), pf[kb][sp], acc[db], 0, 0, 0);
                 }
             }
     };
 
-    if (PHASE == 0) {
-        const int q0 = tile * a.TT;
-        const int qlast = min(a.n, q0 + a.TT) - 1;
-        const int kstart = a.dense ? 0 : max(0, q0 - a.w);
-        const int kend = qlast + 1;
-        for (int kt0 = kstart; kt0 < kend; kt0 += BN) {
-            const bool full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
-                              (a.dense || qlast - kt0 <= a.w);
-            do_tile(kt0, kend, full, 0);
+    // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
+    // ---- compute of tile tau; one barrier per tile.
+    if (ntl > 0) {
+        if (SORTED) {
+            fetch_pos(0);
+            wait_vm();
         }
-    } else {
-        const int s0 = tile * a.TT;
-        const int s1 = min(a.n, s0 + a.TT);
-        const int* offb = a.offsets + (int64_t)b * (a.K + 1);
-        const int gf = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
-        const int gl = clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], 0, a.K - 1);
-        for (int g = gf; g <= gl; ++g) {
-            const int ob = clampi(offb[g], 0, a.n);
-            const int oe = clampi(offb[g + 1], ob, a.n);
-            const int qlo = max(s0, ob), qhi = min(s1, oe);
-            if (qlo >= qhi) continue;
-            const int maxpos = clampi(a.perm[bn + qhi - 1], 0, a.n - 1);
-            const int minpos = clampi(a.perm[bn + qlo], 0, a.n - 1);
-            // first slot in [ob, qhi) whose position is >= maxpos - w
-            int lo = ob, hi = qhi;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (a.perm[bn + mid] < maxpos - a.w) lo = mid + 1; else hi = mid;
+        issue(0, buf0, kpos0);
+        if (SORTED && ntl > 1) fetch_pos(1);
+        for (int tau = 0; tau < ntl; tau += 2) {
+            wait_vm();
+            __syncthreads();
+            if (tau + 1 < ntl) {
+                issue(tau + 1, buf1, kpos1);
+                if (SORTED && tau + 2 < ntl) fetch_pos(tau + 2);
             }
-            const int kend = lo;
-            const bool rows_one_group = (s0 >= ob) && (s1 <= oe);
-            for (int kt0 = ob; kt0 < kend; kt0 += BN) {
-                bool full = false;
-                if (rows_one_group && kt0 + BN <= kend) {
-                    const int last_pos = a.perm[bn + kt0 + BN - 1];
-                    full = (minpos - last_pos > a.w);
-                }
-                do_tile(kt0, kend, full, g);
+            compute(tau, buf0, kpos0);
+            if (tau + 1 >= ntl) break;
+            wait_vm();
+            __syncthreads();
+            if (tau + 2 < ntl) {
+                issue(tau + 2, buf0, kpos0);
+                if (SORTED && tau + 3 < ntl) fetch_pos(tau + 3);
             }
+            compute(tau + 1, buf1, kpos1);
         }
     }
 
@@ -328,8 +450,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
     // acc[db][4*i + j]; l_run covers this lane half's keys.
     const float l_tot = l_run + other_half(l_run);
     const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
-    if (PHASE == 1) {
-        if (!rvalid) return;
+    if (!rvalid) return;
+    if (SORTED) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         float* orow = a.og + row * D;
 #pragma unroll
@@ -340,46 +462,45 @@ __global__ __launch_bounds__(NT) void attn_kernel(AttnArgs a) {
                            acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv};
                 *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i + 4 * hh) = o;
             }
-        if (hh == 0) a.lseg[row] = l_tot > 0.0f ? m_run + __log2f(l_tot) : kNegInf;
-    } else {
-        if (!rvalid) return;
-        float lse2 = m_run + __log2f(l_tot);
-        float cw = 1.0f / l_tot, cg = 0.0f;
-        const float* grow = nullptr;
-        if (a.merge) {
-            const float lg = a.lseg[row];
-            const float M = fmaxf(lse2, lg);
-            const float aw = __builtin_amdgcn_exp2f(lse2 - M);
-            const float ag = __builtin_amdgcn_exp2f(lg - M);
-            const float den = aw + ag;
-            cw = aw / (den * l_tot);
-            cg = ag / den;
-            lse2 = M + __log2f(den);
-            grow = a.og + row * D;
-        }
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d0 = db * 32 + 8 * i + 4 * hh;
-                f32x4 o = {acc[db][4 * i] * cw, acc[db][4 * i + 1] * cw, acc[db][4 * i + 2] * cw,
-                           acc[db][4 * i + 3] * cw};
-                if (grow) {
-                    const f32x4 gv = *reinterpret_cast<const f32x4*>(grow + d0);
-                    o[0] = __builtin_fmaf(gv[0], cg, o[0]);
-                    o[1] = __builtin_fmaf(gv[1], cg, o[1]);
-                    o[2] = __builtin_fmaf(gv[2], cg, o[2]);
-                    o[3] = __builtin_fmaf(gv[3], cg, o[3]);
-                }
-                if (a.out_f32) {
-                    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = o;
-                } else {
-                    const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-                    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + row * D + d0) = ob;
-                }
-            }
-        if (hh == 0 && a.lse) a.lse[row] = lse2 * kLn2;
+        if (hh == 0) a.lseg[row] = l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf;
+        return;
     }
+    float lse2 = m_ref + __log2f(l_tot);
+    float cw = 1.0f / l_tot, cg = 0.0f;
+    const float* grow_p = nullptr;
+    if (PHASE == kWindow && a.merge) {
+        const float lg = a.lseg[row];
+        const float M = fmaxf(lse2, lg);
+        const float aw = __builtin_amdgcn_exp2f(lse2 - M);
+        const float ag = __builtin_amdgcn_exp2f(lg - M);
+        const float den = aw + ag;
+        cw = aw / (den * l_tot);
+        cg = ag / den;
+        lse2 = M + __log2f(den);
+        grow_p = a.og + row * D;
+    }
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int d0 = db * 32 + 8 * i + 4 * hh;
+            f32x4 o = {acc[db][4 * i] * cw, acc[db][4 * i + 1] * cw, acc[db][4 * i + 2] * cw,
+                       acc[db][4 * i + 3] * cw};
+            if (grow_p) {
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(grow_p + d0);
+                o[0] = __builtin_fmaf(gv[0], cg, o[0]);
+                o[1] = __builtin_fmaf(gv[1], cg, o[1]);
+                o[2] = __builtin_fmaf(gv[2], cg, o[2]);
+                o[3] = __builtin_fmaf(gv[3], cg, o[3]);
+            }
+            if (a.out_f32) {
+                *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = o;
+            } else {
+                const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + row * D + d0) = ob;
+            }
+        }
+    if (hh == 0 && a.lse) a.lse[row] = lse2 * kLn2;
 }
 
 // Query heads packed into one workgroup: the largest power of two <= 8 that
@@ -440,21 +561,20 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     AttnArgs a = make_args(p);
-    return launch<1>(a, p.d, stream);
+    return launch<kLongRange>(a, p.d, stream);
 }
 
 hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream) {
     AttnArgs a = make_args(p);
     a.merge = merge && attn_has_long_range(p.n, p.w) ? 1 : 0;
-    return launch<0>(a, p.d, stream);
+    return launch<kWindow>(a, p.d, stream);
 }
 
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream) {
     AttnArgs a = make_args(p);
-    a.dense = 1;
     a.merge = 0;
     a.w = p.n;
-    return launch<0>(a, p.d, stream);
+    return launch<kDense>(a, p.d, stream);
 }
 
 }  // namespace focus
