@@ -133,6 +133,8 @@ def main():
     out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=dv)
     ws_a = torch.empty(focus.focus_assign_workspace_bytes(wl.d_model, K), dtype=torch.uint8,
                        device=dv)
+    ws_s = torch.empty(max(focus.focus_group_sort_workspace_bytes(B, n, K), 1), dtype=torch.uint8,
+                       device=dv)
     ws_n = focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w)
     ws_t = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dv)
     stream = torch.cuda.current_stream()
@@ -146,7 +148,7 @@ def main():
         mark(0)
         focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False, workspace=ws_a)
         mark(1)
-        focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs)
+        focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
         mark(2)
         focus.focus_attn_long_range(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t, out=out)
         mark(3)

@@ -195,22 +195,18 @@ focus_status focus_assign(const float* hidden, const float* P, const float* C, c
 }
 
 size_t focus_group_sort_workspace_bytes(int B, int n, int K) {
-    (void)B;
-    (void)n;
-    (void)K;
-    return 0;
+    if (B < 1 || n < 1 || K < 1 || K > FOCUS_MAX_GROUPS) return 0;
+    return focus::group_sort_workspace(B, n, K);
 }
 
 focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K, int32_t* perm,
                               int32_t* group_offsets, void* workspace, size_t workspace_bytes,
                               focus_stream_t stream) {
-    (void)workspace;
-    (void)workspace_bytes;
     REQUIRE(B >= 1 && n >= 1, FOCUS_ERR_INVALID_ARGUMENT, "B and n must be >= 1 (got B=%d n=%d)",
             B, n);
     REQUIRE(K >= 1 && K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)",
             FOCUS_MAX_GROUPS, K);
-    REQUIRE(B <= kMaxGrid, FOCUS_ERR_UNSUPPORTED, "B too large");
+    REQUIRE(B <= 65535, FOCUS_ERR_UNSUPPORTED, "B must be <= 65535 (got %d)", B);
     REQUIRE_PTR(group_ids, 4);
     REQUIRE_PTR(perm, 4);
     REQUIRE_PTR(group_offsets, 4);
@@ -219,8 +215,13 @@ focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K, int
                 !overlaps(group_offsets, (size_t)B * (K + 1) * 4, group_ids, nb) &&
                 !overlaps(group_offsets, (size_t)B * (K + 1) * 4, perm, nb),
             FOCUS_ERR_INVALID_ARGUMENT, "group_ids, perm and group_offsets must not overlap");
+    const size_t need = focus::group_sort_workspace(B, n, K);
+    REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    REQUIRE(aligned(workspace, 4), FOCUS_ERR_WORKSPACE, "workspace must be 4-byte aligned");
+    REQUIRE(workspace_bytes >= need, FOCUS_ERR_WORKSPACE,
+            "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
     return device_status(focus::launch_group_sort(group_ids, B, n, K, perm, group_offsets,
-                                                  static_cast<hipStream_t>(stream)),
+                                                  workspace, static_cast<hipStream_t>(stream)),
                          "group sort launch");
 }
 

@@ -10,10 +10,16 @@
 //
 // The streaming pass is a dense contraction S^T = W^T H^T (K x tokens) that
 // must keep up with HBM: at K = 32 it needs 16 flop per byte of hidden state,
-// near the fp32 vector ridge, so it runs on bf16 MFMA with fp32-accurate
-// operands: x = hi + lo with hi = bf16(x), lo = bf16(x - hi) for both h and
-// W, and hi*hi + hi*lo + lo*hi accumulated in fp32 (the lo*lo term is below
-// fp32 rounding of the products that are kept).
+// beyond what scalar fp32 FMA sustains at 8 TB/s, so it runs on bf16 MFMA
+// with fp32-accurate operands: x = hi + lo with hi = bf16(x), lo =
+// bf16(x - hi) for both h and W, and hi*hi + hi*lo + lo*hi accumulated in
+// fp32 (the dropped lo*lo term is ~2^-16 of each product).
+//
+// Memory layout for coalescing: the hidden slice of a step (32 tokens x 64
+// columns, 8 KB) is copied HBM -> LDS with global_load_lds_dwordx4, each copy
+// one contiguous 1 KB (4 token rows); the W^T operand is stored by the
+// prologue in MFMA fragment order, so every fragment load is also one
+// contiguous 1 KB.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,61 +30,67 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_inff();
 
-// W^T[k][m] = sum_j P[m][j] C[k][j] for a block of 64 rows m, split into
-// bf16 hi/lo tables of shape [KP][dpad]; padding rows/columns are zero.
-// P is staged through LDS in 128-column slabs (row stride 129 floats, so the
-// 64 lanes of a wave, one row each, hit 64 different banks); C is read with a
-// wave-uniform address (one group k per wave at a time).
-constexpr int PREP_ROWS = 64;
+// Fragment order of the split W^T tables. For 64-column step s, 32-group
+// block mb, k-step e (8 columns) and table (0 = hi, 1 = lo), lane l = 32*hh +
+// rl holds W^T[mb*32 + rl][64*s + 32*hh + 8*e .. +8] as 8 bf16 (16 bytes):
+//   fragment index f = ((s * NB + mb) * 4 + e) * 2 + table,  bytes [f*1024 + 16*l, +16)
+__device__ __forceinline__ int64_t wfrag_elem(int s, int NB, int mb, int e, int table, int lane) {
+    return ((((int64_t)s * NB + mb) * 4 + e) * 2 + table) * 512 + lane * 8;
+}
+
+// W^T[k][m] = sum_j P[m][j] C[k][j]. One thread per output: a workgroup
+// covers 256/KP columns m and all KP groups; P rows and C are staged through
+// LDS in slabs of 128 values of j, C with a row stride of 129 floats so the
+// KP groups read by one wave sit in distinct banks. Outputs are split into
+// hi/lo bf16 and scattered into fragment order; padding groups (k >= K) and
+// columns (m >= d_model) are zero.
 constexpr int PREP_COLS = 128;
+constexpr int PREP_CS = PREP_COLS + 1;
 
 __global__ __launch_bounds__(256) void assign_prep_kernel(const float* __restrict__ P,
                                                           const float* __restrict__ C,
                                                           int d_model, int d_proj, int K,
                                                           int KP, int dpad,
-                                                          __bf16* __restrict__ whi,
-                                                          __bf16* __restrict__ wlo) {
-    __shared__ float Ps[PREP_ROWS * (PREP_COLS + 1)];
-    const int m0 = blockIdx.x * PREP_ROWS;
-    const int r = threadIdx.x % PREP_ROWS, wv = threadIdx.x / PREP_ROWS;
+                                                          __bf16* __restrict__ wfrag) {
+    __shared__ float Cs[64 * PREP_CS];
+    __shared__ float Ps[8 * PREP_COLS];
+    const int rows = 256 / KP;                  // 8 (KP = 32) or 4 (KP = 64)
+    const int m0 = blockIdx.x * rows;
+    const int k = threadIdx.x % KP, r = threadIdx.x / KP;
     const int m = m0 + r;
-    float acc[16];
-#pragma unroll
-    for (int it = 0; it < 16; ++it) acc[it] = 0.0f;
+    float acc = 0.0f;
     for (int j0 = 0; j0 < d_proj; j0 += PREP_COLS) {
         const int jc = min(PREP_COLS, d_proj - j0);
         __syncthreads();
-        for (int x = threadIdx.x; x < PREP_ROWS * jc; x += blockDim.x) {
+        for (int x = threadIdx.x; x < KP * jc; x += 256) {
+            const int kk = x / jc, j = x % jc;
+            Cs[kk * PREP_CS + j] = (kk < K) ? C[(int64_t)kk * d_proj + j0 + j] : 0.0f;
+        }
+        for (int x = threadIdx.x; x < rows * jc; x += 256) {
             const int rr = x / jc, j = x % jc;
             const int mm = m0 + rr;
-            Ps[rr * (PREP_COLS + 1) + j] = (mm < d_model) ? P[(int64_t)mm * d_proj + j0 + j] : 0.0f;
+            Ps[rr * PREP_COLS + j] = (mm < d_model) ? P[(int64_t)mm * d_proj + j0 + j] : 0.0f;
         }
         __syncthreads();
-#pragma unroll
-        for (int it = 0; it < 16; ++it) {
-            const int k = wv + 4 * it;
-            if (k < K) {
-                const float* cr = C + (int64_t)k * d_proj + j0;
-                const float* pr = Ps + r * (PREP_COLS + 1);
-                float a = acc[it];
-                for (int j = 0; j < jc; ++j) a = __builtin_fmaf(pr[j], cr[j], a);
-                acc[it] = a;
-            }
-        }
+        const float* pr = Ps + r * PREP_COLS;
+        const float* cr = Cs + k * PREP_CS;
+        for (int j = 0; j < jc; ++j) acc = __builtin_fmaf(pr[j], cr[j], acc);
     }
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-        const int k = wv + 4 * it;
-        if (k >= KP || m >= dpad) continue;
-        const float a = (m < d_model && k < K) ? acc[it] : 0.0f;
-        const __bf16 hi = (__bf16)a;
-        const __bf16 lo = (__bf16)(a - (float)hi);
-        whi[(int64_t)k * dpad + m] = hi;
-        wlo[(int64_t)k * dpad + m] = lo;
-    }
+    if (m >= dpad) return;
+    const float a = (m < d_model && k < K) ? acc : 0.0f;
+    const __bf16 hi = (__bf16)a;
+    const __bf16 lo = (__bf16)(a - (float)hi);
+    const int NB = KP / 32;
+    const int s = m / 64, within = m % 64;
+    const int hh = within / 32, e = (within % 32) / 8, t = within % 8;
+    const int mb = k / 32, rl = k % 32;
+    const int lane = hh * 32 + rl;
+    wfrag[wfrag_elem(s, NB, mb, e, 0, lane) + t] = hi;
+    wfrag[wfrag_elem(s, NB, mb, e, 1, lane) + t] = lo;
 }
 
 __device__ __forceinline__ float other_half(float x) {
@@ -90,43 +102,76 @@ __device__ __forceinline__ int other_half_i(int x) {
     return (int)((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
-// One workgroup = 32 tokens; its 4 waves split d_model into quarters and
-// their partial score tiles are summed in a fixed order (deterministic).
-// Lane (rl, hh): token t0+rl; in each 64-wide step s it owns hidden columns
-// s*64 + 32*hh .. +32 (one 128-byte run) and feeds them to 4 MFMA k-steps.
-template <int NB>  // number of 32-group blocks: 1 (K <= 32) or 2 (K <= 64)
-__global__ __launch_bounds__(256) void assign_argmax_kernel(
-    const float* __restrict__ hidden, const __bf16* __restrict__ whi,
-    const __bf16* __restrict__ wlo, const float* __restrict__ bias, int64_t ntok,
-    int d_model, int dpad, int K, int32_t* __restrict__ ids, float* __restrict__ margin) {
-    __shared__ float red[3][NB][16][64];
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Per-wave LDS slice of one step: 32 token rows x 64 fp32 columns (256 B per
+// row); 16-byte chunk c of row r sits in slot c ^ (r & 15), so the 16 rows
+// read by one quarter-wave hit 16 distinct chunk slots.
+constexpr int HROWB = 256;
+constexpr int HSTEPB = 32 * HROWB;  // 8 KB
+
+template <int NB>
+struct WRegs {
+    bf16x8 f[NB][4][2];
+};
+
+template <int NB>
+__global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
+    const float* __restrict__ hidden, const __bf16* __restrict__ wfrag,
+    const float* __restrict__ bias, int64_t ntok, int d_model, int dpad, int K,
+    int32_t* __restrict__ ids, float* __restrict__ margin) {
+    // [wave][buffer][8 KB]; reused for the cross-wave reduction at the end.
+    __shared__ __attribute__((aligned(1024))) unsigned char hbuf[4 * 2 * HSTEPB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rl = lane & 31, hh = lane >> 5;
-    const int64_t tok = (int64_t)blockIdx.x * 32 + rl;
+    const int64_t t0 = (int64_t)blockIdx.x * 32;
+    const int64_t tok = t0 + rl;
     const bool tvalid = tok < ntok;
-    const float* hrow = hidden + (tvalid ? tok : 0) * (int64_t)d_model;
 
+    // The 4 waves split the 64-column steps into quarters.
     const int NS = dpad / 64;
     const int s_beg = (NS * wave) / 4, s_end = (NS * (wave + 1)) / 4;
+    unsigned char* mybuf = hbuf + wave * 2 * HSTEPB;
+
+    // This lane's copy share: for copy i (1 KB) row 4*i + lane/16, slot lane%16.
+    const int crow0 = lane >> 4, cslot = lane & 15;
+
+    auto issue = [&](int s, unsigned char* dst, WRegs<NB>& wr) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * i + crow0;
+            const int c = cslot ^ (r & 15);
+            const int64_t trow = min(t0 + r, ntok - 1);
+            const int d = min(64 * s + 4 * c, d_model - 4);  // past d_model: W^T is zero there
+            __builtin_amdgcn_global_load_lds(hidden + trow * d_model + d,
+                                             (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                             16, 0, 0);
+        }
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int tb = 0; tb < 2; ++tb)
+                    wr.f[mb][e][tb] = *reinterpret_cast<const bf16x8*>(
+                        wfrag + wfrag_elem(s, NB, mb, e, tb, lane));
+    };
 
     f32x16 acc[NB];
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
         for (int e = 0; e < 16; ++e) acc[mb][e] = 0.0f;
 
-    for (int s = s_beg; s < s_end; ++s) {
-        const int d0 = s * 64 + hh * 32;
-        float4 hv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int d = d0 + 4 * e;
-            hv[e] = (tvalid && d < d_model) ? *reinterpret_cast<const float4*>(hrow + d)
-                                            : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+    auto compute = [&](const unsigned char* src, const WRegs<NB>& wr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float x[8] = {hv[2 * e].x,     hv[2 * e].y,     hv[2 * e].z,     hv[2 * e].w,
-                                hv[2 * e + 1].x, hv[2 * e + 1].y, hv[2 * e + 1].z, hv[2 * e + 1].w};
+            // columns 32*hh + 8*e .. +8 of token rl: logical chunks c, c+1
+            const int c = 8 * hh + 2 * e;
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + rl * HROWB + ((c ^ (rl & 15)) << 4));
+            const f32x4 x1 =
+                *reinterpret_cast<const f32x4*>(src + rl * HROWB + (((c + 1) ^ (rl & 15)) << 4));
+            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             bf16x8 bh, bl;
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -135,28 +180,45 @@ __global__ __launch_bounds__(256) void assign_argmax_kernel(
             }
 #pragma unroll
             for (int mb = 0; mb < NB; ++mb) {
-                const int64_t woff = (int64_t)(mb * 32 + rl) * dpad + d0 + 8 * e;
-                const bf16x8 ah = *reinterpret_cast<const bf16x8*>(whi + woff);
-                const bf16x8 al = *reinterpret_cast<const bf16x8*>(wlo + woff);
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc[mb], 0, 0, 0);
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc[mb], 0, 0, 0);
-                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr.f[mb][e][0], bl, acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr.f[mb][e][1], bh, acc[mb], 0, 0, 0);
+                acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wr.f[mb][e][0], bh, acc[mb], 0, 0, 0);
             }
         }
+    };
+
+    // Two buffers per wave; the copy of step s+1 is in flight while step s
+    // computes. Each wave reads only its own slice: no barrier needed.
+    WRegs<NB> wa, wb;
+    if (s_beg < s_end) issue(s_beg, mybuf, wa);
+    for (int s = s_beg; s < s_end; s += 2) {
+        wait_vm();
+        if (s + 1 < s_end) issue(s + 1, mybuf + HSTEPB, wb);
+        compute(mybuf, wa);
+        if (s + 1 >= s_end) break;
+        wait_vm();
+        if (s + 2 < s_end) issue(s + 2, mybuf, wa);
+        compute(mybuf + HSTEPB, wb);
     }
 
+    // Cross-wave sum in a fixed order (deterministic), through LDS.
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(hbuf);   // [3][NB][16][64]
     if (wave > 0) {
 #pragma unroll
         for (int mb = 0; mb < NB; ++mb)
-            for (int e = 0; e < 16; ++e) red[wave - 1][mb][e][lane] = acc[mb][e];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[(((wave - 1) * NB + mb) * 16 + e) * 64 + lane] = acc[mb][e];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
         for (int e = 0; e < 16; ++e)
-            acc[mb][e] = ((acc[mb][e] + red[0][mb][e][lane]) + red[1][mb][e][lane]) +
-                         red[2][mb][e][lane];
+            acc[mb][e] = ((acc[mb][e] + red[((0 * NB + mb) * 16 + e) * 64 + lane]) +
+                          red[((1 * NB + mb) * 16 + e) * 64 + lane]) +
+                         red[((2 * NB + mb) * 16 + e) * 64 + lane];
 
     // Lane holds scores of groups k = mb*32 + 8*i + 4*hh + j (e = 4*i + j),
     // visited in increasing k. Top-2 with exact ties resolved to the lowest k.
@@ -164,6 +226,7 @@ __global__ __launch_bounds__(256) void assign_argmax_kernel(
     int i1 = 0x7fffffff;
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int k = mb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
             if (k >= K) continue;
@@ -197,20 +260,18 @@ hipError_t launch_assign(const float* hidden, const float* P, const float* C, co
                          int B, int n, int d_model, int d_proj, int K, int32_t* ids,
                          float* margin, void* workspace, hipStream_t stream) {
     const int KP = assign_kpad(K), dpad = assign_dpad(d_model);
-    __bf16* whi = static_cast<__bf16*>(workspace);
-    __bf16* wlo = reinterpret_cast<__bf16*>(static_cast<char*>(workspace) +
-                                            align_up((size_t)KP * dpad * 2));
-    hipLaunchKernelGGL(assign_prep_kernel, dim3(dpad / PREP_ROWS), dim3(256), 0, stream, P,
-                       C, d_model, d_proj, K, KP, dpad, whi, wlo);
+    __bf16* wfrag = static_cast<__bf16*>(workspace);
+    hipLaunchKernelGGL(assign_prep_kernel, dim3(dpad / (256 / KP)), dim3(256), 0, stream, P, C,
+                       d_model, d_proj, K, KP, dpad, wfrag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntok = (int64_t)B * n;
     const dim3 grid((unsigned)((ntok + 31) / 32));
     if (KP == 32)
-        hipLaunchKernelGGL(assign_argmax_kernel<1>, grid, dim3(256), 0, stream, hidden, whi, wlo,
+        hipLaunchKernelGGL(assign_argmax_kernel<1>, grid, dim3(256), 0, stream, hidden, wfrag,
                            bias, ntok, d_model, dpad, K, ids, margin);
     else
-        hipLaunchKernelGGL(assign_argmax_kernel<2>, grid, dim3(256), 0, stream, hidden, whi, wlo,
+        hipLaunchKernelGGL(assign_argmax_kernel<2>, grid, dim3(256), 0, stream, hidden, wfrag,
                            bias, ntok, d_model, dpad, K, ids, margin);
     return hipGetLastError();
 }

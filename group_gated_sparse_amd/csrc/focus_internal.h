@@ -23,8 +23,10 @@ hipError_t launch_assign(const float* hidden, const float* P, const float* C, co
                          float* margin, void* workspace, hipStream_t stream);
 
 // ---- grouping ---------------------------------------------------------------
+constexpr int SORT_BLOCK_TOKENS = 2048;  // tokens per workgroup of the two sort passes
+size_t group_sort_workspace(int B, int n, int K);
 hipError_t launch_group_sort(const int32_t* ids, int B, int n, int K, int32_t* perm,
-                             int32_t* offsets, hipStream_t stream);
+                             int32_t* offsets, void* workspace, hipStream_t stream);
 
 // ---- attention --------------------------------------------------------------
 struct AttnProblem {

@@ -94,7 +94,8 @@ focus_status focus_assign(const float* hidden, const float* P, const float* C, c
  *                       positions increase inside each group's segment.
  * group_ids [B][n] int32 in [0, K) (values outside are clamped)
  * perm [B][n] int32 (out), group_offsets [B][K+1] int32 (out)
- * Limits: 1 <= K <= 64; B, n >= 1.
+ * workspace: per-block group counts, focus_group_sort_workspace_bytes() bytes
+ * Limits: 1 <= K <= 64; 1 <= B <= 65535; n >= 1.
  * ---------------------------------------------------------------------- */
 size_t focus_group_sort_workspace_bytes(int B, int n, int K);
 focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K,

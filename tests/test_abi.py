@@ -89,7 +89,9 @@ def test_workspace_sizes():
     assert lib.focus_assign_workspace_bytes(64, 4) == 2 * 32 * 64 * 2
     assert lib.focus_assign_workspace_bytes(100, 40) == 2 * 64 * 128 * 2
     assert lib.focus_assign_workspace_bytes(64, 0) == 0
-    assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 0
+    # per-block group counts: B x ceil(n / 2048) x K int32, 256-byte aligned
+    assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 256
+    assert lib.focus_group_sort_workspace_bytes(1, 65536, 64) == 32 * 64 * 4
     # long-range partial: fp32 [B][Hq][n][d] + fp32 [B][Hq][n]
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == 256 * 2 * 32 * 4 + 2048
     # no pair can be further apart than the window: no partial needed
@@ -98,10 +100,11 @@ def test_workspace_sizes():
 
 
 def _sort(**kw):
-    args = dict(ids=A, B=1, n=16, K=4, perm=Bp, offs=C_, stream=None)
+    args = dict(ids=A, B=1, n=16, K=4, perm=Bp, offs=C_, ws=D_, wsb=4096, stream=None)
     args.update(kw)
     return focus.lib().focus_group_sort(args["ids"], args["B"], args["n"], args["K"],
-                                        args["perm"], args["offs"], None, 0, args["stream"])
+                                        args["perm"], args["offs"], args["ws"], args["wsb"],
+                                        args["stream"])
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -112,6 +115,9 @@ def _sort(**kw):
     (dict(K=100), UNSUPPORTED, "K"),
     (dict(n=0), INVALID, "n"),
     (dict(perm=A + 8), INVALID, "overlap"),
+    (dict(B=70000), UNSUPPORTED, "B must be"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(wsb=4), WORKSPACE, "too small"),
 ])
 def test_group_sort_rejects(kw, code, msg):
     assert _sort(**kw) == code
