@@ -55,6 +55,8 @@ constexpr int MAXSEG = 64;   // groups present in one sorted query tile (K <= 64
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+constexpr int SEGCAP = 6;    // group segments stored per planned query tile
+constexpr int PLAN_INTS = 16;
 
 enum { kWindow = 0, kLongRange = 1, kDense = 2 };
 
@@ -65,6 +67,7 @@ struct AttnArgs {
     const int32_t* ids;
     const int32_t* perm;
     const int32_t* offsets;
+    const int* plan;  // long-range tile plan [B][ntiles][PLAN_INTS] or null
     float* og;     // long-range partial output [B][Hq][n][D] (normalised)
     float* lseg;   // long-range partial log2-sum-exp [B][Hq][n] (-inf: no key)
     void* out;
@@ -137,6 +140,65 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return x * per + (x < rem ? x : rem) + local;
 }
 
+// Key slots [ob, kend) that group g contributes to the long-range pass of
+// the sorted query slots [s0, s1): the group's segment [ob, oe) of perm, cut
+// at the first slot whose position is >= (largest query position of g in the
+// tile) - w. Positions increase inside a segment, so that cut is a binary
+// search, and no later slot of the segment can pair with any query of g here.
+__device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32_t* offb, int n,
+                                              int w, int s0, int s1, int g, int& ob, int& kend) {
+    ob = clampi(offb[g], 0, n);
+    const int oe = clampi(offb[g + 1], ob, n);
+    const int qlo = max(s0, ob), qhi = min(s1, oe);
+    kend = ob;
+    if (qlo < qhi) {
+        const int maxpos = clampi(perm_b[qhi - 1], 0, n - 1);
+        int lo = ob, hi = qhi;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (perm_b[mid] < maxpos - w) lo = mid + 1; else hi = mid;
+        }
+        kend = lo;
+    }
+}
+
+// Tile plan of the long-range pass, once per (batch, sorted query tile) and
+// shared by every kv head: record = {nseg (-1: more than SEGCAP groups, the
+// attention kernel then derives its segments itself), first group, all query
+// rows in one group, smallest query position, (ob, kend) per group}.
+__global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restrict__ ids,
+                                                        const int32_t* __restrict__ perm,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int n, int K, int w, int TT, int ntiles,
+                                                        int32_t* __restrict__ plan) {
+    const int b = blockIdx.y;
+    const int tile = blockIdx.x * 256 + threadIdx.x;
+    if (tile >= ntiles) return;
+    const int64_t bn = (int64_t)b * n;
+    const int32_t* perm_b = perm + bn;
+    const int32_t* offb = offsets + (int64_t)b * (K + 1);
+    const int s0 = tile * TT, s1 = min(n, s0 + TT);
+    const int gf = clampi(ids[bn + clampi(perm_b[s0], 0, n - 1)], 0, K - 1);
+    const int gl = clampi(ids[bn + clampi(perm_b[s1 - 1], 0, n - 1)], gf, K - 1);
+    const int nseg = gl - gf + 1;
+    int32_t* rec = plan + ((int64_t)b * ntiles + tile) * PLAN_INTS;
+    if (nseg > SEGCAP) {
+        rec[0] = -1;
+        return;
+    }
+    for (int t = 0; t < nseg; ++t) {
+        int ob, kend;
+        segment_range(perm_b, offb, n, w, s0, s1, gf + t, ob, kend);
+        rec[4 + 2 * t] = ob;
+        rec[5 + 2 * t] = kend;
+    }
+    const int ob0 = clampi(offb[gf], 0, n), oe0 = clampi(offb[gf + 1], ob0, n);
+    rec[0] = nseg;
+    rec[1] = gf;
+    rec[2] = (s0 >= ob0 && s1 <= oe0) ? 1 : 0;
+    rec[3] = clampi(perm_b[s0], 0, n - 1);
+}
+
 template <int D, int PHASE>
 __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     using G = Geom<D>;
@@ -171,19 +233,6 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         g_i = clampi(a.ids[bn + pos_i], 0, a.K - 1);
     }
 
-    // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
-    const int64_t qrow_off = (((int64_t)b * a.Hq + h) * a.n + pos_i) * D;
-    bf16x8 qf[G::KS];
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-        if (rvalid) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qrow_off + 16 * ks + 8 * hh);
-        } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) qf[ks][t] = (__bf16)0.0f;
-        }
-    }
-
     const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * a.n * D;
     const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * a.n * D;
 
@@ -202,28 +251,33 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     } else {
         const int s0 = tile * a.TT;
         const int s1 = min(a.n, s0 + a.TT);
-        const int* offb = a.offsets + (int64_t)b * (a.K + 1);
-        gfirst = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
-        const int glast = clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1);
-        const int nseg = glast - gfirst + 1;
-        if (tid < nseg) {
-            const int g = gfirst + tid;
-            const int ob = clampi(offb[g], 0, a.n);
-            const int oe = clampi(offb[g + 1], ob, a.n);
-            const int qlo = max(s0, ob), qhi = min(s1, oe);
-            int kend = ob;
-            if (qlo < qhi) {
-                // first slot in [ob, qhi) whose position is >= (largest query position) - w
-                const int maxpos = clampi(a.perm[bn + qhi - 1], 0, a.n - 1);
-                int lo = ob, hi = qhi;
-                while (lo < hi) {
-                    const int mid = (lo + hi) >> 1;
-                    if (a.perm[bn + mid] < maxpos - a.w) lo = mid + 1; else hi = mid;
-                }
-                kend = lo;
+        const int32_t* offb = a.offsets + (int64_t)b * (a.K + 1);
+        const int32_t* rec = a.plan ? a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS : nullptr;
+        int nseg = rec ? rec[0] : -1;
+        if (nseg >= 0) {
+            nseg = min(nseg, SEGCAP);
+            gfirst = clampi(rec[1], 0, a.K - 1);
+            rows_one_group = rec[2] != 0;
+            minpos = clampi(rec[3], 0, a.n - 1);
+            if (tid < nseg) {
+                seg_ob[tid] = clampi(rec[4 + 2 * tid], 0, a.n);
+                seg_kend[tid] = clampi(rec[5 + 2 * tid], seg_ob[tid], a.n);
             }
-            seg_ob[tid] = ob;
-            seg_kend[tid] = kend;
+        } else {
+            gfirst = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
+            const int glast =
+                clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1);
+            nseg = glast - gfirst + 1;
+            if (tid < nseg) {
+                int ob, kend;
+                segment_range(a.perm + bn, offb, a.n, a.w, s0, s1, gfirst + tid, ob, kend);
+                seg_ob[tid] = ob;
+                seg_kend[tid] = kend;
+            }
+            const int ob0 = clampi(offb[gfirst], 0, a.n);
+            const int oe0 = clampi(offb[gfirst + 1], ob0, a.n);
+            rows_one_group = (s0 >= ob0) && (s1 <= oe0);
+            minpos = clampi(a.perm[bn + s0], 0, a.n - 1);
         }
         __syncthreads();
         if (tid == 0) {
@@ -236,10 +290,6 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         }
         __syncthreads();
         ntl = seg_t0[nseg];
-        const int ob0 = clampi(offb[gfirst], 0, a.n);
-        const int oe0 = clampi(offb[gfirst + 1], ob0, a.n);
-        rows_one_group = (s0 >= ob0) && (s1 <= oe0);
-        minpos = clampi(a.perm[bn + s0], 0, a.n - 1);
     }
 
     // Tile tau -> (segment, first key slot, end of valid slots).
@@ -314,6 +364,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
     float m_ref = kNegInf, l_run = 0.0f;
+    bf16x8 qf[G::KS];  // Q^T fragments, loaded once the first key tile is in flight
 
     auto compute = [&](int tau, const unsigned char* bufp, const int* kposp) {
         int kt0, kend;
@@ -427,6 +478,20 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         }
         issue(0, buf0, kpos0);
         if (SORTED && ntl > 1) fetch_pos(1);
+    }
+    // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
+    const int64_t qrow_off = (((int64_t)b * a.Hq + h) * a.n + pos_i) * D;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        if (rvalid) {
+            qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qrow_off + 16 * ks + 8 * hh);
+        } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) qf[ks][t] = (__bf16)0.0f;
+        }
+    }
+
+    if (ntl > 0) {
         for (int tau = 0; tau < ntl; tau += 2) {
             wait_vm();
             __syncthreads();
@@ -537,9 +602,12 @@ AttnArgs make_args(const AttnProblem& p) {
     a.sl2 = p.scale * 1.44269504088896340736f;
     a.out_f32 = p.out_f32;
     if (p.workspace) {
-        a.og = static_cast<float*>(p.workspace);
-        a.lseg = reinterpret_cast<float*>(static_cast<char*>(p.workspace) +
-                                          align_up((size_t)p.B * p.Hq * p.n * p.d * 4));
+        char* ws = static_cast<char*>(p.workspace);
+        const size_t og_bytes = align_up((size_t)p.B * p.Hq * p.n * p.d * 4);
+        const size_t lse_bytes = align_up((size_t)p.B * p.Hq * p.n * 4);
+        a.og = reinterpret_cast<float*>(ws);
+        a.lseg = reinterpret_cast<float*>(ws + og_bytes);
+        a.plan = reinterpret_cast<const int32_t*>(ws + og_bytes + lse_bytes);
     }
     return a;
 }
@@ -561,17 +629,24 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     AttnArgs a = make_args(p);
+    hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
+                       p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT, a.ntiles,
+                       const_cast<int32_t*>(a.plan));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     return launch<kLongRange>(a, p.d, stream);
 }
 
 hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream) {
     AttnArgs a = make_args(p);
+    a.plan = nullptr;
     a.merge = merge && attn_has_long_range(p.n, p.w) ? 1 : 0;
     return launch<kWindow>(a, p.d, stream);
 }
 
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream) {
     AttnArgs a = make_args(p);
+    a.plan = nullptr;
     a.merge = 0;
     a.w = p.n;
     return launch<kDense>(a, p.d, stream);

@@ -46,9 +46,13 @@ struct AttnProblem {
 
 // True when some pair further apart than the window can exist (n - 1 > w).
 inline bool attn_has_long_range(int n, int w) { return (int64_t)n - 1 > (int64_t)w; }
+// Long-range partial output (fp32 [B][Hq][n][d]), its log2-sum-exp (fp32
+// [B][Hq][n]) and the tile plan (64 bytes per sorted query tile of >= 16
+// tokens).
 inline size_t attn_workspace(int B, int Hq, int n, int d, int w) {
     if (!attn_has_long_range(n, w)) return 0;
-    return align_up((size_t)B * Hq * n * d * 4) + align_up((size_t)B * Hq * n * 4);
+    return align_up((size_t)B * Hq * n * d * 4) + align_up((size_t)B * Hq * n * 4) +
+           align_up((size_t)B * ((n + 15) / 16) * 64);
 }
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream);
