@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle attention sample")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run one plain 1 GiB device-to-device copy (a reference "
+                         "dispatch for calibrating HBM byte counters)")
     return ap.parse_args()
 
 
@@ -233,6 +236,16 @@ def main():
         res["speedup_attn_vs_dense"] = dense_ms / attn_ms
         res["speedup_step_vs_dense"] = dense_ms / ms_step
         log(f"dense {dense_ms:.3f} ms ({res['dense_tflops']:.1f} TFLOP/s)")
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dv)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_probe_bytes"] = src.numel() * 4
+        del src, dst
 
     del hidden, q, k, v, out, ws_t
     torch.cuda.empty_cache()

@@ -95,25 +95,30 @@ struct Geom {
     static constexpr int DB = D / 32;                         // 32-wide blocks of O^T
 };
 
-// Byte offset of 16-byte chunk `ch` of tile row `row` in LDS. The chunk index
-// is XOR-swizzled per 256-byte bank line so that (a) 16 consecutive rows
-// reading the same logical chunk (the K operand) land on 16 distinct chunk
-// slots, and (b) the 4 rows x 2 chunks of a transposing V read are distinct.
-// The swizzle depends only on row bits 0-3, so adding 16*r rows is affine.
+// LDS tile layout: row r (one key) is ROWB contiguous bytes; its 16-byte
+// chunk c is stored in slot c ^ swz(r). The LDS serves 256 bytes (64 banks)
+// per cycle; a read is conflict-free when the lanes served together hit
+// distinct 16-byte bank groups (address / 16 mod 16). Measured on gfx950, the
+// patterns that matter are
+//   K operand (16-byte reads): 16 consecutive rows, one logical chunk;
+//   V operand (transposing 8-byte reads, 32 lanes together): 4 consecutive
+//     rows (aligned to 4) x logical chunks c0..c0+3 (c0 a multiple of 4),
+// and the swizzles below make both conflict-free. They depend on row bits
+// 0-3 only, so row + 16*j keeps the same swizzle.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);          // 16 chunks per row
+    if (D == 64) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);    // 8 chunks, 2 rows per 256 B
+    return (r >> 2) & 3;                                           // 4 chunks, 4 rows per 256 B
+}
 template <int D>
 __device__ __forceinline__ int lds_off(int row, int ch) {
-    constexpr int NCH = Geom<D>::NCH, RPL = Geom<D>::RPL;
-    const int u = row / RPL;
-    const int f = ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
-    return row * Geom<D>::ROWB + ((ch ^ f) << 4);
+    return row * Geom<D>::ROWB + ((ch ^ swz<D>(row)) << 4);
 }
-// Inverse for the copy: chunk slot `pc` of row `row` holds logical chunk pc ^ f.
+// Inverse for the copy: chunk slot `pc` of row `row` holds logical chunk pc ^ swz.
 template <int D>
 __device__ __forceinline__ int logical_chunk(int row, int pc) {
-    constexpr int NCH = Geom<D>::NCH, RPL = Geom<D>::RPL;
-    const int u = row / RPL;
-    const int f = ((u & (NCH / 2 - 1)) << 1) | ((u / (NCH / 2)) & 1);
-    return pc ^ f;
+    return pc ^ swz<D>(row);
 }
 
 __device__ __forceinline__ float other_half(float x) {
@@ -462,7 +467,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
                         (__attribute__((address_space(3))) s16x4*)(vb + voff[db][0]));
                     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                         (__attribute__((address_space(3))) s16x4*)(vb + voff[db][1]));
-                    const s16x8 vv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                     acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         __builtin_bit_cast(bf16x8, vv), pf[kb][sp], acc[db], 0, 0, 0);
                 }
