@@ -16,7 +16,8 @@
 //     gathered through perm, so every visited tile is dense in one group.
 //     Writes the normalised partial output and its log2-sum-exp per row.
 //   window pass (sequence order): for each tile of tokens, the key band
-//     [q0 - w, q0 + TT - 1]; its epilogue merges the long-range partial.
+//     [q0 - w, q0 + TT - 1]. The long-range partial is merged by starting
+//     the online softmax from it (log-sum-exp merge, exact).
 //   dense causal (baseline): the window pass with the band [0, q0 + TT - 1].
 //
 // The two key sets {i-j <= w} and {i-j > w, same group} are disjoint, so
@@ -484,6 +485,28 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         issue(0, buf0, kpos0);
         if (SORTED && ntl > 1) fetch_pos(1);
     }
+    // Window pass: start the online softmax from the long-range partial. A
+    // normalised partial O_g with log2-sum-exp L_g is exactly the state
+    // (acc = O_g, l = 1, reference max = L_g), so the window keys accumulate
+    // on top of it and the final normalisation merges both parts; the loads
+    // share the round trip of the Q rows and the first K/V tile.
+    if (PHASE == kWindow && a.merge && rvalid) {
+        const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
+        const float lg = a.lseg[row];
+        if (lg != kNegInf) {
+            const float* grow_p = a.og + row * D;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const f32x4 gv = *reinterpret_cast<const f32x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[db][4 * i + j] = gv[j];
+                }
+            m_ref = lg;
+            l_run = (hh == 0) ? 1.0f : 0.0f;  // halves are summed at the end
+        }
+    }
     // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
     const int64_t qrow_off = (((int64_t)b * a.Hq + h) * a.n + pos_i) * D;
 #pragma unroll
@@ -535,34 +558,15 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         if (hh == 0) a.lseg[row] = l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf;
         return;
     }
-    float lse2 = m_ref + __log2f(l_tot);
-    float cw = 1.0f / l_tot, cg = 0.0f;
-    const float* grow_p = nullptr;
-    if (PHASE == kWindow && a.merge) {
-        const float lg = a.lseg[row];
-        const float M = fmaxf(lse2, lg);
-        const float aw = __builtin_amdgcn_exp2f(lse2 - M);
-        const float ag = __builtin_amdgcn_exp2f(lg - M);
-        const float den = aw + ag;
-        cw = aw / (den * l_tot);
-        cg = ag / den;
-        lse2 = M + __log2f(den);
-        grow_p = a.og + row * D;
-    }
+    const float lse2 = m_ref + __log2f(l_tot);
+    const float cw = 1.0f / l_tot;
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int d0 = db * 32 + 8 * i + 4 * hh;
-            f32x4 o = {acc[db][4 * i] * cw, acc[db][4 * i + 1] * cw, acc[db][4 * i + 2] * cw,
-                       acc[db][4 * i + 3] * cw};
-            if (grow_p) {
-                const f32x4 gv = *reinterpret_cast<const f32x4*>(grow_p + d0);
-                o[0] = __builtin_fmaf(gv[0], cg, o[0]);
-                o[1] = __builtin_fmaf(gv[1], cg, o[1]);
-                o[2] = __builtin_fmaf(gv[2], cg, o[2]);
-                o[3] = __builtin_fmaf(gv[3], cg, o[3]);
-            }
+            const f32x4 o = {acc[db][4 * i] * cw, acc[db][4 * i + 1] * cw, acc[db][4 * i + 2] * cw,
+                             acc[db][4 * i + 3] * cw};
             if (a.out_f32) {
                 *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = o;
             } else {
