@@ -81,6 +81,7 @@ focus_status check_attn_shape(const AttnShape& s, bool needs_groups) {
     // Workgroup count of the attention grids: B * Hq * ceil(n / 16) / 8 at most.
     REQUIRE((int64_t)s.B * s.Hq * ((s.n + 15) / 16) <= kMaxGrid, FOCUS_ERR_UNSUPPORTED,
             "problem too large for one launch grid");
+    REQUIRE((int64_t)s.B * s.Hkv <= 65535, FOCUS_ERR_UNSUPPORTED, "B*Hkv must be <= 65535");
     return ok();
 }
 
@@ -126,7 +127,7 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     REQUIRE_PTR(group_ids, 4);
     REQUIRE_PTR(perm, 4);
     REQUIRE_PTR(group_offsets, 4);
-    const size_t need = focus::attn_workspace(B, Hq, n, d, w);
+    const size_t need = focus::attn_workspace(B, Hq, Hkv, n, d, w);
     if (need > 0) {
         REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -226,11 +227,10 @@ focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K, int
 }
 
 size_t focus_attn_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int window) {
-    (void)Hkv;
     (void)K;
-    if (B < 1 || Hq < 1 || n < 1 || window < 0) return 0;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;
     if (d_head != 32 && d_head != 64 && d_head != 128) return 0;
-    return focus::attn_workspace(B, Hq, n, d_head, window);
+    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window);
 }
 
 focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -7,14 +7,16 @@
 // window 0 <= i-j <= w, and beyond the window only keys of its own group;
 // the softmax is exact over the kept keys. The Korean page §2.3 splits the
 // work into a local-window attention and an intra-group long-range
-// attention; here those are two kernels joined by a log-sum-exp merge:
+// attention; here those are two passes joined by a log-sum-exp merge:
 //
-//   long-range pass (group-sorted order): for each tile of 128/G sorted
-//     tokens x G query heads that share one kv head, visit only the key
-//     tiles of the groups present in the tile, and inside a group only keys
-//     whose position is below (largest query position) - w. Keys are
-//     gathered through perm, so every visited tile is dense in one group.
-//     Writes the normalised partial output and its log2-sum-exp per row.
+//   long-range pass (group-sorted order): K and V are first copied into
+//     group-sorted order (row s = row perm[s]); a plan kernel lists, per
+//     sorted query tile, the key-slot range of each group present (keys of
+//     the group with position below (largest query position) - w). The
+//     attention kernel, for each tile of 128/G sorted tokens x G query heads
+//     sharing one kv head, visits only those key tiles, so every visited
+//     tile is dense in one group. It writes the normalised partial output and
+//     its log2-sum-exp per row.
 //   window pass (sequence order): for each tile of tokens, the key band
 //     [q0 - w, q0 + TT - 1]. The long-range partial is merged by starting
 //     the online softmax from it (log-sum-exp merge, exact).
@@ -48,6 +50,7 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;       // keys per tile
 constexpr int NT = 256;      // threads per workgroup
@@ -56,21 +59,21 @@ constexpr int MAXSEG = 64;   // groups present in one sorted query tile (K <= 64
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
-constexpr int SEGCAP = 6;    // group segments stored per planned query tile
-constexpr int PLAN_INTS = 16;
+constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 
 enum { kWindow = 0, kLongRange = 1, kDense = 2 };
 
 struct AttnArgs {
     const uint16_t* q;
-    const uint16_t* k;
+    const uint16_t* k;      // sequence order (window / dense) or sorted copy (long-range)
     const uint16_t* v;
     const int32_t* ids;
     const int32_t* perm;
     const int32_t* offsets;
-    const int* plan;  // long-range tile plan [B][ntiles][PLAN_INTS] or null
-    float* og;     // long-range partial output [B][Hq][n][D] (normalised)
-    float* lseg;   // long-range partial log2-sum-exp [B][Hq][n] (-inf: no key)
+    const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
+    int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
+    float* og;              // long-range partial output [B][Hq][n][D] (normalised)
+    float* lseg;            // long-range partial log2-sum-exp [B][Hq][n] (-inf: no key)
     void* out;
     float* lse;
     int B, Hq, Hkv, n, K, w;
@@ -89,7 +92,6 @@ template <int D>
 struct Geom {
     static constexpr int NCH = D / 8;                         // 16-byte chunks per row
     static constexpr int ROWB = D * 2;                        // bytes per row
-    static constexpr int RPL = ROWB >= 256 ? 1 : 256 / ROWB;  // rows per 256-byte bank line
     static constexpr int TILEB = BN * ROWB;                   // bytes of one K or V tile
     static constexpr int NI = TILEB / (4 * 1024);             // 1 KB copies per wave per tile
     static constexpr int KS = D / 16;                         // k-steps of S^T = K Q^T
@@ -146,32 +148,73 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
     return x * per + (x < rem ? x : rem) + local;
 }
 
+// ---------------------------------------------------------------------------
+// Sorted copies for the long-range pass: k_s[b][h][s] = k[b][h][perm[b][s]]
+// (same for v), one 16-byte chunk per thread, and spos[b][s] = perm[b][s]
+// followed by KPOS_PAD padding slots (kNoPos), written by the kv-head-0 grid
+// row.
+__global__ __launch_bounds__(256) void attn_gather_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const int32_t* __restrict__ perm,
+                                                          int n, int Hkv, int D,
+                                                          uint16_t* __restrict__ ks,
+                                                          uint16_t* __restrict__ vs,
+                                                          int32_t* __restrict__ spos) {
+    const int nch = D / 8;
+    const int bh = blockIdx.y, b = bh / Hkv, h = bh % Hkv;
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t s = x / nch;
+    const int c = (int)(x % nch);
+    if (s >= n + KPOS_PAD) return;
+    if (s >= n) {
+        if (h == 0 && c == 0) spos[(int64_t)b * (n + KPOS_PAD) + s] = kNoPos;
+        return;
+    }
+    const int pos = clampi(perm[(int64_t)b * n + s], 0, n - 1);
+    if (h == 0 && c == 0) spos[(int64_t)b * (n + KPOS_PAD) + s] = pos;
+    const int64_t base = (int64_t)bh * n * D;
+    *reinterpret_cast<u32x4*>(ks + base + s * D + c * 8) =
+        *reinterpret_cast<const u32x4*>(k + base + (int64_t)pos * D + c * 8);
+    *reinterpret_cast<u32x4*>(vs + base + s * D + c * 8) =
+        *reinterpret_cast<const u32x4*>(v + base + (int64_t)pos * D + c * 8);
+}
+
 // Key slots [ob, kend) that group g contributes to the long-range pass of
 // the sorted query slots [s0, s1): the group's segment [ob, oe) of perm, cut
 // at the first slot whose position is >= (largest query position of g in the
 // tile) - w. Positions increase inside a segment, so that cut is a binary
 // search, and no later slot of the segment can pair with any query of g here.
+// kfull: slots below it pair with every query of g in the tile (position
+// below (smallest query position) - w).
+__device__ __forceinline__ int first_slot_at_or_above(const int32_t* perm_b, int lo, int hi,
+                                                      int bound) {
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (perm_b[mid] < bound) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
 __device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32_t* offb, int n,
-                                              int w, int s0, int s1, int g, int& ob, int& kend) {
+                                              int w, int s0, int s1, int g, int& ob, int& kend,
+                                              int& kfull) {
     ob = clampi(offb[g], 0, n);
     const int oe = clampi(offb[g + 1], ob, n);
     const int qlo = max(s0, ob), qhi = min(s1, oe);
     kend = ob;
+    kfull = ob;
     if (qlo < qhi) {
         const int maxpos = clampi(perm_b[qhi - 1], 0, n - 1);
-        int lo = ob, hi = qhi;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (perm_b[mid] < maxpos - w) lo = mid + 1; else hi = mid;
-        }
-        kend = lo;
+        const int minpos = clampi(perm_b[qlo], 0, n - 1);
+        kend = first_slot_at_or_above(perm_b, ob, qhi, maxpos - w);
+        kfull = first_slot_at_or_above(perm_b, ob, kend, minpos - w);
     }
 }
 
 // Tile plan of the long-range pass, once per (batch, sorted query tile) and
 // shared by every kv head: record = {nseg (-1: more than SEGCAP groups, the
 // attention kernel then derives its segments itself), first group, all query
-// rows in one group, smallest query position, (ob, kend) per group}.
+// rows in one group, key tiles in total, then per group (ob, kend, first
+// tile index, kfull)}.
 __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restrict__ ids,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets,
@@ -192,27 +235,36 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
         rec[0] = -1;
         return;
     }
+    int run = 0;
     for (int t = 0; t < nseg; ++t) {
-        int ob, kend;
-        segment_range(perm_b, offb, n, w, s0, s1, gf + t, ob, kend);
-        rec[4 + 2 * t] = ob;
-        rec[5 + 2 * t] = kend;
+        int ob, kend, kfull;
+        segment_range(perm_b, offb, n, w, s0, s1, gf + t, ob, kend, kfull);
+        rec[4 + 4 * t] = ob;
+        rec[5 + 4 * t] = kend;
+        rec[6 + 4 * t] = run;
+        rec[7 + 4 * t] = kfull;
+        run += (kend - ob + BN - 1) / BN;
     }
     const int ob0 = clampi(offb[gf], 0, n), oe0 = clampi(offb[gf + 1], ob0, n);
     rec[0] = nseg;
     rec[1] = gf;
     rec[2] = (s0 >= ob0 && s1 <= oe0) ? 1 : 0;
-    rec[3] = clampi(perm_b[s0], 0, n - 1);
+    rec[3] = run;
 }
 
+// ---------------------------------------------------------------------------
 template <int D, int PHASE>
 __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     using G = Geom<D>;
     constexpr bool SORTED = PHASE == kLongRange;
-    __shared__ __attribute__((aligned(1024))) unsigned char buf0[2 * G::TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char buf1[2 * G::TILEB];
-    __shared__ int kpos0[BN], kpos1[BN];
-    __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1];
+    // smem = [K/V buffer 0 | K/V buffer 1]; buffer 1 also stages the Q tile in
+    // the prologue, and the whole block stages the output rows in the epilogue.
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
+    unsigned char* const buf0 = smem;
+    unsigned char* const buf1 = smem + 2 * G::TILEB;
+    __shared__ __attribute__((aligned(1024))) int kpos0[KPOS_PAD], kpos1[KPOS_PAD];
+    __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1], seg_kfull[MAXSEG];
+    __shared__ int rowpos[ROWS];  // sequence position of each query row (sorted pass)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 31, hh = lane >> 5;
@@ -233,20 +285,16 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     const int s_row = tile * a.TT + tok;
     const bool rvalid = s_row < a.n;
     int pos_i = rvalid ? s_row : 0;
-    int g_i = -1;
-    if (SORTED && rvalid) {
-        pos_i = clampi(a.perm[bn + s_row], 0, a.n - 1);
-        g_i = clampi(a.ids[bn + pos_i], 0, a.K - 1);
-    }
+    if (SORTED && rvalid) pos_i = clampi(a.perm[bn + s_row], 0, a.n - 1);
 
     const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * a.n * D;
     const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * a.n * D;
 
-    // ---- the key tiles this workgroup visits: ntl tiles, tile tau at
-    // ---- key slot kt0(tau), valid slots below kend(tau).
+    // ---- the key tiles this workgroup visits: ntl tiles, tile tau at key
+    // ---- slot kt0(tau), valid slots below kend(tau).
     int ntl = 0;
     int kstart = 0, kend0 = 0;               // sequence-order passes
-    int gfirst = 0, minpos = 0;              // long-range pass
+    int gfirst = 0, g_i = -1;                // long-range pass
     bool rows_one_group = false;
     if (!SORTED) {
         const int q0 = tile * a.TT;
@@ -257,58 +305,72 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     } else {
         const int s0 = tile * a.TT;
         const int s1 = min(a.n, s0 + a.TT);
-        const int32_t* offb = a.offsets + (int64_t)b * (a.K + 1);
-        const int32_t* rec = a.plan ? a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS : nullptr;
-        int nseg = rec ? rec[0] : -1;
+        const int32_t* rec = a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS;
+        if (hh == 0) rowpos[R] = pos_i;  // published by the barrier below
+        int nseg = rec[0];
         if (nseg >= 0) {
             nseg = min(nseg, SEGCAP);
             gfirst = clampi(rec[1], 0, a.K - 1);
             rows_one_group = rec[2] != 0;
-            minpos = clampi(rec[3], 0, a.n - 1);
             if (tid < nseg) {
-                seg_ob[tid] = clampi(rec[4 + 2 * tid], 0, a.n);
-                seg_kend[tid] = clampi(rec[5 + 2 * tid], seg_ob[tid], a.n);
+                const int ob = clampi(rec[4 + 4 * tid], 0, a.n);
+                const int kend = clampi(rec[5 + 4 * tid], ob, a.n);
+                seg_ob[tid] = ob;
+                seg_kend[tid] = kend;
+                seg_t0[tid] = rec[6 + 4 * tid];
+                seg_kfull[tid] = clampi(rec[7 + 4 * tid], ob, kend);
             }
+            if (tid == 0) seg_t0[nseg] = rec[3];
+            __syncthreads();
         } else {
+            // More groups in this tile than a plan record holds: derive the
+            // segments here (every tile of them is treated as partial).
+            const int32_t* offb = a.offsets + (int64_t)b * (a.K + 1);
             gfirst = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
             const int glast =
                 clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1);
             nseg = glast - gfirst + 1;
             if (tid < nseg) {
-                int ob, kend;
-                segment_range(a.perm + bn, offb, a.n, a.w, s0, s1, gfirst + tid, ob, kend);
+                int ob, kend, kfull;
+                segment_range(a.perm + bn, offb, a.n, a.w, s0, s1, gfirst + tid, ob, kend, kfull);
                 seg_ob[tid] = ob;
                 seg_kend[tid] = kend;
+                seg_kfull[tid] = ob;
             }
-            const int ob0 = clampi(offb[gfirst], 0, a.n);
-            const int oe0 = clampi(offb[gfirst + 1], ob0, a.n);
-            rows_one_group = (s0 >= ob0) && (s1 <= oe0);
-            minpos = clampi(a.perm[bn + s0], 0, a.n - 1);
-        }
-        __syncthreads();
-        if (tid == 0) {
-            int run = 0;
-            for (int t = 0; t < nseg; ++t) {
-                seg_t0[t] = run;
-                run += (seg_kend[t] - seg_ob[t] + BN - 1) / BN;
+            __syncthreads();
+            if (tid == 0) {
+                int run = 0;
+                for (int t = 0; t < nseg; ++t) {
+                    seg_t0[t] = run;
+                    run += (seg_kend[t] - seg_ob[t] + BN - 1) / BN;
+                }
+                seg_t0[nseg] = run;
             }
-            seg_t0[nseg] = run;
+            __syncthreads();
         }
-        __syncthreads();
         ntl = seg_t0[nseg];
+        // the row's group: segments are consecutive in sorted order
+        if (rvalid) {
+            int t = 0;
+            while (t + 1 < nseg && seg_ob[t + 1] <= s_row) ++t;
+            g_i = gfirst + t;
+        }
     }
 
-    // Tile tau -> (segment, first key slot, end of valid slots).
-    int seg_cur = 0;
-    auto locate = [&](int tau, int& seg, int& kt0, int& kend) {
+    // Tile tau -> (segment, first key slot, end of valid slots, all pairs kept).
+    auto locate = [&](int tau, int& seg, int& kt0, int& kend, bool& full) {
         if (!SORTED) {
             seg = 0;
             kt0 = kstart + tau * BN;
             kend = kend0;
+            const int q0 = tile * a.TT;
+            full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
+                   (PHASE == kDense || kend - 1 - kt0 <= a.w);
         } else {
             while (seg_t0[seg + 1] <= tau) ++seg;
             kt0 = seg_ob[seg] + (tau - seg_t0[seg]) * BN;
             kend = seg_kend[seg];
+            full = rows_one_group && (kt0 + BN <= seg_kfull[seg]);
         }
     };
 
@@ -321,32 +383,21 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         crow[i] = o / G::ROWB;
         cch[i] = logical_chunk<D>(crow[i], (o % G::ROWB) / 16);
     }
-    int cpos[G::NI];  // sorted pass: positions of the rows of the next copy
-
-    auto fetch_pos = [&](int tau) {
-        int seg = seg_cur, kt0, kend;
-        locate(tau, seg, kt0, kend);
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i)
-            cpos[i] = a.perm[bn + min(kt0 + crow[i], kend - 1)];
-    };
+    int seg_issue = 0, seg_cur = 0;
     auto issue = [&](int tau, unsigned char* bufp, int* kposp) {
-        int seg = seg_cur, kt0, kend;
-        locate(tau, seg, kt0, kend);
+        int kt0, kend;
+        bool full;
+        locate(tau, seg_issue, kt0, kend, full);
 #pragma unroll
         for (int i = 0; i < G::NI; ++i) {
-            int pos;
-            if (SORTED) {
-                pos = clampi(cpos[i], 0, a.n - 1);
-                if ((16 * lane) % G::ROWB == 0)
-                    kposp[crow[i]] = (kt0 + crow[i] < kend) ? pos : 0x7fffffff;
-            } else {
-                pos = min(kt0 + crow[i], kend - 1);
-            }
-            const int64_t go = (int64_t)pos * D + cch[i] * 8;
+            const int slot = min(kt0 + crow[i], kend - 1);
+            const int64_t go = (int64_t)slot * D + cch[i] * 8;
             copy16(kbase + go, bufp + (wave * G::NI + i) * 1024);
             copy16(vbase + go, bufp + G::TILEB + (wave * G::NI + i) * 1024);
         }
+        // positions of the tile's key slots, for the mask of a partial tile
+        if (SORTED && !full && wave == 0)
+            copy16(a.spos + (int64_t)b * (a.n + KPOS_PAD) + kt0 + 4 * lane, kposp);
     };
 
     // LDS offsets of this lane's operand reads (tile-relative).
@@ -374,7 +425,8 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
 
     auto compute = [&](int tau, const unsigned char* bufp, const int* kposp) {
         int kt0, kend;
-        locate(tau, seg_cur, kt0, kend);
+        bool full;
+        locate(tau, seg_cur, kt0, kend, full);
         // S^T = K Q^T for two 32-key blocks.
         f32x16 st[2];
 #pragma unroll
@@ -389,18 +441,8 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
             }
         }
 
-        // Mask (boundary tiles only). Lane holds keys kidx = kb*32 +
+        // Mask (partial tiles only). Lane holds keys kidx = kb*32 +
         // 8*(e>>2) + 4*hh + (e&3) of its row.
-        bool full;
-        if (!SORTED) {
-            const int q0 = tile * a.TT;
-            const int qlast = kend - 1;
-            full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
-                   (PHASE == kDense || qlast - kt0 <= a.w);
-        } else {
-            full = rows_one_group && seg_cur == 0 && (kt0 + BN <= kend) &&
-                   (minpos - kposp[BN - 1] > a.w);
-        }
         if (!full) {
             const int seg_g = gfirst + seg_cur;
 #pragma unroll
@@ -475,16 +517,8 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
             }
     };
 
-    // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
-    // ---- compute of tile tau; one barrier per tile.
-    if (ntl > 0) {
-        if (SORTED) {
-            fetch_pos(0);
-            wait_vm();
-        }
-        issue(0, buf0, kpos0);
-        if (SORTED && ntl > 1) fetch_pos(1);
-    }
+    // ---- prologue: first K/V copy in flight, then the row data.
+    if (ntl > 0) issue(0, buf0, kpos0);
     // Window pass: start the online softmax from the long-range partial. A
     // normalised partial O_g with log2-sum-exp L_g is exactly the state
     // (acc = O_g, l = 1, reference max = L_g), so the window keys accumulate
@@ -507,83 +541,97 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
             l_run = (hh == 0) ? 1.0f : 0.0f;  // halves are summed at the end
         }
     }
-    // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
-    const int64_t qrow_off = (((int64_t)b * a.Hq + h) * a.n + pos_i) * D;
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-        if (rvalid) {
-            qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qrow_off + 16 * ks + 8 * hh);
+    // Q tile (128 rows x ROWB bytes) -> buffer 1 with 1 KB copies, each row
+    // one contiguous run in HBM (rows past n copy a valid row; never stored).
+    auto row_of = [&](int r, int& hr, int& pr) {   // query row r -> (head, position)
+        hr = kvh * a.hpk + slice * a.G + r / a.TT;
+        if (SORTED) {
+            pr = rowpos[r];
         } else {
+            pr = min(tile * a.TT + r % a.TT, a.n - 1);
+        }
+    };
 #pragma unroll
-            for (int t = 0; t < 8; ++t) qf[ks][t] = (__bf16)0.0f;
-        }
+    for (int c = 0; c < 2 * G::NI; ++c) {
+        const int o = (wave * 2 * G::NI + c) * 1024 + 16 * lane;
+        const int r = o / G::ROWB;
+        int hr, pr;
+        row_of(r, hr, pr);
+        const int ch = logical_chunk<D>(r, (o % G::ROWB) / 16);
+        copy16(a.q + (((int64_t)b * a.Hq + hr) * a.n + pr) * D + ch * 8,
+               buf1 + (wave * 2 * G::NI + c) * 1024);
     }
+    wait_vm();
+    __syncthreads();
+    // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(buf1 + lds_off<D>(R, 2 * ks + hh));
+    // buffer 1 is refilled right after the next barrier: the reads must be done
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-    if (ntl > 0) {
-        for (int tau = 0; tau < ntl; tau += 2) {
-            wait_vm();
-            __syncthreads();
-            if (tau + 1 < ntl) {
-                issue(tau + 1, buf1, kpos1);
-                if (SORTED && tau + 2 < ntl) fetch_pos(tau + 2);
-            }
-            compute(tau, buf0, kpos0);
-            if (tau + 1 >= ntl) break;
-            wait_vm();
-            __syncthreads();
-            if (tau + 2 < ntl) {
-                issue(tau + 2, buf0, kpos0);
-                if (SORTED && tau + 3 < ntl) fetch_pos(tau + 3);
-            }
-            compute(tau + 1, buf1, kpos1);
-        }
+    // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
+    // ---- compute of tile tau; one barrier per tile.
+    for (int tau = 0; tau < ntl; tau += 2) {
+        wait_vm();
+        __syncthreads();
+        if (tau + 1 < ntl) issue(tau + 1, buf1, kpos1);
+        compute(tau, buf0, kpos0);
+        if (tau + 1 >= ntl) break;
+        wait_vm();
+        __syncthreads();
+        if (tau + 2 < ntl) issue(tau + 2, buf0, kpos0);
+        compute(tau + 1, buf1, kpos1);
     }
 
     // Epilogue. Lane holds rows' O^T entries d = db*32 + 8*i + 4*hh + j at
-    // acc[db][4*i + j]; l_run covers this lane half's keys.
+    // acc[db][4*i + j]; l_run covers this lane half's keys. The rows are
+    // written to LDS (chunk slots XOR-swizzled by row) and stored as whole
+    // contiguous rows.
     const float l_tot = l_run + other_half(l_run);
     const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
-    if (!rvalid) return;
+    float scale_o;
+    int esize;
     if (SORTED) {
-        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        float* orow = a.og + row * D;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 o = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv,
-                           acc[db][4 * i + 2] * inv, acc[db][4 * i + 3] * inv};
-                *reinterpret_cast<f32x4*>(orow + db * 32 + 8 * i + 4 * hh) = o;
-            }
-        if (hh == 0) a.lseg[row] = l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf;
-        return;
+        scale_o = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        esize = 4;
+        if (rvalid && hh == 0) a.lseg[row] = l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf;
+    } else {
+        scale_o = 1.0f / l_tot;
+        esize = a.out_f32 ? 4 : 2;
+        if (rvalid && hh == 0 && a.lse) a.lse[row] = (m_ref + __log2f(l_tot)) * kLn2;
     }
-    const float lse2 = m_ref + __log2f(l_tot);
-    const float cw = 1.0f / l_tot;
+    const int RB = D * esize;          // bytes per output row
+    const int nchk = RB / 16;          // 16-byte chunks per row
+    const int cmask = (nchk < 16 ? nchk : 16) - 1;
+    __syncthreads();                   // all waves are done with the K/V buffers
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int d0 = db * 32 + 8 * i + 4 * hh;
-            const f32x4 o = {acc[db][4 * i] * cw, acc[db][4 * i + 1] * cw, acc[db][4 * i + 2] * cw,
-                             acc[db][4 * i + 3] * cw};
-            if (a.out_f32) {
-                *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + row * D + d0) = o;
+            const int qd = db * 8 + 2 * i + hh;   // quad index: d = 4*qd .. +3
+            const f32x4 o = {acc[db][4 * i] * scale_o, acc[db][4 * i + 1] * scale_o,
+                             acc[db][4 * i + 2] * scale_o, acc[db][4 * i + 3] * scale_o};
+            if (esize == 4) {
+                *reinterpret_cast<f32x4*>(smem + R * RB + ((qd ^ (R & cmask)) << 4)) = o;
             } else {
                 const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-                *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.out) + row * D + d0) = ob;
+                const int half = (qd & 1) ^ ((R >> 4) & 1);
+                *reinterpret_cast<bf16x4*>(smem + R * RB + (((qd >> 1) ^ (R & cmask)) << 4) +
+                                           half * 8) = ob;
             }
         }
-    if (hh == 0 && a.lse) a.lse[row] = lse2 * kLn2;
-}
-
-// Query heads packed into one workgroup: the largest power of two <= 8 that
-// divides Hq/Hkv. All packed heads share the kv head, the token set and the
-// mask, so each K/V tile staged in LDS serves G*TT = 128 query rows.
-int heads_per_wg(int hpk) {
-    int g = 1;
-    while (g < 8 && hpk % (2 * g) == 0) g *= 2;
-    return g;
+    __syncthreads();
+    char* dst = SORTED ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
+    for (int idx = tid; idx < ROWS * nchk; idx += NT) {
+        const int r = idx / nchk, c = idx % nchk;
+        if (tile * a.TT + r % a.TT >= a.n) continue;   // rows past the sequence end
+        int hr, pr;
+        row_of(r, hr, pr);
+        u32x4 val = *reinterpret_cast<const u32x4*>(smem + r * RB + ((c ^ (r & cmask)) << 4));
+        if (esize == 2 && ((r >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
+        *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * a.n + pr) * RB) + c * 16) = val;
+    }
 }
 
 AttnArgs make_args(const AttnProblem& p) {
@@ -603,7 +651,7 @@ AttnArgs make_args(const AttnProblem& p) {
     a.K = p.K;
     a.w = p.w;
     a.hpk = p.Hq / p.Hkv;
-    a.G = heads_per_wg(a.hpk);
+    a.G = attn_heads_per_wg(a.hpk);
     a.TT = ROWS / a.G;
     a.nslices = a.hpk / a.G;
     a.ntiles = (p.n + a.TT - 1) / a.TT;
@@ -611,12 +659,12 @@ AttnArgs make_args(const AttnProblem& p) {
     a.sl2 = p.scale * 1.44269504088896340736f;
     a.out_f32 = p.out_f32;
     if (p.workspace) {
-        char* ws = static_cast<char*>(p.workspace);
-        const size_t og_bytes = align_up((size_t)p.B * p.Hq * p.n * p.d * 4);
-        const size_t lse_bytes = align_up((size_t)p.B * p.Hq * p.n * 4);
-        a.og = reinterpret_cast<float*>(ws);
-        a.lseg = reinterpret_cast<float*>(ws + og_bytes);
-        a.plan = reinterpret_cast<const int32_t*>(ws + og_bytes + lse_bytes);
+        const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d);
+        char* base = static_cast<char*>(p.workspace);
+        a.og = reinterpret_cast<float*>(base + ws.og);
+        a.lseg = reinterpret_cast<float*>(base + ws.lseg);
+        a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
+        a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
     }
     return a;
 }
@@ -635,27 +683,45 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
 
 }  // namespace
 
+int attn_heads_per_wg(int hpk) {
+    // Query heads packed into one workgroup: the largest power of two <= 8
+    // that divides Hq/Hkv. All packed heads share the kv head, the token set
+    // and the mask, so each K/V tile staged in LDS serves G*TT = 128 rows.
+    int g = 1;
+    while (g < 8 && hpk % (2 * g) == 0) g *= 2;
+    return g;
+}
+
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     AttnArgs a = make_args(p);
+    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d);
+    char* base = static_cast<char*>(p.workspace);
+    uint16_t* ks = reinterpret_cast<uint16_t*>(base + ws.ks);
+    uint16_t* vs = reinterpret_cast<uint16_t*>(base + ws.vs);
+    const int64_t chunks = (int64_t)(p.n + KPOS_PAD) * (p.d / 8);
+    hipLaunchKernelGGL(attn_gather_kernel, dim3((unsigned)((chunks + 255) / 256), p.B * p.Hkv),
+                       dim3(256), 0, stream, p.k, p.v, p.perm, p.n, p.Hkv, p.d, ks, vs, a.spos);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
                        p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT, a.ntiles,
                        const_cast<int32_t*>(a.plan));
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
+    a.k = ks;
+    a.v = vs;
     return launch<kLongRange>(a, p.d, stream);
 }
 
 hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream) {
     AttnArgs a = make_args(p);
-    a.plan = nullptr;
     a.merge = merge && attn_has_long_range(p.n, p.w) ? 1 : 0;
     return launch<kWindow>(a, p.d, stream);
 }
 
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream) {
     AttnArgs a = make_args(p);
-    a.plan = nullptr;
     a.merge = 0;
     a.w = p.n;
     return launch<kDense>(a, p.d, stream);

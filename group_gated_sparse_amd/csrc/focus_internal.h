@@ -46,13 +46,37 @@ struct AttnProblem {
 
 // True when some pair further apart than the window can exist (n - 1 > w).
 inline bool attn_has_long_range(int n, int w) { return (int64_t)n - 1 > (int64_t)w; }
-// Long-range partial output (fp32 [B][Hq][n][d]), its log2-sum-exp (fp32
-// [B][Hq][n]) and the tile plan (64 bytes per sorted query tile of >= 16
-// tokens).
-inline size_t attn_workspace(int B, int Hq, int n, int d, int w) {
+
+constexpr int KPOS_PAD = 256;   // padding slots after the sorted positions (one 1 KB copy)
+constexpr int SEGCAP = 7;       // group segments stored per planned query tile
+constexpr int PLAN_INTS = 32;   // ints per plan record (4 + 4 * SEGCAP)
+
+int attn_heads_per_wg(int hpk);
+inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_wg(Hq / Hkv); }
+
+// Long-range workspace, byte offsets: partial output (fp32 [B][Hq][n][d]),
+// its log2-sum-exp (fp32 [B][Hq][n]), the tile plan, group-sorted copies of
+// K and V (bf16 [B][Hkv][n][d]) and the sorted positions (int32 [B][n + pad]).
+struct AttnWorkspace {
+    size_t og, lseg, plan, ks, vs, spos, total;
+};
+inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d) {
+    AttnWorkspace w{};
+    const int TT = attn_tokens_per_tile(Hq, Hkv);
+    const size_t ntiles = (size_t)(n + TT - 1) / TT;
+    size_t off = 0;
+    w.og = off;   off += align_up((size_t)B * Hq * n * d * 4);
+    w.lseg = off; off += align_up((size_t)B * Hq * n * 4);
+    w.plan = off; off += align_up((size_t)B * ntiles * PLAN_INTS * 4);
+    w.ks = off;   off += align_up((size_t)B * Hkv * n * d * 2);
+    w.vs = off;   off += align_up((size_t)B * Hkv * n * d * 2);
+    w.spos = off; off += align_up((size_t)B * (n + KPOS_PAD) * 4);
+    w.total = off;
+    return w;
+}
+inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w) {
     if (!attn_has_long_range(n, w)) return 0;
-    return align_up((size_t)B * Hq * n * d * 4) + align_up((size_t)B * Hq * n * 4) +
-           align_up((size_t)B * ((n + 15) / 16) * 64);
+    return attn_workspace_layout(B, Hq, Hkv, n, d).total;
 }
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream);
