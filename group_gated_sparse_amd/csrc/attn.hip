@@ -15,7 +15,8 @@
 //     the group with position below (largest query position) - w). The
 //     attention kernel, for each tile of 128/G sorted tokens x G query heads
 //     sharing one kv head, visits only those key tiles, so every visited
-//     tile is dense in one group. It writes the normalised partial output and
+//     tile is dense in one group. It writes the normalised partial output (in
+//     bf16, as a flash-attention call returns it) and
 //     its log2-sum-exp per row.
 //   window pass (sequence order): for each tile of tokens, the key band
 //     [q0 - w, q0 + TT - 1]. The long-range partial is merged by starting
@@ -52,7 +53,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 64;       // keys per tile
 constexpr int NT = 256;      // threads per workgroup
 constexpr int ROWS = 128;    // query rows per workgroup (4 waves x 32)
 constexpr int MAXSEG = 64;   // groups present in one sorted query tile (K <= 64)
@@ -72,7 +72,7 @@ struct AttnArgs {
     const int32_t* offsets;
     const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
     int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
-    float* og;              // long-range partial output [B][Hq][n][D] (normalised)
+    __bf16* og;             // long-range partial output [B][Hq][n][D] (normalised, bf16)
     float* lseg;            // long-range partial log2-sum-exp [B][Hq][n] (-inf: no key)
     void* out;
     float* lse;
@@ -88,14 +88,28 @@ struct AttnArgs {
     int merge;
 };
 
-template <int D>
+// Workgroups per CU each attention kernel is built for. Three lets one
+// workgroup wait on memory while two compute; it needs <= 168 registers per
+// lane, which the long-range and dense passes at d = 128 exceed (their extra
+// masking state would spill), so those stay at two.
+constexpr int attn_occupancy(int D, int PHASE) { return (D == 128 && PHASE != 0) ? 2 : 3; }
+// Keys per tile: 32 where a 64-key tile would not leave room for three
+// workgroups (LDS and registers), else 64.
+constexpr int attn_tile_keys(int D, int PHASE) {
+    return (D != 32 && attn_occupancy(D, PHASE) == 3) ? 32 : 64;
+}
+
+template <int D, int BN_ = 64>
 struct Geom {
+    static constexpr int BN = BN_;                            // keys per tile
+    static constexpr int KB = BN / 32;                        // 32-key MFMA blocks per tile
     static constexpr int NCH = D / 8;                         // 16-byte chunks per row
     static constexpr int ROWB = D * 2;                        // bytes per row
     static constexpr int TILEB = BN * ROWB;                   // bytes of one K or V tile
     static constexpr int NI = TILEB / (4 * 1024);             // 1 KB copies per wave per tile
     static constexpr int KS = D / 16;                         // k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;                         // 32-wide blocks of O^T
+    static constexpr bool QSTAGE = 128 * ROWB <= 2 * TILEB;   // Q tile fits buffer 1
 };
 
 // LDS tile layout: row r (one key) is ROWB contiguous bytes; its 16-byte
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets,
                                                         int n, int K, int w, int TT, int ntiles,
-                                                        int32_t* __restrict__ plan) {
+                                                        int bn_keys, int32_t* __restrict__ plan) {
     const int b = blockIdx.y;
     const int tile = blockIdx.x * 256 + threadIdx.x;
     if (tile >= ntiles) return;
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
         rec[5 + 4 * t] = kend;
         rec[6 + 4 * t] = run;
         rec[7 + 4 * t] = kfull;
-        run += (kend - ob + BN - 1) / BN;
+        run += (kend - ob + bn_keys - 1) / bn_keys;
     }
     const int ob0 = clampi(offb[gf], 0, n), oe0 = clampi(offb[gf + 1], ob0, n);
     rec[0] = nseg;
@@ -254,8 +268,9 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
 
 // ---------------------------------------------------------------------------
 template <int D, int PHASE>
-__global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
-    using G = Geom<D>;
+__global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(AttnArgs a) {
+    using G = Geom<D, attn_tile_keys(D, PHASE)>;
+    constexpr int BN = G::BN;
     constexpr bool SORTED = PHASE == kLongRange;
     // smem = [K/V buffer 0 | K/V buffer 1]; buffer 1 also stages the Q tile in
     // the prologue, and the whole block stages the output rows in the epilogue.
@@ -427,10 +442,10 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         int kt0, kend;
         bool full;
         locate(tau, seg_cur, kt0, kend, full);
-        // S^T = K Q^T for two 32-key blocks.
-        f32x16 st[2];
+        // S^T = K Q^T for the tile's 32-key blocks.
+        f32x16 st[G::KB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < G::KB; ++kb) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) st[kb][e] = 0.0f;
 #pragma unroll
@@ -446,7 +461,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         if (!full) {
             const int seg_g = gfirst + seg_cur;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int kidx = kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
@@ -464,7 +479,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         // Online softmax with a lagging reference max.
         float tmax = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, st[kb][e]);
         tmax = fmaxf(tmax, other_half(tmax)) * a.sl2;
@@ -483,9 +498,9 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         }
         const float m_use = (m_ref == kNegInf) ? 0.0f : m_ref;
         float psum = 0.0f;
-        bf16x8 pf[2][2];
+        bf16x8 pf[G::KB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         // 16-lane group addressing row key0 + m/4, columns 4*(m%4) .. +3 of
         // its 16-column half.
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp) {
                 const unsigned char* vb = bufp + (kb * 32 + 16 * sp) * G::ROWB;
@@ -528,21 +543,19 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
         const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
         const float lg = a.lseg[row];
         if (lg != kNegInf) {
-            const float* grow_p = a.og + row * D;
+            const __bf16* grow_p = a.og + row * D;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const f32x4 gv = *reinterpret_cast<const f32x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
+                    const bf16x4 gv = *reinterpret_cast<const bf16x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[db][4 * i + j] = gv[j];
+                    for (int j = 0; j < 4; ++j) acc[db][4 * i + j] = (float)gv[j];
                 }
             m_ref = lg;
             l_run = (hh == 0) ? 1.0f : 0.0f;  // halves are summed at the end
         }
     }
-    // Q tile (128 rows x ROWB bytes) -> buffer 1 with 1 KB copies, each row
-    // one contiguous run in HBM (rows past n copy a valid row; never stored).
     auto row_of = [&](int r, int& hr, int& pr) {   // query row r -> (head, position)
         hr = kvh * a.hpk + slice * a.G + r / a.TT;
         if (SORTED) {
@@ -551,24 +564,34 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
             pr = min(tile * a.TT + r % a.TT, a.n - 1);
         }
     };
+    if (G::QSTAGE) {
+        // Q tile (128 rows x ROWB bytes) -> buffer 1 with 1 KB copies, each row
+        // one contiguous run in HBM (rows past n copy a valid row; never stored).
 #pragma unroll
-    for (int c = 0; c < 2 * G::NI; ++c) {
-        const int o = (wave * 2 * G::NI + c) * 1024 + 16 * lane;
-        const int r = o / G::ROWB;
-        int hr, pr;
-        row_of(r, hr, pr);
-        const int ch = logical_chunk<D>(r, (o % G::ROWB) / 16);
-        copy16(a.q + (((int64_t)b * a.Hq + hr) * a.n + pr) * D + ch * 8,
-               buf1 + (wave * 2 * G::NI + c) * 1024);
+        for (int c = 0; c < 2 * G::NI; ++c) {
+            const int o = (wave * 2 * G::NI + c) * 1024 + 16 * lane;
+            const int r = o / G::ROWB;
+            int hr, pr;
+            row_of(r, hr, pr);
+            const int ch = logical_chunk<D>(r, (o % G::ROWB) / 16);
+            copy16(a.q + (((int64_t)b * a.Hq + hr) * a.n + pr) * D + ch * 8,
+                   buf1 + (wave * 2 * G::NI + c) * 1024);
+        }
+        wait_vm();
+        __syncthreads();
+        // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(buf1 + lds_off<D>(R, 2 * ks + hh));
+        // buffer 1 is refilled right after the next barrier: the reads must be done
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    } else {
+        // Q^T fragments straight from HBM: Q[row][16*ks + 8*hh .. +8].
+        const int64_t qrow_off = (((int64_t)b * a.Hq + h) * a.n + pos_i) * D;
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks)
+            qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qrow_off + 16 * ks + 8 * hh);
     }
-    wait_vm();
-    __syncthreads();
-    // Q^T fragments: lane holds Q[row][16*ks + 8*hh .. +8] for every k-step.
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks)
-        qf[ks] = *reinterpret_cast<const bf16x8*>(buf1 + lds_off<D>(R, 2 * ks + hh));
-    // buffer 1 is refilled right after the next barrier: the reads must be done
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
     // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
     // ---- compute of tile tau; one barrier per tile.
@@ -594,7 +617,7 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     int esize;
     if (SORTED) {
         scale_o = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        esize = 4;
+        esize = 2;   // bf16 partial, as a flash-attention call would return it
         if (rvalid && hh == 0) a.lseg[row] = l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf;
     } else {
         scale_o = 1.0f / l_tot;
@@ -604,33 +627,41 @@ __global__ __launch_bounds__(NT, 2) void attn_kernel(AttnArgs a) {
     const int RB = D * esize;          // bytes per output row
     const int nchk = RB / 16;          // 16-byte chunks per row
     const int cmask = (nchk < 16 ? nchk : 16) - 1;
-    __syncthreads();                   // all waves are done with the K/V buffers
-#pragma unroll
-    for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int qd = db * 8 + 2 * i + hh;   // quad index: d = 4*qd .. +3
-            const f32x4 o = {acc[db][4 * i] * scale_o, acc[db][4 * i + 1] * scale_o,
-                             acc[db][4 * i + 2] * scale_o, acc[db][4 * i + 3] * scale_o};
-            if (esize == 4) {
-                *reinterpret_cast<f32x4*>(smem + R * RB + ((qd ^ (R & cmask)) << 4)) = o;
-            } else {
-                const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
-                const int half = (qd & 1) ^ ((R >> 4) & 1);
-                *reinterpret_cast<bf16x4*>(smem + R * RB + (((qd >> 1) ^ (R & cmask)) << 4) +
-                                           half * 8) = ob;
-            }
-        }
-    __syncthreads();
+    const int rpp = min(ROWS, (4 * G::TILEB) / RB);   // rows staged per pass
     char* dst = SORTED ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
-    for (int idx = tid; idx < ROWS * nchk; idx += NT) {
-        const int r = idx / nchk, c = idx % nchk;
-        if (tile * a.TT + r % a.TT >= a.n) continue;   // rows past the sequence end
-        int hr, pr;
-        row_of(r, hr, pr);
-        u32x4 val = *reinterpret_cast<const u32x4*>(smem + r * RB + ((c ^ (r & cmask)) << 4));
-        if (esize == 2 && ((r >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
-        *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * a.n + pr) * RB) + c * 16) = val;
+    for (int r0 = 0; r0 < ROWS; r0 += rpp) {
+        __syncthreads();               // K/V buffers (or the previous pass) are free
+        if (R >= r0 && R < r0 + rpp) {
+            const int rs = R - r0;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int qd = db * 8 + 2 * i + hh;   // quad index: d = 4*qd .. +3
+                    const f32x4 o = {acc[db][4 * i] * scale_o, acc[db][4 * i + 1] * scale_o,
+                                     acc[db][4 * i + 2] * scale_o, acc[db][4 * i + 3] * scale_o};
+                    if (esize == 4) {
+                        *reinterpret_cast<f32x4*>(smem + rs * RB + ((qd ^ (rs & cmask)) << 4)) = o;
+                    } else {
+                        const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
+                        const int half = (qd & 1) ^ ((rs >> 4) & 1);
+                        *reinterpret_cast<bf16x4*>(smem + rs * RB +
+                                                   (((qd >> 1) ^ (rs & cmask)) << 4) + half * 8) = ob;
+                    }
+                }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < rpp * nchk; idx += NT) {
+            const int rs = idx / nchk, c = idx % nchk;
+            const int r = r0 + rs;
+            if (tile * a.TT + r % a.TT >= a.n) continue;   // rows past the sequence end
+            int hr, pr;
+            row_of(r, hr, pr);
+            u32x4 val = *reinterpret_cast<const u32x4*>(smem + rs * RB + ((c ^ (rs & cmask)) << 4));
+            if (esize == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
+            *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * a.n + pr) * RB) + c * 16) =
+                val;
+        }
     }
 }
 
@@ -661,7 +692,7 @@ AttnArgs make_args(const AttnProblem& p) {
     if (p.workspace) {
         const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d);
         char* base = static_cast<char*>(p.workspace);
-        a.og = reinterpret_cast<float*>(base + ws.og);
+        a.og = reinterpret_cast<__bf16*>(base + ws.og);
         a.lseg = reinterpret_cast<float*>(base + ws.lseg);
         a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
         a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
@@ -706,6 +737,7 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
                        p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT, a.ntiles,
+                       attn_tile_keys(p.d, kLongRange),
                        const_cast<int32_t*>(a.plan));
     e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -54,7 +54,7 @@ constexpr int PLAN_INTS = 32;   // ints per plan record (4 + 4 * SEGCAP)
 int attn_heads_per_wg(int hpk);
 inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_wg(Hq / Hkv); }
 
-// Long-range workspace, byte offsets: partial output (fp32 [B][Hq][n][d]),
+// Long-range workspace, byte offsets: partial output (bf16 [B][Hq][n][d]),
 // its log2-sum-exp (fp32 [B][Hq][n]), the tile plan, group-sorted copies of
 // K and V (bf16 [B][Hkv][n][d]) and the sorted positions (int32 [B][n + pad]).
 struct AttnWorkspace {
@@ -65,7 +65,7 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d)
     const int TT = attn_tokens_per_tile(Hq, Hkv);
     const size_t ntiles = (size_t)(n + TT - 1) / TT;
     size_t off = 0;
-    w.og = off;   off += align_up((size_t)B * Hq * n * d * 4);
+    w.og = off;   off += align_up((size_t)B * Hq * n * d * 2);
     w.lseg = off; off += align_up((size_t)B * Hq * n * 4);
     w.plan = off; off += align_up((size_t)B * ntiles * PLAN_INTS * 4);
     w.ks = off;   off += align_up((size_t)B * Hkv * n * d * 2);

@@ -92,11 +92,11 @@ def test_workspace_sizes():
     # per-block group counts: B x ceil(n / 2048) x K int32, 256-byte aligned
     assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 256
     assert lib.focus_group_sort_workspace_bytes(1, 65536, 64) == 32 * 64 * 4
-    # long-range: partial fp32 [B][Hq][n][d] + lse fp32 [B][Hq][n] + 128 B plan per query
+    # long-range: partial bf16 [B][Hq][n][d] + lse fp32 [B][Hq][n] + 128 B plan per query
     # tile (here 64 tokens x 2 heads) + sorted bf16 K and V [B][Hkv][n][d] + int32 sorted
     # positions [B][n + 256], each region 256-byte aligned
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == (
-        256 * 2 * 32 * 4 + 2048 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4)
+        256 * 2 * 32 * 2 + 2048 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4)
     # no pair can be further apart than the window: no partial needed
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
