@@ -213,3 +213,54 @@ def test_whole_path_small_workloads(wl):
     ref, rlse, vis = oracle.attn(x["q"], x["k"], x["v"], gids, wl.w, wl.softmax_scale)
     check_attn(host(out).reshape(-1, wl.d), ref.reshape(-1, wl.d), wl.name)
     assert int(vis[:, 0].sum()) == visited_pairs(gids, wl.w)
+
+
+@pytest.mark.parametrize("wl", [workloads.ZIPF7B, workloads.LONG64K, workloads.GQA70B],
+                         ids=lambda w: w.name)
+def test_whole_path_full_size_sampled(wl):
+    """The benchmark's launch sequence at full size (assign, sort, long-range
+    pass, window merge; bf16 output), checked on sampled tokens and rows: ids
+    against the oracle on 4096 tokens, perm/offsets bit-exact on all tokens,
+    attention on the start, window edge, end and random rows of every head.
+    A second window merge with fp32 output and lse gets the strict bar."""
+    say(f"[full] {wl.name}: drawing inputs")
+    x = synth.make_inputs(wl)
+    B, n, K, w, d, Hq = wl.B, wl.n, wl.K, wl.w, wl.d, wl.Hq
+    hidden, P, C = dev(x["hidden"]), dev(x["P"]), dev(x["C"])
+    bias = None if x["bias"] is None else dev(x["bias"])
+    q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
+    say(f"[full] {wl.name}: running the path")
+    ids, margin = focus.focus_assign(hidden, P, C, bias, want_margin=True)
+    perm, offs = focus.focus_group_sort(ids, K)
+    ws = torch.empty(max(focus.focus_attn_workspace_bytes(B, Hq, wl.Hkv, n, d, K, w), 1),
+                     dtype=torch.uint8, device=q.device)
+    out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=q.device)
+    focus.focus_attn_long_range(q, k, v, ids, perm, offs, K, w, wl.softmax_scale, workspace=ws,
+                                out=out)
+    focus.focus_attn_window_merge(q, k, v, ids, perm, offs, K, w, wl.softmax_scale, workspace=ws,
+                                  out=out)
+    out32 = torch.empty((B, Hq, n, d), dtype=torch.float32, device=q.device)
+    lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    focus.focus_attn_window_merge(q, k, v, ids, perm, offs, K, w, wl.softmax_scale, workspace=ws,
+                                  out=out32, lse=lse)
+    torch.cuda.synchronize()
+    del hidden, q, k, v, ws
+    gids = host(ids)
+
+    rng = np.random.default_rng(zlib.crc32(wl.name.encode()))
+    tok = np.unique(np.concatenate([[0, B * n - 1], rng.integers(0, B * n, size=4096)]))
+    rids, rmargin = oracle.assign(x["hidden"], x["P"], x["C"], x["bias"], tokens=tok)
+    check_ids(gids.ravel()[tok], rids.ravel(), rmargin.ravel(),
+              x["hidden"].reshape(-1, wl.d_model)[tok], x["P"], x["C"], x["bias"], wl.name)
+    gm, rm = host(margin).ravel()[tok], rmargin.ravel()
+    assert np.max(np.abs(gm - rm)) < 1e-4
+    rperm, roffs = oracle.group_sort(gids, K)
+    assert np.array_equal(host(perm), rperm) and np.array_equal(host(offs), roffs)
+
+    rows = sample_rows(rng, B, Hq, n, w, per_head=max(16, 2048 // Hq))
+    ref, rlse, _ = oracle.attn(x["q"], x["k"], x["v"], gids, w, wl.softmax_scale, rows=rows)
+    got16 = host(out.float()).reshape(-1, d)[rows]
+    check_attn(got16, ref.reshape(-1, d), f"{wl.name} bf16 out", bf16_out=True)
+    got32 = host(out32).reshape(-1, d)[rows]
+    check_attn(got32, ref.reshape(-1, d), f"{wl.name} fp32 out")
+    assert np.max(np.abs(host(lse).ravel()[rows] - rlse.ravel())) < 1e-3
