@@ -34,9 +34,10 @@
 // with v_mfma_f32_32x32x16_bf16 and fp32 accumulation. K and V tiles are
 // copied HBM -> LDS by global_load_lds_dwordx4 into two LDS buffers: the copy
 // of tile t+1 runs while tile t is computed, one barrier per tile. The
-// running max is only moved (and the accumulator rescaled) when a row's max
-// grows by more than 2^8, so probabilities stay <= 256 and the rescale is
-// rare; the final normalisation is exact either way.
+// probabilities are taken against a reference max that is only moved (and
+// the accumulator rescaled) when a lane's probability sum for a tile exceeds
+// 2^8, so no per-tile max is computed on the common path, probabilities stay
+// <= 256, and the final normalisation is exact either way.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,7 +59,7 @@ constexpr int ROWS = 128;    // query rows per workgroup (4 waves x 32)
 constexpr int MAXSEG = 64;   // groups present in one sorted query tile (K <= 64)
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kRescaleSlack = 8.0f;  // log2 units the running max may lag
+constexpr float kProbSumCap = 256.0f;  // a lane's probability sum that triggers a rescale
 constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 
 enum { kWindow = 0, kLongRange = 1, kDense = 2 };
@@ -392,23 +393,39 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // This lane's share of a tile copy: NI rows (one per 1 KB copy) and the
     // logical chunk it fetches from each.
     int crow[G::NI], cch[G::NI];
+    int lane_off[G::NI];   // element offset of this lane's 16 bytes within a tile
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
         const int o = (wave * G::NI + i) * 1024 + 16 * lane;
         crow[i] = o / G::ROWB;
         cch[i] = logical_chunk<D>(crow[i], (o % G::ROWB) / 16);
+        lane_off[i] = crow[i] * D + cch[i] * 8;
     }
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave index in a scalar register
     int seg_issue = 0, seg_cur = 0;
     auto issue = [&](int tau, unsigned char* bufp, int* kposp) {
         int kt0, kend;
         bool full;
         locate(tau, seg_issue, kt0, kend, full);
+        unsigned char* dst = bufp + wave_s * G::NI * 1024;
+        if (kt0 + BN <= a.n) {
+            // the whole tile lies inside the sequence: a scalar tile base plus
+            // fixed per-lane offsets (rows past kend are read but masked)
+            const uint16_t* kt = kbase + (int64_t)kt0 * D;
+            const uint16_t* vt = vbase + (int64_t)kt0 * D;
 #pragma unroll
-        for (int i = 0; i < G::NI; ++i) {
-            const int slot = min(kt0 + crow[i], kend - 1);
-            const int64_t go = (int64_t)slot * D + cch[i] * 8;
-            copy16(kbase + go, bufp + (wave * G::NI + i) * 1024);
-            copy16(vbase + go, bufp + G::TILEB + (wave * G::NI + i) * 1024);
+            for (int i = 0; i < G::NI; ++i) {
+                copy16(kt + lane_off[i], dst + i * 1024);
+                copy16(vt + lane_off[i], dst + G::TILEB + i * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::NI; ++i) {
+                const int slot = min(kt0 + crow[i], kend - 1);
+                const int64_t go = (int64_t)slot * D + cch[i] * 8;
+                copy16(kbase + go, dst + i * 1024);
+                copy16(vbase + go, dst + G::TILEB + i * 1024);
+            }
         }
         // positions of the tile's key slots, for the mask of a partial tile
         if (SORTED && !full && wave == 0)
@@ -476,37 +493,50 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 }
         }
 
-        // Online softmax with a lagging reference max.
-        float tmax = kNegInf;
+        // Online softmax with a lagging reference max m_ref. Probabilities
+        // are taken against m_ref as it stands; only when a lane's sum of
+        // them exceeds 2^8 (some score grew more than 8 in log2 units past
+        // m_ref), or a row has no reference yet, is the reference moved to
+        // the tile max, the accumulator rescaled and the tile recomputed.
+        // Either way every probability is <= 2^8; the row sum adds them in
+        // fp32 and the PV product takes them rounded to bf16.
+        bf16x8 pf[G::KB][2];
+        float psum;
+        auto probs = [&](float m_use) {
+            float ps4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int kb = 0; kb < G::KB; ++kb)
+            for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, st[kb][e]);
-        tmax = fmaxf(tmax, other_half(tmax)) * a.sl2;
-        const bool grow = tmax > m_ref + kRescaleSlack;
-        if (__any(grow)) {
-            // growing rows: alpha = 2^(m_ref - tmax) (0 when m_ref = -inf);
-            // the other rows of the wave keep their reference (alpha = 1).
-            const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.0f;
-            const float m_new = grow ? tmax : m_ref;
+                for (int e = 0; e < 16; ++e) {
+                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
+                    ps4[e & 3] += p;
+                    pf[kb][e >> 3][e & 7] = (__bf16)p;
+                }
+            psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+        };
+        bool need = m_ref == kNegInf;
+        if (!__any(need)) {
+            probs(m_ref);
+            need = psum > kProbSumCap;
+        }
+        if (__any(need)) {
+            float tmax = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, st[kb][e]);
+            tmax = fmaxf(tmax, other_half(tmax)) * a.sl2;
+            // every row may move its reference up to the tile max
+            const float m_new = fmaxf(m_ref, tmax);
+            const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
             l_run *= alpha;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
             m_ref = m_new;
+            probs(m_ref == kNegInf ? 0.0f : m_ref);
         }
-        const float m_use = (m_ref == kNegInf) ? 0.0f : m_ref;
-        float psum = 0.0f;
-        bf16x8 pf[G::KB][2];
-#pragma unroll
-        for (int kb = 0; kb < G::KB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
-                psum += p;
-                pf[kb][e >> 3][e & 7] = (__bf16)p;
-            }
         l_run += psum;
 
         // O^T += V^T P^T. For k-step (kb, sp) the B slots 0..3 / 4..7 of lane
