@@ -285,14 +285,20 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 31, hh = lane >> 5;
 
+    // Work item of this workgroup. The indices are uniform; readfirstlane
+    // keeps them (and every address derived from them) in scalar registers.
     const int L = xcd_remap(blockIdx.x, a.total);
     int tile = L % a.ntiles;
     int rest = L / a.ntiles;
-    const int slice = rest % a.nslices;
+    int slice = rest % a.nslices;
     rest /= a.nslices;
-    const int kvh = rest % a.Hkv;
-    const int b = rest / a.Hkv;
+    int kvh = rest % a.Hkv;
+    int b = rest / a.Hkv;
     if (SORTED) tile = a.ntiles - 1 - tile;  // heavier sorted tiles first
+    tile = __builtin_amdgcn_readfirstlane(tile);
+    slice = __builtin_amdgcn_readfirstlane(slice);
+    kvh = __builtin_amdgcn_readfirstlane(kvh);
+    b = __builtin_amdgcn_readfirstlane(b);
 
     const int R = wave * 32 + rl;
     const int hslot = R / a.TT, tok = R % a.TT;
@@ -392,14 +398,15 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
 
     // This lane's share of a tile copy: NI rows (one per 1 KB copy) and the
     // logical chunk it fetches from each.
-    int crow[G::NI], cch[G::NI];
-    int lane_off[G::NI];   // element offset of this lane's 16 bytes within a tile
+    // lane_off = byte offset of this lane's 16 bytes within a tile
+    // (row * ROWB + 16 * logical chunk); unsigned, so a copy addresses
+    // memory as a scalar tile base plus a 32-bit lane offset.
+    uint32_t lane_off[G::NI];
 #pragma unroll
     for (int i = 0; i < G::NI; ++i) {
         const int o = (wave * G::NI + i) * 1024 + 16 * lane;
-        crow[i] = o / G::ROWB;
-        cch[i] = logical_chunk<D>(crow[i], (o % G::ROWB) / 16);
-        lane_off[i] = crow[i] * D + cch[i] * 8;
+        const int crow = o / G::ROWB;
+        lane_off[i] = crow * G::ROWB + logical_chunk<D>(crow, (o % G::ROWB) / 16) * 16;
     }
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave index in a scalar register
     int seg_issue = 0, seg_cur = 0;
@@ -411,8 +418,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         if (kt0 + BN <= a.n) {
             // the whole tile lies inside the sequence: a scalar tile base plus
             // fixed per-lane offsets (rows past kend are read but masked)
-            const uint16_t* kt = kbase + (int64_t)kt0 * D;
-            const uint16_t* vt = vbase + (int64_t)kt0 * D;
+            const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)kt0 * D);
+            const char* vt = reinterpret_cast<const char*>(vbase + (int64_t)kt0 * D);
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
                 copy16(kt + lane_off[i], dst + i * 1024);
@@ -421,8 +428,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         } else {
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
-                const int slot = min(kt0 + crow[i], kend - 1);
-                const int64_t go = (int64_t)slot * D + cch[i] * 8;
+                const int slot = min(kt0 + (int)(lane_off[i] / G::ROWB), kend - 1);
+                const int64_t go = (int64_t)slot * D + (lane_off[i] % G::ROWB) / 2;
                 copy16(kbase + go, dst + i * 1024);
                 copy16(vbase + go, dst + G::TILEB + i * 1024);
             }
@@ -503,16 +510,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         bf16x8 pf[G::KB][2];
         float psum;
         auto probs = [&](float m_use) {
-            float ps4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float ps2[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
-                    ps4[e & 3] += p;
+                    ps2[e & 1] += p;
                     pf[kb][e >> 3][e & 7] = (__bf16)p;
                 }
-            psum = (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
+            psum = ps2[0] + ps2[1];
         };
         bool need = m_ref == kNegInf;
         if (!__any(need)) {
