@@ -89,13 +89,11 @@ struct AttnArgs {
     int merge;
 };
 
-// Workgroups per CU each attention kernel is built for. Three lets one
-// workgroup wait on memory while two compute; it needs <= 168 registers per
-// lane, which the long-range and dense passes at d = 128 exceed (their extra
-// masking state would spill), so those stay at two.
-constexpr int attn_occupancy(int D, int PHASE) { return (D == 128 && PHASE != 0) ? 2 : 3; }
-// Keys per tile: 32 where a 64-key tile would not leave room for three
-// workgroups (LDS and registers), else 64.
+// Workgroups per CU each attention kernel is built for: three (one can
+// wait on memory while two compute) wherever the registers fit, i.e. all but
+// the dense pass at d = 128. Keys per tile: 32 at three workgroups per CU
+// for d = 64/128 (LDS and registers), 64 otherwise.
+constexpr int attn_occupancy(int D, int PHASE) { return (D == 128 && PHASE == kDense) ? 2 : 3; }
 constexpr int attn_tile_keys(int D, int PHASE) {
     return (D != 32 && attn_occupancy(D, PHASE) == 3) ? 32 : 64;
 }
@@ -329,11 +327,12 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         const int s1 = min(a.n, s0 + a.TT);
         const int32_t* rec = a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS;
         if (hh == 0) rowpos[R] = pos_i;  // published by the barrier below
-        int nseg = rec[0];
+        // plan values are uniform: readfirstlane keeps them in scalar registers
+        int nseg = __builtin_amdgcn_readfirstlane(rec[0]);
         if (nseg >= 0) {
             nseg = min(nseg, SEGCAP);
-            gfirst = clampi(rec[1], 0, a.K - 1);
-            rows_one_group = rec[2] != 0;
+            gfirst = clampi(__builtin_amdgcn_readfirstlane(rec[1]), 0, a.K - 1);
+            rows_one_group = __builtin_amdgcn_readfirstlane(rec[2]) != 0;
             if (tid < nseg) {
                 const int ob = clampi(rec[4 + 4 * tid], 0, a.n);
                 const int kend = clampi(rec[5 + 4 * tid], ob, a.n);
@@ -348,9 +347,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             // More groups in this tile than a plan record holds: derive the
             // segments here (every tile of them is treated as partial).
             const int32_t* offb = a.offsets + (int64_t)b * (a.K + 1);
-            gfirst = clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1);
-            const int glast =
-                clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1);
+            gfirst = __builtin_amdgcn_readfirstlane(
+                clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1));
+            const int glast = __builtin_amdgcn_readfirstlane(
+                clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1));
             nseg = glast - gfirst + 1;
             if (tid < nseg) {
                 int ob, kend, kfull;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             }
             __syncthreads();
         }
-        ntl = seg_t0[nseg];
+        ntl = __builtin_amdgcn_readfirstlane(seg_t0[nseg]);
         // the row's group: segments are consecutive in sorted order
         if (rvalid) {
             int t = 0;
@@ -389,10 +389,12 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
                    (PHASE == kDense || kend - 1 - kt0 <= a.w);
         } else {
-            while (seg_t0[seg + 1] <= tau) ++seg;
-            kt0 = seg_ob[seg] + (tau - seg_t0[seg]) * BN;
-            kend = seg_kend[seg];
-            full = rows_one_group && (kt0 + BN <= seg_kfull[seg]);
+            // segment values are uniform (LDS, written by one thread each)
+            while (__builtin_amdgcn_readfirstlane(seg_t0[seg + 1]) <= tau) ++seg;
+            kt0 = __builtin_amdgcn_readfirstlane(seg_ob[seg]) +
+                  (tau - __builtin_amdgcn_readfirstlane(seg_t0[seg])) * BN;
+            kend = __builtin_amdgcn_readfirstlane(seg_kend[seg]);
+            full = rows_one_group && (kt0 + BN <= __builtin_amdgcn_readfirstlane(seg_kfull[seg]));
         }
     };
 
@@ -482,21 +484,27 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
 
         // Mask (partial tiles only). Lane holds keys kidx = kb*32 +
         // 8*(e>>2) + 4*hh + (e&3) of its row.
+        // (branch-free: every condition is evaluated, combined with &)
         if (!full) {
-            const int seg_g = gfirst + seg_cur;
+            const bool row_ok = !SORTED || g_i == gfirst + seg_cur;
 #pragma unroll
             for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int kidx = kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                    const int key = kt0 + kidx;
-                    bool ok;
-                    if (!SORTED) {
-                        ok = key < kend && key <= pos_i && pos_i - key <= a.w;
-                    } else {
-                        ok = g_i == seg_g && key < kend && pos_i - kposp[kidx] > a.w;
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int k0 = kb * 32 + 8 * e4 + 4 * hh;   // keys k0 .. k0+3
+                    int4 kp = {0, 0, 0, 0};
+                    if (SORTED) kp = *reinterpret_cast<const int4*>(kposp + k0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int key = kt0 + k0 + j;
+                        bool ok;
+                        if (!SORTED) {
+                            ok = (key < kend) & (key <= pos_i) & (pos_i - key <= a.w);
+                        } else {
+                            ok = row_ok & (key < kend) & (pos_i - kp[j] > a.w);
+                        }
+                        st[kb][4 * e4 + j] = ok ? st[kb][4 * e4 + j] : kNegInf;
                     }
-                    if (!ok) st[kb][e] = kNegInf;
                 }
         }
 
@@ -571,12 +579,15 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
 
     // ---- prologue: first K/V copy in flight, then the row data.
     if (ntl > 0) issue(0, buf0, kpos0);
-    // Window pass: start the online softmax from the long-range partial. A
+    // A merging pass starts the online softmax from a partial result: a
     // normalised partial O_g with log2-sum-exp L_g is exactly the state
-    // (acc = O_g, l = 1, reference max = L_g), so the window keys accumulate
+    // (acc = O_g, l = 1, reference max = L_g), so this pass's keys accumulate
     // on top of it and the final normalisation merges both parts; the loads
-    // share the round trip of the Q rows and the first K/V tile.
-    if (PHASE == kWindow && a.merge && rvalid) {
+    // share the round trip of the Q rows and the first K/V tile. (The window
+    // pass merges the long-range partial; the long-range pass never merges,
+    // but keeping the path in its code gives it a far better register
+    // allocation at three workgroups per CU.)
+    if (PHASE != kDense && a.merge && rvalid) {
         const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
         const float lg = a.lseg[row];
         if (lg != kNegInf) {
