@@ -4,11 +4,14 @@
                     [--skip-cpu-baseline] [--skip-dense]
 
 One step = the whole hot path on one batch of seeded synthetic input already
-resident in HBM: focus_assign -> focus_group_sort -> focus_attn_long_range
--> focus_attn_window_merge (the two passes of focus_attn_fwd), all through
-the C ABI on one stream. W untimed warm-up steps, then K timed steps between
-two device synchronisations. Per-kernel times come from HIP events recorded
-on the same stream around each call inside the timed loop.
+resident in HBM, all through the C ABI: focus_attn_window (the window pass,
+which needs no group data) on a second stream, while focus_assign ->
+focus_group_sort run on the main stream; then, once both are done,
+focus_attn_long_range_merge on the main stream (together the two passes are
+focus_attn_fwd). --no-overlap runs all four calls in order on one stream.
+W untimed warm-up steps, then K timed steps between two device
+synchronisations. Per-call times come from HIP events recorded around each
+call, on the stream it runs on, inside the timed loop.
 
 Prints ONE JSON line. value = visited-pair TFLOP/s of the whole step
 (4*d flops per allowed (query head, i, j) pair / step time). Also reported:
@@ -46,6 +49,8 @@ def parse():
     ap.add_argument("--skip-dense", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle attention sample")
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="run the window pass on the main stream, after the sort")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch for calibrating HBM byte counters)")
@@ -142,28 +147,46 @@ def main():
     ws_t = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dv)
     stream = torch.cuda.current_stream()
 
-    names = ["assign", "sort", "long_range", "window_merge"]
+    side = torch.cuda.Stream()   # default priority
+    overlap = not args.no_overlap
+    # events: 0 step start, 1 assign end, 2 sort end, 3 merge start, 4 step end (main
+    # stream); 5 window start, 6 window end (the stream the window pass runs on)
+    NEV = 7
 
     def step(evs=None):
-        def mark(i):
+        def mark(i, st):
             if evs is not None:
-                evs[i].record(stream)
-        mark(0)
-        focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False, workspace=ws_a)
-        mark(1)
-        focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
-        mark(2)
-        focus.focus_attn_long_range(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t, out=out)
-        mark(3)
-        focus.focus_attn_window_merge(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t,
-                                      out=out)
-        mark(4)
+                evs[i].record(st)
+        ws_stream = side if overlap else stream
+        mark(0, stream)
+        if overlap:
+            side.wait_stream(stream)   # the previous merge has consumed the workspace
+        else:
+            focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False,
+                               workspace=ws_a)
+            mark(1, stream)
+            focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
+            mark(2, stream)
+        mark(5, ws_stream)
+        focus.focus_attn_window(q, k, v, K, w, scale, workspace=ws_t, out=out, stream=ws_stream)
+        mark(6, ws_stream)
+        if overlap:
+            focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False,
+                               workspace=ws_a)
+            mark(1, stream)
+            focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
+            mark(2, stream)
+            stream.wait_stream(side)
+        mark(3, stream)
+        focus.focus_attn_long_range_merge(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t,
+                                          out=out)
+        mark(4, stream)
 
-    log(f"warm-up {args.warmup} steps")
+    log(f"warm-up {args.warmup} steps ({'overlapped' if overlap else 'one stream'})")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -171,9 +194,12 @@ def main():
         step(evs[s])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    phase = {nm: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-             for i, nm in enumerate(names)}
-    ev_step = float(np.mean([evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps)]))
+
+    def span(i, j):
+        return float(np.mean([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)]))
+    phase = {"assign": span(0, 1), "sort": span(1, 2), "window": span(5, 6),
+             "long_range_merge": span(3, 4)}
+    ev_step = span(0, 4)
     ms_step = max(wall_ms, ev_step)
     log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
 
@@ -181,7 +207,7 @@ def main():
     win, lr = metrics.pair_counts(gids, w)
     pairs = win + lr
     flops = metrics.attn_flops(pairs, Hq, d)
-    attn_ms = phase["long_range"] + phase["window_merge"]
+    attn_ms = phase["window"] + phase["long_range_merge"]
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -197,7 +223,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "n": n, "d_head": d,
                    "d_model": wl.d_model, "d_proj": wl.d_proj, "K": K, "window": w,
-                   "out_dtype": "bf16"},
+                   "out_dtype": "bf16",
+                   "streams": "window pass overlapped with assign+sort" if overlap
+                   else "one stream"},
         "visited_pairs_per_head": pairs,
         "window_pairs_per_head": win,
         "long_range_pairs_per_head": lr,
@@ -209,11 +237,11 @@ def main():
     }
 
     # The dominant kernel of the step and its roofline (bf16 MFMA bound).
-    kern = max(("long_range", "window_merge"), key=lambda nm: phase[nm])
-    kflops = metrics.attn_flops(lr if kern == "long_range" else win, Hq, d)
+    kern = max(("long_range_merge", "window"), key=lambda nm: phase[nm])
+    kflops = metrics.attn_flops(lr if kern == "long_range_merge" else win, Hq, d)
     ach = kflops / (phase[kern] * 1e-3) / 1e12
-    res["roofline"] = {"kernel": "attn_kernel<128,1> (long-range pass)" if kern == "long_range"
-                       else "attn_kernel<128,0> (window pass + merge)",
+    res["roofline"] = {"kernel": f"attn_kernel<{d},1> (long-range pass + merge)"
+                       if kern == "long_range_merge" else f"attn_kernel<{d},0> (window pass)",
                        "bound": "mfma", "achieved": ach,
                        "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                        "frac": ach / metrics.MI355X_BF16_DENSE_TFLOPS, "traffic": None,

@@ -112,7 +112,7 @@ focus_status check_attn_buffers(const uint16_t* q, const uint16_t* k, const uint
     return ok();
 }
 
-enum class AttnPart { kAll, kLongRange, kWindowMerge };
+enum class AttnPart { kAll, kWindow, kLongRangeMerge };
 
 focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* group_ids, const int32_t* perm,
@@ -124,9 +124,11 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     if (st != FOCUS_OK) return st;
     st = check_attn_buffers(q, k, v, s, out, out_dtype, lse, scale);
     if (st != FOCUS_OK) return st;
-    REQUIRE_PTR(group_ids, 4);
-    REQUIRE_PTR(perm, 4);
-    REQUIRE_PTR(group_offsets, 4);
+    if (part != AttnPart::kWindow) {   // the window pass reads no group data
+        REQUIRE_PTR(group_ids, 4);
+        REQUIRE_PTR(perm, 4);
+        REQUIRE_PTR(group_offsets, 4);
+    }
     const size_t need = focus::attn_workspace(B, Hq, Hkv, n, d, w);
     if (need > 0) {
         REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
@@ -137,13 +139,13 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     focus::AttnProblem p{q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n, d, K, w, scale,
                          out, out_dtype == FOCUS_F32 ? 1 : 0, lse, need > 0 ? workspace : nullptr};
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (part != AttnPart::kWindowMerge) {
+    if (part != AttnPart::kLongRangeMerge) {
+        hipError_t e = focus::launch_attn_window(p, hs);
+        if (e != hipSuccess) return device_status(e, "window attention launch");
+    }
+    if (part != AttnPart::kWindow) {
         hipError_t e = focus::launch_attn_long_range(p, hs);
         if (e != hipSuccess) return device_status(e, "long-range attention launch");
-    }
-    if (part != AttnPart::kLongRange) {
-        hipError_t e = focus::launch_attn_window(p, true, hs);
-        if (e != hipSuccess) return device_status(e, "window attention launch");
     }
     return ok();
 }
@@ -244,24 +246,25 @@ focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                       stream);
 }
 
-focus_status focus_attn_long_range(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   const int32_t* group_ids, const int32_t* perm,
-                                   const int32_t* group_offsets, int B, int Hq, int Hkv, int n,
-                                   int d_head, int K, int window, float scale, void* out,
-                                   focus_dtype out_dtype, float* lse, void* workspace,
-                                   size_t workspace_bytes, focus_stream_t stream) {
-    return attn_entry(AttnPart::kLongRange, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv,
-                      n, d_head, K, window, scale, out, out_dtype, lse, workspace,
-                      workspace_bytes, stream);
+focus_status focus_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* group_ids, const int32_t* perm,
+                               const int32_t* group_offsets, int B, int Hq, int Hkv, int n,
+                               int d_head, int K, int window, float scale, void* out,
+                               focus_dtype out_dtype, float* lse, void* workspace,
+                               size_t workspace_bytes, focus_stream_t stream) {
+    return attn_entry(AttnPart::kWindow, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n,
+                      d_head, K, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
+                      stream);
 }
 
-focus_status focus_attn_window_merge(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* group_ids, const int32_t* perm,
-                                     const int32_t* group_offsets, int B, int Hq, int Hkv, int n,
-                                     int d_head, int K, int window, float scale, void* out,
-                                     focus_dtype out_dtype, float* lse, void* workspace,
-                                     size_t workspace_bytes, focus_stream_t stream) {
-    return attn_entry(AttnPart::kWindowMerge, q, k, v, group_ids, perm, group_offsets, B, Hq,
+focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* group_ids, const int32_t* perm,
+                                         const int32_t* group_offsets, int B, int Hq, int Hkv,
+                                         int n, int d_head, int K, int window, float scale,
+                                         void* out, focus_dtype out_dtype, float* lse,
+                                         void* workspace, size_t workspace_bytes,
+                                         focus_stream_t stream) {
+    return attn_entry(AttnPart::kLongRangeMerge, q, k, v, group_ids, perm, group_offsets, B, Hq,
                       Hkv, n, d_head, K, window, scale, out, out_dtype, lse, workspace,
                       workspace_bytes, stream);
 }

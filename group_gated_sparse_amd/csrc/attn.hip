@@ -9,18 +9,20 @@
 // work into a local-window attention and an intra-group long-range
 // attention; here those are two passes joined by a log-sum-exp merge:
 //
+//   window pass (sequence order): for each tile of tokens, the key band
+//     [q0 - w, q0 + TT - 1]. It needs no group data, so it can run while the
+//     groups are being assigned and sorted. It writes the normalised partial
+//     output as 16 bits per element (fp16 with a per-row power-of-two scale)
+//     and its log2-sum-exp per row.
 //   long-range pass (group-sorted order): K and V are first copied into
 //     group-sorted order (row s = row perm[s]); a plan kernel lists, per
 //     sorted query tile, the key-slot range of each group present (keys of
 //     the group with position below (largest query position) - w). The
 //     attention kernel, for each tile of 128/G sorted tokens x G query heads
 //     sharing one kv head, visits only those key tiles, so every visited
-//     tile is dense in one group. It writes the normalised partial output (in
-//     bf16, as a flash-attention call returns it) and
-//     its log2-sum-exp per row.
-//   window pass (sequence order): for each tile of tokens, the key band
-//     [q0 - w, q0 + TT - 1]. The long-range partial is merged by starting
-//     the online softmax from it (log-sum-exp merge, exact).
+//     tile is dense in one group. The window partial is merged by starting
+//     the online softmax from it (log-sum-exp merge, exact), and the final
+//     rows are written to their original positions.
 //   dense causal (baseline): the window pass with the band [0, q0 + TT - 1].
 //
 // The two key sets {i-j <= w} and {i-j > w, same group} are disjoint, so
@@ -52,6 +54,8 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;      // threads per workgroup
@@ -73,8 +77,8 @@ struct AttnArgs {
     const int32_t* offsets;
     const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
     int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
-    __bf16* og;             // long-range partial output [B][Hq][n][D] (normalised, bf16)
-    float* lseg;            // long-range partial log2-sum-exp [B][Hq][n] (-inf: no key)
+    _Float16* og;           // window partial [B][Hq][n][D]: O * 2^-e in fp16 (|.| < 1)
+    f32x2* lseg;            // per row (log2-sum-exp L or -inf: no key, e)
     void* out;
     float* lse;
     int B, Hq, Hkv, n, K, w;
@@ -86,7 +90,8 @@ struct AttnArgs {
     int total;     // workgroups
     float sl2;     // scale * log2(e)
     int out_f32;
-    int merge;
+    int merge;     // start from the partial in og/lseg (row of the original position)
+    int partial;   // write the normalised partial to og/lseg instead of out/lse
 };
 
 // Workgroups per CU each attention kernel is built for: three (one can
@@ -579,29 +584,31 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
 
     // ---- prologue: first K/V copy in flight, then the row data.
     if (ntl > 0) issue(0, buf0, kpos0);
-    // A merging pass starts the online softmax from a partial result: a
-    // normalised partial O_g with log2-sum-exp L_g is exactly the state
-    // (acc = O_g, l = 1, reference max = L_g), so this pass's keys accumulate
-    // on top of it and the final normalisation merges both parts; the loads
-    // share the round trip of the Q rows and the first K/V tile. (The window
-    // pass merges the long-range partial; the long-range pass never merges,
-    // but keeping the path in its code gives it a far better register
-    // allocation at three workgroups per CU.)
+    // A merging pass starts the online softmax from a partial result. The
+    // partial is stored as O~ = O * 2^-e (fp16, |O~| < 1) with the row's
+    // log2-sum-exp L and e; (acc = O~, l = 2^-e, reference max = L + e) is
+    // exactly the state that result stands for, so this pass's keys
+    // accumulate on top of it and the final normalisation merges both parts;
+    // the loads share the round trip of the Q rows and the first K/V tile.
+    // (The long-range pass merges the window partial; the window pass never
+    // merges, but keeping the path in its code gives both kernels a far
+    // better register allocation at three workgroups per CU.)
     if (PHASE != kDense && a.merge && rvalid) {
         const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
-        const float lg = a.lseg[row];
-        if (lg != kNegInf) {
-            const __bf16* grow_p = a.og + row * D;
+        const f32x2 le = a.lseg[row];
+        if (le[0] != kNegInf) {
+            const _Float16* grow_p = a.og + row * D;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const bf16x4 gv = *reinterpret_cast<const bf16x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
+                    const f16x4 gv = *reinterpret_cast<const f16x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) acc[db][4 * i + j] = (float)gv[j];
                 }
-            m_ref = lg;
-            l_run = (hh == 0) ? 1.0f : 0.0f;  // halves are summed at the end
+            m_ref = le[0] + le[1];
+            // halves are summed at the end
+            l_run = (hh == 0) ? __builtin_ldexpf(1.0f, -(int)le[1]) : 0.0f;
         }
     }
     auto row_of = [&](int r, int& hr, int& pr) {   // query row r -> (head, position)
@@ -661,14 +668,26 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // contiguous rows.
     const float l_tot = l_run + other_half(l_run);
     const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
-    float scale_o;
+    float scale_o = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     int esize;
-    if (SORTED) {
-        scale_o = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-        esize = 2;   // bf16 partial, as a flash-attention call would return it
-        if (rvalid && hh == 0) a.lseg[row] = l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf;
+    if (a.partial) {
+        // 16-bit partial with a per-row power-of-two scale: O~ = O * 2^-e
+        // with e the exponent of max |O| (so |O~| < 1), kept in fp16, whose
+        // 11-bit significand keeps the merge as precise as the final output
+        esize = 2;
+        float mx = 0.0f;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, __builtin_fabsf(acc[db][e]));
+        mx = fmaxf(mx, other_half(mx)) * scale_o;
+        const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+        scale_o = __builtin_ldexpf(scale_o, -ex);
+        if (rvalid && hh == 0) {
+            const f32x2 le = {l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf, (float)ex};
+            a.lseg[row] = le;
+        }
     } else {
-        scale_o = 1.0f / l_tot;
         esize = a.out_f32 ? 4 : 2;
         if (rvalid && hh == 0 && a.lse) a.lse[row] = (m_ref + __log2f(l_tot)) * kLn2;
     }
@@ -676,7 +695,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     const int nchk = RB / 16;          // 16-byte chunks per row
     const int cmask = (nchk < 16 ? nchk : 16) - 1;
     const int rpp = min(ROWS, (4 * G::TILEB) / RB);   // rows staged per pass
-    char* dst = SORTED ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
+    char* dst = a.partial ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
     for (int r0 = 0; r0 < ROWS; r0 += rpp) {
         __syncthreads();               // K/V buffers (or the previous pass) are free
         if (R >= r0 && R < r0 + rpp) {
@@ -691,10 +710,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     if (esize == 4) {
                         *reinterpret_cast<f32x4*>(smem + rs * RB + ((qd ^ (rs & cmask)) << 4)) = o;
                     } else {
-                        const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2], (__bf16)o[3]};
                         const int half = (qd & 1) ^ ((rs >> 4) & 1);
-                        *reinterpret_cast<bf16x4*>(smem + rs * RB +
-                                                   (((qd >> 1) ^ (rs & cmask)) << 4) + half * 8) = ob;
+                        unsigned char* sp = smem + rs * RB + (((qd >> 1) ^ (rs & cmask)) << 4) + half * 8;
+                        if (a.partial) {
+                            const f16x4 oh = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2],
+                                              (_Float16)o[3]};
+                            *reinterpret_cast<f16x4*>(sp) = oh;
+                        } else {
+                            const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2],
+                                               (__bf16)o[3]};
+                            *reinterpret_cast<bf16x4*>(sp) = ob;
+                        }
                     }
                 }
         }
@@ -740,8 +766,8 @@ AttnArgs make_args(const AttnProblem& p) {
     if (p.workspace) {
         const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d);
         char* base = static_cast<char*>(p.workspace);
-        a.og = reinterpret_cast<__bf16*>(base + ws.og);
-        a.lseg = reinterpret_cast<float*>(base + ws.lseg);
+        a.og = reinterpret_cast<_Float16*>(base + ws.og);
+        a.lseg = reinterpret_cast<f32x2*>(base + ws.lseg);
         a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
         a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
     }
@@ -791,18 +817,23 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     if (e != hipSuccess) return e;
     a.k = ks;
     a.v = vs;
+    a.merge = 1;     // start from the window partial, write the final output
+    a.partial = 0;
     return launch<kLongRange>(a, p.d, stream);
 }
 
-hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream) {
+hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream) {
     AttnArgs a = make_args(p);
-    a.merge = merge && attn_has_long_range(p.n, p.w) ? 1 : 0;
+    a.merge = 0;
+    // with a long-range part to come, the window result is a partial
+    a.partial = attn_has_long_range(p.n, p.w) ? 1 : 0;
     return launch<kWindow>(a, p.d, stream);
 }
 
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream) {
     AttnArgs a = make_args(p);
     a.merge = 0;
+    a.partial = 0;
     a.w = p.n;
     return launch<kDense>(a, p.d, stream);
 }

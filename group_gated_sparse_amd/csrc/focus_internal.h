@@ -54,9 +54,10 @@ constexpr int PLAN_INTS = 32;   // ints per plan record (4 + 4 * SEGCAP)
 int attn_heads_per_wg(int hpk);
 inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_wg(Hq / Hkv); }
 
-// Long-range workspace, byte offsets: partial output (bf16 [B][Hq][n][d]),
-// its log2-sum-exp (fp32 [B][Hq][n]), the tile plan, group-sorted copies of
-// K and V (bf16 [B][Hkv][n][d]) and the sorted positions (int32 [B][n + pad]).
+// Attention workspace, byte offsets: the window partial output (fp16
+// [B][Hq][n][d], scaled per row), its log2-sum-exp and scale exponent (fp32
+// pairs [B][Hq][n]), the tile plan, group-sorted copies of K and V (bf16
+// [B][Hkv][n][d]) and the sorted positions (int32 [B][n + pad]).
 struct AttnWorkspace {
     size_t og, lseg, plan, ks, vs, spos, total;
 };
@@ -66,7 +67,7 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d)
     const size_t ntiles = (size_t)(n + TT - 1) / TT;
     size_t off = 0;
     w.og = off;   off += align_up((size_t)B * Hq * n * d * 2);
-    w.lseg = off; off += align_up((size_t)B * Hq * n * 4);
+    w.lseg = off; off += align_up((size_t)B * Hq * n * 8);
     w.plan = off; off += align_up((size_t)B * ntiles * PLAN_INTS * 4);
     w.ks = off;   off += align_up((size_t)B * Hkv * n * d * 2);
     w.vs = off;   off += align_up((size_t)B * Hkv * n * d * 2);
@@ -79,7 +80,7 @@ inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w) {
     return attn_workspace_layout(B, Hq, Hkv, n, d).total;
 }
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
-hipError_t launch_attn_window(const AttnProblem& p, bool merge, hipStream_t stream);
+hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream);
 
 }  // namespace focus

@@ -38,9 +38,9 @@ _SIGNATURES = {
     "focus_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "focus_attn_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p,
                         _sz, _p], _i),
-    "focus_attn_long_range": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
+    "focus_attn_window": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
                                _p, _p, _sz, _p], _i),
-    "focus_attn_window_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
+    "focus_attn_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
                                  _i, _p, _p, _sz, _p], _i),
     "dense_causal_attn_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p], _i),
 }
@@ -168,15 +168,18 @@ def focus_attn_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K
 
 
 def _attn_call(fn_name, q, k, v, group_ids, perm, group_offsets, K, window, scale, out,
-               out_dtype, lse, want_lse, workspace, stream):
+               out_dtype, lse, want_lse, workspace, stream, needs_groups=True):
     B, Hq, n, d = q.shape
     Hkv = k.shape[1]
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, (B, Hkv, n, d))
     _need(v, "v", torch.bfloat16, (B, Hkv, n, d))
-    _need(group_ids, "group_ids", torch.int32, (B, n))
-    _need(perm, "perm", torch.int32, (B, n))
-    _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
+    if needs_groups or group_ids is not None:
+        _need(group_ids, "group_ids", torch.int32, (B, n))
+    if needs_groups or perm is not None:
+        _need(perm, "perm", torch.int32, (B, n))
+    if needs_groups or group_offsets is not None:
+        _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
     if out is None:
         out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
     if out.dtype not in (torch.bfloat16, torch.float32):
@@ -206,19 +209,22 @@ def focus_attn_fwd(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
     return out, lse
 
 
-def focus_attn_long_range(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
-                          scale: float, *, workspace, out=None, out_dtype=torch.bfloat16,
-                          lse=None, want_lse: bool = False, stream=None):
-    """First pass of focus_attn_fwd (writes the long-range partial into workspace)."""
-    return _attn_call("focus_attn_long_range", q, k, v, group_ids, perm, group_offsets, K,
-                      window, scale, out, out_dtype, lse, want_lse, workspace, stream)
+def focus_attn_window(q, k, v, K: int, window: int, scale: float, *, workspace,
+                      out=None, out_dtype=torch.bfloat16, lse=None, want_lse: bool = False,
+                      stream=None):
+    """First pass of focus_attn_fwd: the local window. It reads no group data;
+    it writes the window partial into workspace (or out/lse directly when no
+    pair lies beyond the window)."""
+    return _attn_call("focus_attn_window", q, k, v, None, None, None, K, window, scale, out,
+                      out_dtype, lse, want_lse, workspace, stream, needs_groups=False)
 
 
-def focus_attn_window_merge(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
-                            scale: float, *, workspace, out=None, out_dtype=torch.bfloat16,
-                            lse=None, want_lse: bool = False, stream=None):
-    """Second pass of focus_attn_fwd (window attention + merge with the partial)."""
-    return _attn_call("focus_attn_window_merge", q, k, v, group_ids, perm, group_offsets, K,
+def focus_attn_long_range_merge(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
+                                scale: float, *, workspace, out=None, out_dtype=torch.bfloat16,
+                                lse=None, want_lse: bool = False, stream=None):
+    """Second pass of focus_attn_fwd: same-group pairs beyond the window,
+    merged with the window partial; writes out (and lse)."""
+    return _attn_call("focus_attn_long_range_merge", q, k, v, group_ids, perm, group_offsets, K,
                       window, scale, out, out_dtype, lse, want_lse, workspace, stream)
 
 

@@ -113,10 +113,11 @@ focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K,
  *   lse[b][h][i] = log sum_{j in A_i} exp(scale * q_i . k_j)   (natural log)
  *
  * Each allowed pair is counted once (the two sets are disjoint). The work is
- * done in two passes, as the Korean page §2.3 splits the pattern: an
+ * done in two passes, as the Korean page §2.3 splits the pattern: a
+ * local-window pass in sequence order, which needs no group data, and an
  * intra-group long-range pass in group-sorted order (tiles of keys from
- * other groups are never visited) and a local-window pass in sequence order
- * that merges both parts by log-sum-exp.
+ * other groups are never visited) that merges both parts by log-sum-exp and
+ * writes the result.
  *
  * q [B][Hq][n][d_head] bf16 bits; k, v [B][Hkv][n][d_head] bf16 bits
  * group_ids [B][n], perm [B][n], group_offsets [B][K+1]: as produced by
@@ -135,22 +136,31 @@ focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                             float scale, void* out, focus_dtype out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, focus_stream_t stream);
 
-/* The two passes of focus_attn_fwd as separate calls (same arguments and the
- * same workspace, which carries the long-range partial result from the first
- * call to the second). focus_attn_fwd == long_range then window_merge. */
-focus_status focus_attn_long_range(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                   const int32_t* group_ids, const int32_t* perm,
-                                   const int32_t* group_offsets,
-                                   int B, int Hq, int Hkv, int n, int d_head, int K, int window,
-                                   float scale, void* out, focus_dtype out_dtype, float* lse,
-                                   void* workspace, size_t workspace_bytes, focus_stream_t stream);
-focus_status focus_attn_window_merge(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                     const int32_t* group_ids, const int32_t* perm,
-                                     const int32_t* group_offsets,
-                                     int B, int Hq, int Hkv, int n, int d_head, int K, int window,
-                                     float scale, void* out, focus_dtype out_dtype, float* lse,
-                                     void* workspace, size_t workspace_bytes,
-                                     focus_stream_t stream);
+/* The two passes of focus_attn_fwd as separate calls, with the same
+ * arguments and the same workspace, which carries the window partial result
+ * from the first call to the second: focus_attn_fwd == focus_attn_window
+ * then focus_attn_long_range_merge on one stream.
+ *
+ * focus_attn_window reads no group data (group_ids, perm and group_offsets
+ * may be NULL), so a caller can run it on a second stream while the groups
+ * are assigned and sorted, and start focus_attn_long_range_merge once both
+ * are done. When no pair can lie beyond the window (n - 1 <= window) it
+ * writes out and lse itself and focus_attn_long_range_merge does nothing;
+ * otherwise it writes only the workspace. A workspace must not be used by a
+ * second window pass before the merge of the first has run. */
+focus_status focus_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                               const int32_t* group_ids, const int32_t* perm,
+                               const int32_t* group_offsets,
+                               int B, int Hq, int Hkv, int n, int d_head, int K, int window,
+                               float scale, void* out, focus_dtype out_dtype, float* lse,
+                               void* workspace, size_t workspace_bytes, focus_stream_t stream);
+focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* group_ids, const int32_t* perm,
+                                         const int32_t* group_offsets,
+                                         int B, int Hq, int Hkv, int n, int d_head, int K,
+                                         int window, float scale, void* out,
+                                         focus_dtype out_dtype, float* lse, void* workspace,
+                                         size_t workspace_bytes, focus_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Baseline: plain causal attention (every pair j <= i), the "full attention"

@@ -92,11 +92,11 @@ def test_workspace_sizes():
     # per-block group counts: B x ceil(n / 2048) x K int32, 256-byte aligned
     assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 256
     assert lib.focus_group_sort_workspace_bytes(1, 65536, 64) == 32 * 64 * 4
-    # long-range: partial bf16 [B][Hq][n][d] + lse fp32 [B][Hq][n] + 128 B plan per query
+    # partial fp16 [B][Hq][n][d] + (lse, exponent) fp32 pairs [B][Hq][n] + 128 B plan per query
     # tile (here 64 tokens x 2 heads) + sorted bf16 K and V [B][Hkv][n][d] + int32 sorted
     # positions [B][n + 256], each region 256-byte aligned
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == (
-        256 * 2 * 32 * 2 + 2048 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4)
+        256 * 2 * 32 * 2 + 4096 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4)
     # no pair can be further apart than the window: no partial needed
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
@@ -137,13 +137,11 @@ def _attn(fn="focus_attn_fwd", **kw):
              args["out"], args["dt"], args["lse"], args["ws"], args["wsb"], args["stream"])
 
 
-@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_long_range",
-                                "focus_attn_window_merge"])
+@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_window",
+                                "focus_attn_long_range_merge"])
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(q=None), INVALID, "q"),
     (dict(k=Bp + 8), INVALID, "aligned"),
-    (dict(ids=None), INVALID, "group_ids"),
-    (dict(offs=None), INVALID, "group_offsets"),
     (dict(out=None), INVALID, "out"),
     (dict(d=48), UNSUPPORTED, "d_head"),
     (dict(d=256), UNSUPPORTED, "d_head"),
@@ -166,6 +164,22 @@ def _attn(fn="focus_attn_fwd", **kw):
 def test_attn_rejects(fn, kw, code, msg):
     assert _attn(fn, **kw) == code
     assert msg in _err()
+
+
+@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_long_range_merge"])
+@pytest.mark.parametrize("kw,msg", [(dict(ids=None), "group_ids"), (dict(perm=None), "perm"),
+                                    (dict(offs=None), "group_offsets")])
+def test_attn_passes_needing_groups_reject_missing_group_data(fn, kw, msg):
+    assert _attn(fn, **kw) == INVALID
+    assert msg in _err()
+
+
+def test_window_pass_takes_no_group_data():
+    """The window pass reads no group data, so NULL ids / perm / offsets pass
+    validation; a bad request is still rejected on its own merits (here the
+    workspace is too small, after the group pointers were skipped)."""
+    assert _attn("focus_attn_window", ids=None, perm=None, offs=None, wsb=1024) == WORKSPACE
+    assert "too small" in _err()
 
 
 @pytest.mark.parametrize("kw,code,msg", [

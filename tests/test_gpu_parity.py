@@ -129,7 +129,9 @@ def test_deterministic_and_stream_independent():
 
 
 def test_two_calls_equal_one():
-    """focus_attn_long_range then focus_attn_window_merge == focus_attn_fwd."""
+    """focus_attn_window (on a second stream, no group data, started before
+    the groups are sorted) then focus_attn_long_range_merge ==
+    focus_attn_fwd, bit for bit."""
     say("[attn] split calls")
     rng = np.random.default_rng(10)
     B, Hq, Hkv, n, d, K, w = 1, 4, 4, 480, 64, 5, 33
@@ -137,14 +139,23 @@ def test_two_calls_equal_one():
     ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
     tq, tk, tv, tid = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(ids)
     perm, offs = focus.focus_group_sort(tid, K)
-    one, _ = focus.focus_attn_fwd(tq, tk, tv, tid, perm, offs, K, w, 0.125, out_dtype=torch.float32)
+    one, lse1 = focus.focus_attn_fwd(tq, tk, tv, tid, perm, offs, K, w, 0.125,
+                                     out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
     ws = torch.empty(focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w), dtype=torch.uint8,
                      device="cuda")
     two = torch.empty_like(one)
-    focus.focus_attn_long_range(tq, tk, tv, tid, perm, offs, K, w, 0.125, workspace=ws, out=two)
-    focus.focus_attn_window_merge(tq, tk, tv, tid, perm, offs, K, w, 0.125, workspace=ws, out=two)
+    lse2 = torch.empty_like(lse1)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    side.wait_stream(main)
+    focus.focus_attn_window(tq, tk, tv, K, w, 0.125, workspace=ws, out=two, lse=lse2, stream=side)
+    perm2, offs2 = focus.focus_group_sort(tid, K, stream=main)
+    main.wait_stream(side)
+    focus.focus_attn_long_range_merge(tq, tk, tv, tid, perm2, offs2, K, w, 0.125, workspace=ws,
+                                      out=two, lse=lse2, stream=main)
     torch.cuda.synchronize()
-    assert torch.equal(one, two)
+    assert torch.equal(one, two) and torch.equal(lse1, lse2)
 
 
 # ---------------------------------------------------------------- sort
@@ -218,11 +229,12 @@ def test_whole_path_small_workloads(wl):
 @pytest.mark.parametrize("wl", [workloads.ZIPF7B, workloads.LONG64K, workloads.GQA70B],
                          ids=lambda w: w.name)
 def test_whole_path_full_size_sampled(wl):
-    """The benchmark's launch sequence at full size (assign, sort, long-range
-    pass, window merge; bf16 output), checked on sampled tokens and rows: ids
-    against the oracle on 4096 tokens, perm/offsets bit-exact on all tokens,
-    attention on the start, window edge, end and random rows of every head.
-    A second window merge with fp32 output and lse gets the strict bar."""
+    """The benchmark's launch sequence at full size (window pass on a second
+    stream while assign and sort run, then the long-range merge; bf16
+    output), checked on sampled tokens and rows: ids against the oracle on
+    4096 tokens, perm/offsets bit-exact on all tokens, attention on the
+    start, window edge, end and random rows of every head. A second merge of
+    the same window partial with fp32 output and lse gets the strict bar."""
     say(f"[full] {wl.name}: drawing inputs")
     x = synth.make_inputs(wl)
     B, n, K, w, d, Hq = wl.B, wl.n, wl.K, wl.w, wl.d, wl.Hq
@@ -230,19 +242,21 @@ def test_whole_path_full_size_sampled(wl):
     bias = None if x["bias"] is None else dev(x["bias"])
     q, k, v = dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"])
     say(f"[full] {wl.name}: running the path")
-    ids, margin = focus.focus_assign(hidden, P, C, bias, want_margin=True)
-    perm, offs = focus.focus_group_sort(ids, K)
     ws = torch.empty(max(focus.focus_attn_workspace_bytes(B, Hq, wl.Hkv, n, d, K, w), 1),
                      dtype=torch.uint8, device=q.device)
     out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=q.device)
-    focus.focus_attn_long_range(q, k, v, ids, perm, offs, K, w, wl.softmax_scale, workspace=ws,
-                                out=out)
-    focus.focus_attn_window_merge(q, k, v, ids, perm, offs, K, w, wl.softmax_scale, workspace=ws,
-                                  out=out)
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    side.wait_stream(main)
+    focus.focus_attn_window(q, k, v, K, w, wl.softmax_scale, workspace=ws, out=out, stream=side)
+    ids, margin = focus.focus_assign(hidden, P, C, bias, want_margin=True, stream=main)
+    perm, offs = focus.focus_group_sort(ids, K, stream=main)
+    main.wait_stream(side)
+    focus.focus_attn_long_range_merge(q, k, v, ids, perm, offs, K, w, wl.softmax_scale,
+                                      workspace=ws, out=out, stream=main)
     out32 = torch.empty((B, Hq, n, d), dtype=torch.float32, device=q.device)
     lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
-    focus.focus_attn_window_merge(q, k, v, ids, perm, offs, K, w, wl.softmax_scale, workspace=ws,
-                                  out=out32, lse=lse)
+    focus.focus_attn_long_range_merge(q, k, v, ids, perm, offs, K, w, wl.softmax_scale,
+                                      workspace=ws, out=out32, lse=lse, stream=main)
     torch.cuda.synchronize()
     del hidden, q, k, v, ws
     gids = host(ids)
