@@ -57,6 +57,33 @@ def parse():
     return ap.parse_args()
 
 
+TRAFFIC_SOURCES = ("group_gated_sparse_amd/csrc/attn.hip", "group_gated_sparse_amd/csrc/focus_internal.h",
+                   "group_gated_sparse_amd/csrc/assign.hip", "group_gated_sparse_amd/csrc/sort.hip",
+                   "group_gated_sparse_amd/build.py")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic_<workload>.txt: FETCH_SIZE and WRITE_SIZE
+    scaled by a plain-copy calibration), or None when there is none or it was
+    taken on kernel sources other than the ones in this tree."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    sha, value = None, None
+    for line in open(path):
+        if line.startswith("sources_sha256:"):
+            sha = line.split(":", 1)[1].strip()
+        elif line.startswith(f"kernel {kernel}:"):
+            value = float(line.split("hbm_bytes")[1].split()[0])
+    return value if sha == h.hexdigest() else None
+
+
 def cpu_baseline(x, wl, target_s):
     """The oracle as it stands, on the host cores: full assignment and group
     sort, attention on a random row sample extrapolated per visited pair."""
@@ -240,11 +267,15 @@ def main():
     kern = max(("long_range_merge", "window"), key=lambda nm: phase[nm])
     kflops = metrics.attn_flops(lr if kern == "long_range_merge" else win, Hq, d)
     ach = kflops / (phase[kern] * 1e-3) / 1e12
-    res["roofline"] = {"kernel": f"attn_kernel<{d},1> (long-range pass + merge)"
-                       if kern == "long_range_merge" else f"attn_kernel<{d},0> (window pass)",
+    kname = f"attn_kernel<{d},1>" if kern == "long_range_merge" else f"attn_kernel<{d},0>"
+    res["roofline"] = {"kernel": kname + (" (long-range pass + merge)" if kern == "long_range_merge"
+                                          else " (window pass)"),
                        "bound": "mfma", "achieved": ach,
                        "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
-                       "frac": ach / metrics.MI355X_BF16_DENSE_TFLOPS, "traffic": None,
+                       "frac": ach / metrics.MI355X_BF16_DENSE_TFLOPS,
+                       "traffic": measured_traffic(wl.name, kname),
+                       "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                       "copy-calibrated)",
                        "flops_per_launch": kflops, "avg_launch_ms": phase[kern]}
 
     if not args.skip_dense:
