@@ -486,6 +486,18 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 st[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[kb], 0, 0, 0);
             }
         }
+        // Schedule (DS-read group 0x100, MFMA group 0x008): keep three K
+        // fragment reads in flight ahead of the S MFMAs, otherwise each MFMA
+        // waits out a full LDS round trip.
+        {
+            constexpr int NS = G::KB * G::KS;
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+            for (int j = 0; j < NS; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (j + 3 < NS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+        }
 
         // Mask (partial tiles only). Lane holds keys kidx = kb*32 +
         // 8*(e>>2) + 4*hh + (e&3) of its row.
@@ -580,6 +592,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                         __builtin_bit_cast(bf16x8, vv), pf[kb][sp], acc[db], 0, 0, 0);
                 }
             }
+        // Same for the PV MFMAs: V^T reads for three MFMAs ahead.
+        {
+            constexpr int NP = G::KB * 2 * G::DB;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * 3, 1);
+#pragma unroll
+            for (int j = 0; j < NP; ++j) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                if (j + 3 < NP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            }
+        }
     };
 
     // ---- prologue: first K/V copy in flight, then the row data.
