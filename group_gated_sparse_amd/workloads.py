@@ -62,5 +62,11 @@ LONG64K = Workload("long_n65536", B=1, Hq=8, Hkv=8, n=65536, d=128, d_model=1024
 GQA70B = Workload("70b_gqa_n32768", B=1, Hq=64, Hkv=8, n=32768, d=128, d_model=8192,
                   d_proj=128, K=32, w=1024, seed=1004)
 
-ALL = [TINY, GPT2, ZIPF7B, LONG64K, GQA70B]
+# The pages' one-million-token regime (Korean page §3.4, Japanese page §3.3;
+# K, w and the model are not stated there): the 64K layer shape at n = 2^20.
+LONG1M = Workload("long_n1048576", B=1, Hq=8, Hkv=8, n=1 << 20, d=128, d_model=1024,
+                  d_proj=128, K=64, w=1024, pc_kind="orthonormal",
+                  q_prescale=1.0 / 128 ** 0.5, scale=1.0, seed=1005)
+
+ALL = [TINY, GPT2, ZIPF7B, LONG64K, GQA70B, LONG1M]
 BY_NAME = {w.name: w for w in ALL}

@@ -226,7 +226,9 @@ def test_whole_path_small_workloads(wl):
     assert int(vis[:, 0].sum()) == visited_pairs(gids, wl.w)
 
 
-@pytest.mark.parametrize("wl", [workloads.ZIPF7B, workloads.LONG64K, workloads.GQA70B],
+@pytest.mark.parametrize("wl", [workloads.ZIPF7B, workloads.LONG64K, workloads.GQA70B,
+                                pytest.param(workloads.LONG1M,
+                                             marks=pytest.mark.timeout(900))],
                          ids=lambda w: w.name)
 def test_whole_path_full_size_sampled(wl):
     """The benchmark's launch sequence at full size (window pass on a second
