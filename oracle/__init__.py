@@ -58,6 +58,14 @@ def configure(lib):
     lib.oracle_pair_count.argtypes = [_p, _i64, _i64, _i64, ctypes.c_int]
     lib.oracle_pair_count.restype = _i64
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_assign_topk.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _p,
+                                       _i64, _p, _p, ctypes.c_int]
+    lib.oracle_assign_topk.restype = ctypes.c_int
+    lib.oracle_attn_multi.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                      ctypes.c_double, _p, _i64, _p, _p, _p, ctypes.c_int]
+    lib.oracle_attn_multi.restype = ctypes.c_int
+    lib.oracle_pair_count_multi.argtypes = [_p, _i64, _i64, _i64, _i64, ctypes.c_int]
+    lib.oracle_pair_count_multi.restype = _i64
     return lib
 
 
@@ -208,4 +216,96 @@ def pair_count(ids, w: int, nthreads: int = 0) -> int:
     r = _load().oracle_pair_count(_ptr(ids), B, n, int(w), nthreads)
     if r < 0:
         raise ValueError("oracle_pair_count rejected its arguments")
+    return int(r)
+
+
+# ---- multi-membership (top-m groups per token) -------------------------------
+# Korean page §2.3 / Japanese page §2.2: at inference a token may join its top-k
+# groups (k = 2 at K = 4 in the Korean page §3.4 and the Japanese page §3.3);
+# a far pair is then kept when the two tokens share any group.
+
+def assign_topk(hidden, P, C, m: int, bias=None, tokens=None, nthreads: int = 0):
+    """Top-m groups per token by the fp32 scores of assign(): ids (B, n, m)
+    in decreasing score order (exact ties to the lowest index) and margin
+    s_(m) - s_(m+1) (+inf when K == m)."""
+    hidden = _c(hidden, np.float32)
+    P = _c(P, np.float32)
+    C = _c(C, np.float32)
+    bias = _c(bias, np.float32)
+    B, n, d_model = hidden.shape
+    d_proj = P.shape[1]
+    K = C.shape[0]
+    assert P.shape == (d_model, d_proj) and C.shape == (K, d_proj)
+    if tokens is not None:
+        tokens = _c(tokens, np.int64).ravel()
+        count = tokens.size
+    else:
+        count = B * n
+    ids = np.empty((count, m), dtype=np.int32)
+    margin = np.empty(count, dtype=np.float32)
+    rc = _load().oracle_assign_topk(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n, d_model,
+                                    d_proj, K, int(m), _ptr(tokens),
+                                    count if tokens is not None else 0, _ptr(ids), _ptr(margin),
+                                    nthreads)
+    if rc != 0:
+        raise ValueError("oracle_assign_topk rejected its arguments")
+    if tokens is None:
+        ids = ids.reshape(B, n, m)
+        margin = margin.reshape(B, n)
+    return ids, margin
+
+
+def group_sort_multi(ids, K: int):
+    """Stable sort of membership entries by group. ids (B, n, m); entry
+    e = t*m + c is token t's c-th group. Returns (perm (B, n*m) of entry
+    indices, offsets (B, K+1)): each group's entries are one segment in
+    increasing position."""
+    ids = _c(ids, np.int32)
+    B, n, m = ids.shape
+    return group_sort(ids.reshape(B, n * m), K)
+
+
+def _attn_multi_common(q, k, v, ids):
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    ids = _c(ids, np.int32)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, n, d) and v.shape == k.shape
+    assert ids.ndim == 3 and ids.shape[:2] == (B, n)
+    return q, k, v, ids, B, Hq, Hkv, n, d, ids.shape[2]
+
+
+def attn_multi(q, k, v, ids, w: int, scale: float, rows=None, nthreads: int = 0):
+    """Exact softmax attention over
+    A_i = {j <= i : i-j <= w or groups(i) and groups(j) intersect}, ids (B, n, m);
+    otherwise as attn()."""
+    q, k, v, ids, B, Hq, Hkv, n, d, m = _attn_multi_common(q, k, v, ids)
+    if rows is not None:
+        rows = _c(rows, np.int64).ravel()
+        count = rows.size
+    else:
+        count = B * Hq * n
+    out = np.empty((count, d), dtype=np.float64)
+    lse = np.empty(count, dtype=np.float64)
+    visited = np.empty(count, dtype=np.int64)
+    rc = _load().oracle_attn_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(ids), m, B, Hq, Hkv, n, d,
+                                   int(w), float(scale), _ptr(rows),
+                                   count if rows is not None else 0, _ptr(out), _ptr(lse),
+                                   _ptr(visited), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_attn_multi rejected its arguments")
+    if rows is None:
+        return out.reshape(B, Hq, n, d), lse.reshape(B, Hq, n), visited.reshape(B, Hq, n)
+    return out, lse, visited
+
+
+def pair_count_multi(ids, w: int, nthreads: int = 0) -> int:
+    """sum over b, i of |A_i| for the multi-membership pattern (ids (B, n, m))."""
+    ids = _c(ids, np.int32)
+    B, n, m = ids.shape
+    r = _load().oracle_pair_count_multi(_ptr(ids), m, B, n, int(w), nthreads)
+    if r < 0:
+        raise ValueError("oracle_pair_count_multi rejected its arguments")
     return int(r)

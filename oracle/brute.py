@@ -58,3 +58,42 @@ def attention(q, k, v, ids, w, scale):
         out.append(oh)
         weights.append(wh)
     return out, weights
+
+
+def keeps_sets(i: int, j: int, w: int, gi, gj) -> bool:
+    """Multi-membership rule (Korean page §2.3, Japanese page §2.2: a token
+    may belong to its top-k groups): far pairs are kept when the two tokens
+    have at least one group in common."""
+    if j > i:
+        return False
+    if abs(i - j) <= w:
+        return True
+    return len(set(gi) & set(gj)) > 0
+
+
+def attention_sets(q, k, v, groups, w, scale):
+    """As attention(), with groups[i] the collection of token i's groups.
+    Returns (out [Hq][n][d], kept-pair counts [Hq][n])."""
+    Hq, Hkv = len(q), len(k)
+    n, d = len(q[0]), len(q[0][0])
+    share = Hq // Hkv
+    out, counts = [], []
+    for h in range(Hq):
+        kv = h // share
+        Kf = [[bf16_to_float(x) for x in row] for row in k[kv]]
+        Vf = [[bf16_to_float(x) for x in row] for row in v[kv]]
+        oh, ch = [], []
+        for i in range(n):
+            qi = [bf16_to_float(x) for x in q[h][i]]
+            scores = {}
+            for j in range(n):
+                if keeps_sets(i, j, w, groups[i], groups[j]):
+                    scores[j] = scale * math.fsum(a * b for a, b in zip(qi, Kf[j]))
+            top = max(scores.values())
+            ex = {j: math.exp(s - top) for j, s in scores.items()}
+            tot = math.fsum(ex.values())
+            oh.append([math.fsum(ex[j] / tot * Vf[j][c] for j in scores) for c in range(d)])
+            ch.append(len(scores))
+        out.append(oh)
+        counts.append(ch)
+    return out, counts

@@ -23,6 +23,9 @@
  *   ties go to the lowest group index; the window is the causal band
  *   0 <= i-j <= w; long-range pairs are causal (j <= i); an allowed pair is
  *   counted once; the softmax is renormalised over the allowed set.
+ *   Multi-membership (top-m groups per token, m = 2 in the pages' runs): a far
+ *   pair is kept when the tokens share at least one group, and still counted
+ *   once; the top-m groups are the m highest scores, ties to the lowest index.
  *
  * Precision: assignment in fp32 (build with -ffp-contract=off, sums in
  * ascending index order, as written); attention in fp64 on the exact values
@@ -62,6 +65,24 @@ int oracle_max_threads(void) {
 #endif
 }
 
+/* Scores of one token: z = h P (fp32, summed in increasing index), then
+ * s[k] = z . C_k + bias_k. */
+static void token_scores(const float* h, const float* P, const float* C, const float* bias,
+                         int64_t d_model, int64_t d_proj, int64_t K, float* z, float* s) {
+    for (int64_t j = 0; j < d_proj; ++j) z[j] = 0.0f;
+    for (int64_t m = 0; m < d_model; ++m) {
+        const float hm = h[m];
+        const float* Prow = P + m * d_proj;
+        for (int64_t j = 0; j < d_proj; ++j) z[j] = z[j] + hm * Prow[j];
+    }
+    for (int64_t k = 0; k < K; ++k) {
+        float acc = 0.0f;
+        const float* Ck = C + k * d_proj;
+        for (int64_t j = 0; j < d_proj; ++j) acc = acc + z[j] * Ck[j];
+        s[k] = bias ? acc + bias[k] : acc;
+    }
+}
+
 /*
  * Hard group assignment (Japanese page §2.1 and §2.2; Korean page §2.3):
  *   z = h_t · P            (d_proj values, each summed over m = 0..d_model-1)
@@ -92,19 +113,7 @@ int oracle_assign(const float* hidden, const float* P, const float* C, const flo
                 bad = 1;
                 continue;
             }
-            const float* h = hidden + tok * d_model;
-            for (int64_t j = 0; j < d_proj; ++j) z[j] = 0.0f;
-            for (int64_t m = 0; m < d_model; ++m) {
-                const float hm = h[m];
-                const float* Prow = P + m * d_proj;
-                for (int64_t j = 0; j < d_proj; ++j) z[j] = z[j] + hm * Prow[j];
-            }
-            for (int64_t k = 0; k < K; ++k) {
-                float acc = 0.0f;
-                const float* Ck = C + k * d_proj;
-                for (int64_t j = 0; j < d_proj; ++j) acc = acc + z[j] * Ck[j];
-                s[k] = bias ? acc + bias[k] : acc;
-            }
+            token_scores(hidden + tok * d_model, P, C, bias, d_model, d_proj, K, z, s);
             int64_t best = 0;
             for (int64_t k = 1; k < K; ++k)
                 if (s[k] > s[best]) best = k;
@@ -121,7 +130,7 @@ int oracle_assign(const float* hidden, const float* P, const float* C, const flo
 }
 
 /*
- * Stable grouping of tokens (spec step 2; the pages only say tokens are
+ * Stable grouping of tokens (the grouping step; the pages only say tokens are
  * grouped): counting sort per batch element.
  *   offsets[b][k] = number of tokens of batch b with id < k  (K+1 entries)
  *   perm[b][offsets[b][g] + r] = t, where t is the r-th token (in increasing t)
@@ -346,6 +355,137 @@ int64_t oracle_pair_count(const int32_t* ids, int64_t B, int64_t n, int64_t w, i
         for (int64_t i = 0; i < n; ++i) {
             int64_t cnt = 0;
             for (int64_t j = 0; j <= i; ++j) cnt += pair_allowed(i, j, w, g[i], g[j]);
+            total += cnt;
+        }
+    }
+    return total;
+}
+
+/* ------------------------------------------------------------------------
+ * Multi-membership variant (Korean page §2.3 and Japanese page §2.2: at
+ * inference each token takes its top-k groups; the Korean page §3.4 and
+ * the Japanese page §3.3 report k = 2 at K = 4). A far pair is kept when the
+ * two tokens share ANY group; the kept set is a set, so a pair sharing two
+ * groups is still counted once.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Top-m groups of each token, by the same fp32 scores as oracle_assign:
+ * ids[r][0..m-1] = the m highest scores in decreasing order, exact ties to
+ * the lowest index; margin[r] = s_(m) - s_(m+1) (+inf when K == m), the
+ * score gap that decides membership of the m-th group.
+ */
+int oracle_assign_topk(const float* hidden, const float* P, const float* C, const float* bias,
+                       int64_t B, int64_t n, int64_t d_model, int64_t d_proj, int64_t K,
+                       int64_t m, const int64_t* tokens, int64_t ntokens,
+                       int32_t* ids, float* margin, int nthreads) {
+    if (!hidden || !P || !C || !ids || B < 1 || n < 1 || d_model < 1 || d_proj < 1 || K < 1 ||
+        m < 1 || m > K)
+        return -1;
+    int64_t count = tokens ? ntokens : B * n;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel
+    {
+        float* z = (float*)malloc(sizeof(float) * (size_t)d_proj);
+        float* s = (float*)malloc(sizeof(float) * (size_t)K);
+        char* taken = (char*)malloc((size_t)K);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < count; ++r) {
+            int64_t tok = tokens ? tokens[r] : r;
+            if (tok < 0 || tok >= B * n) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            token_scores(hidden + tok * d_model, P, C, bias, d_model, d_proj, K, z, s);
+            for (int64_t k = 0; k < K; ++k) taken[k] = 0;
+            float last = 0.0f;
+            for (int64_t c = 0; c < m; ++c) {       /* repeated argmax over the rest */
+                int64_t best = -1;
+                for (int64_t k = 0; k < K; ++k)
+                    if (!taken[k] && (best < 0 || s[k] > s[best])) best = k;
+                taken[best] = 1;
+                ids[r * m + c] = (int32_t)best;
+                last = s[best];
+            }
+            float next = -INFINITY;
+            for (int64_t k = 0; k < K; ++k)
+                if (!taken[k] && s[k] > next) next = s[k];
+            if (margin) margin[r] = (K == m) ? INFINITY : last - next;
+        }
+        free(z);
+        free(s);
+        free(taken);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Does token j (groups gj[0..m-1]) share a group with token i (gi)? */
+static int share_group(const int32_t* gi, const int32_t* gj, int64_t m) {
+    for (int64_t a = 0; a < m; ++a)
+        for (int64_t c = 0; c < m; ++c)
+            if (gi[a] == gj[c]) return 1;
+    return 0;
+}
+
+/*
+ * Attention over the multi-membership pattern, fp64, same conventions as
+ * oracle_attn: ids [B][n][m];
+ *   A_i = { j : j <= i and (i - j <= w or groups(i) and groups(j) intersect) }.
+ */
+int oracle_attn_multi(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const int32_t* ids, int64_t m, int64_t B, int64_t Hq, int64_t Hkv,
+                      int64_t n, int64_t d, int64_t w, double scale, const int64_t* rows,
+                      int64_t nrows, double* out, double* lse, int64_t* visited, int nthreads) {
+    if (m < 1 || check_attn_args(q, k, v, ids, B, Hq, Hkv, n, d, w) || !out) return -1;
+    int64_t count = rows ? nrows : B * Hq * n;
+    int64_t group = Hq / Hkv;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)n);
+        int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)n);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < count; ++r) {
+            int64_t row = rows ? rows[r] : r;
+            if (row < 0 || row >= B * Hq * n) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int64_t i = row % n, bh = row / n, h = bh % Hq, b = bh / Hq;
+            int64_t kvh = h / group;
+            const int32_t* g = ids + b * n * m;
+            int64_t cnt = 0;
+            for (int64_t j = 0; j <= i; ++j)
+                if (i - j <= w || share_group(g + i * m, g + j * m, m)) keys[cnt++] = j;
+            double l_se;
+            attend_list(q + row * d, k + (b * Hkv + kvh) * n * d, v + (b * Hkv + kvh) * n * d,
+                        d, scale, keys, cnt, s, out + r * d, &l_se);
+            if (lse) lse[r] = l_se;
+            if (visited) visited[r] = cnt;
+        }
+        free(s);
+        free(keys);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Sum over b and i of |A_i| for the multi-membership pattern. */
+int64_t oracle_pair_count_multi(const int32_t* ids, int64_t m, int64_t B, int64_t n, int64_t w,
+                                int nthreads) {
+    if (!ids || m < 1 || B < 1 || n < 1 || w < 0) return -1;
+    set_threads(nthreads);
+    int64_t total = 0;
+    for (int64_t b = 0; b < B; ++b) {
+        const int32_t* g = ids + b * n * m;
+#pragma omp parallel for schedule(dynamic, 64) reduction(+ : total)
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t cnt = 0;
+            for (int64_t j = 0; j <= i; ++j)
+                cnt += (i - j <= w) || share_group(g + i * m, g + j * m, m);
             total += cnt;
         }
     }

@@ -16,6 +16,7 @@ import oracle
 import test_golden
 import test_oracle_assign_sort as tas
 import test_oracle_attn as tat
+import test_oracle_multi as tmu
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -36,6 +37,13 @@ MUTANTS = {
     "bias subtracted": ("s[k] = bias ? acc + bias[k] : acc;", "s[k] = bias ? acc - bias[k] : acc;"),
     "projection transposed": ("z[j] = z[j] + hm * Prow[j];", "z[j] = z[j] + hm * P[j * d_model + m];"),
     "off-by-one long-range start": ("for (int64_t j = 0; j < i - w; ++j)", "for (int64_t j = 0; j <= i - w; ++j)"),
+    "shared group compares one slot": ("if (gi[a] == gj[c]) return 1;", "if (gi[a] == gj[a]) return 1;"),
+    "top-m ties go high": ("(best < 0 || s[k] > s[best])", "(best < 0 || s[k] >= s[best])"),
+    "top-m margin from the first rank": ("INFINITY : last - next;", "INFINITY : s[ids[r * m]] - next;"),
+    "multi window bound exclusive": ("if (i - j <= w || share_group(g + i * m, g + j * m, m)) keys",
+                                     "if (i - j < w || share_group(g + i * m, g + j * m, m)) keys"),
+    "multi pair count adds both tests": ("cnt += (i - j <= w) || share_group(",
+                                         "cnt += (i - j <= w) + share_group("),
 }
 
 PINS = [
@@ -53,6 +61,11 @@ PINS = [
     tas.test_assign_exact_tie_takes_lowest_index,
     lambda: tas.test_sort_matches_stable_argsort(3, 100, 4),
     test_golden.test_hand_worked_pattern_and_uniform_score_outputs,
+    tmu.test_topk_matches_fp64_ranking_outside_tie_band,
+    tmu.test_topk_exact_ties_take_lowest_index_and_m_equals_K,
+    lambda: tmu.test_all_groups_is_dense_causal(5),
+    lambda: tmu.test_brute_force_set_enumeration(*tmu.CASES[2]),
+    lambda: tmu.test_pair_count_inclusion_exclusion(300, 11, 4),
 ]
 
 
