@@ -9,6 +9,8 @@ which needs no group data) on a second stream, while focus_assign ->
 focus_group_sort run on the main stream; then, once both are done,
 focus_attn_long_range_merge on the main stream (together the two passes are
 focus_attn_fwd). --no-overlap runs all four calls in order on one stream.
+Workloads with m = 2 groups per token use focus_assign_topk, the sort of the
+n*m membership entries and focus_attn_topk_long_range_merge instead.
 W untimed warm-up steps, then K timed steps between two device
 synchronisations. Per-call times come from HIP events recorded around each
 call, on the stream it runs on, inside the timed loop.
@@ -91,11 +93,18 @@ def cpu_baseline(x, wl, target_s):
     from group_gated_sparse_amd import metrics
     cores = oracle.max_threads()
     t0 = time.perf_counter()
-    ids, _ = oracle.assign(x["hidden"], x["P"], x["C"], x["bias"])
+    if wl.m == 1:
+        ids, _ = oracle.assign(x["hidden"], x["P"], x["C"], x["bias"])
+    else:
+        ids, _ = oracle.assign_topk(x["hidden"], x["P"], x["C"], wl.m, x["bias"])
     t_assign = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.group_sort(ids, wl.K)
+    if wl.m == 1:
+        oracle.group_sort(ids, wl.K)
+    else:
+        oracle.group_sort_multi(ids, wl.K)
     t_sort = time.perf_counter() - t0
+    attend = oracle.attn if wl.m == 1 else oracle.attn_multi
     rng = np.random.default_rng(7)
     total_rows = wl.B * wl.Hq * wl.n
     rows_done = 0
@@ -105,14 +114,17 @@ def cpu_baseline(x, wl, target_s):
     while t_attn < target_s and rows_done < total_rows:
         rows = rng.integers(0, total_rows, size=batch)
         t0 = time.perf_counter()
-        _, _, vis = oracle.attn(x["q"], x["k"], x["v"], ids, wl.w, wl.softmax_scale, rows=rows)
+        _, _, vis = attend(x["q"], x["k"], x["v"], ids, wl.w, wl.softmax_scale, rows=rows)
         t_attn += time.perf_counter() - t0
         rows_done += batch
         pairs_done += int(vis.sum())
         if t_attn > 0:
             batch = int(min(max(batch, batch * (target_s - t_attn) / t_attn), 262144))
             batch = max(batch, 256)
-    win, lr = metrics.pair_counts(ids, wl.w)
+    if wl.m == 1:
+        win, lr = metrics.pair_counts(ids, wl.w)
+    else:
+        win, lr, _ = metrics.pair_counts_multi(ids, wl.w)
     pairs_all = (win + lr) * wl.Hq
     t_attn_all = t_attn * pairs_all / max(pairs_done, 1)
     step_s = t_assign + t_sort + t_attn_all
@@ -159,18 +171,21 @@ def main():
     hidden, P, C = dev(x["hidden"]), dev(x["P"]), dev(x["C"])
     bias = None if x["bias"] is None else dev(x["bias"])
     q, k, v = dev16(x["q"]), dev16(x["k"]), dev16(x["v"])
-    B, n, K, w, d, Hq, Hkv = wl.B, wl.n, wl.K, wl.w, wl.d, wl.Hq, wl.Hkv
+    B, n, K, w, d, Hq, Hkv, m = wl.B, wl.n, wl.K, wl.w, wl.d, wl.Hq, wl.Hkv, wl.m
     scale = wl.softmax_scale
     dv = q.device
-    ids = torch.empty((B, n), dtype=torch.int32, device=dv)
-    perm = torch.empty((B, n), dtype=torch.int32, device=dv)
+    ids = torch.empty((B, n) if m == 1 else (B, n, m), dtype=torch.int32, device=dv)
+    perm = torch.empty((B, n * m), dtype=torch.int32, device=dv)
     offs = torch.empty((B, K + 1), dtype=torch.int32, device=dv)
     out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device=dv)
     ws_a = torch.empty(focus.focus_assign_workspace_bytes(wl.d_model, K), dtype=torch.uint8,
                        device=dv)
-    ws_s = torch.empty(max(focus.focus_group_sort_workspace_bytes(B, n, K), 1), dtype=torch.uint8,
-                       device=dv)
-    ws_n = focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w)
+    ws_s = torch.empty(max(focus.focus_group_sort_workspace_bytes(B, n * m, K), 1),
+                       dtype=torch.uint8, device=dv)
+    if m == 1:
+        ws_n = focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w)
+    else:
+        ws_n = focus.focus_attn_topk_workspace_bytes(B, Hq, Hkv, n, d, K, m, w)
     ws_t = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dv)
     stream = torch.cuda.current_stream()
 
@@ -179,6 +194,22 @@ def main():
     # events: 0 step start, 1 assign end, 2 sort end, 3 merge start, 4 step end (main
     # stream); 5 window start, 6 window end (the stream the window pass runs on)
     NEV = 7
+
+    def assign():
+        if m == 1:
+            focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False,
+                               workspace=ws_a)
+        else:
+            focus.focus_assign_topk(hidden, P, C, m, bias, group_ids=ids, want_margin=False,
+                                    workspace=ws_a)
+
+    def long_range():
+        if m == 1:
+            focus.focus_attn_long_range_merge(q, k, v, ids, perm, offs, K, w, scale,
+                                              workspace=ws_t, out=out)
+        else:
+            focus.focus_attn_topk_long_range_merge(q, k, v, ids, perm, offs, K, m, w, scale,
+                                                   workspace=ws_t, out=out)
 
     def step(evs=None):
         def mark(i, st):
@@ -189,8 +220,7 @@ def main():
         if overlap:
             side.wait_stream(stream)   # the previous merge has consumed the workspace
         else:
-            focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False,
-                               workspace=ws_a)
+            assign()
             mark(1, stream)
             focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
             mark(2, stream)
@@ -198,15 +228,13 @@ def main():
         focus.focus_attn_window(q, k, v, K, w, scale, workspace=ws_t, out=out, stream=ws_stream)
         mark(6, ws_stream)
         if overlap:
-            focus.focus_assign(hidden, P, C, bias, group_ids=ids, want_margin=False,
-                               workspace=ws_a)
+            assign()
             mark(1, stream)
             focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
             mark(2, stream)
             stream.wait_stream(side)
         mark(3, stream)
-        focus.focus_attn_long_range_merge(q, k, v, ids, perm, offs, K, w, scale, workspace=ws_t,
-                                          out=out)
+        long_range()
         mark(4, stream)
 
     log(f"warm-up {args.warmup} steps ({'overlapped' if overlap else 'one stream'})")
@@ -231,7 +259,11 @@ def main():
     log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
 
     gids = ids.cpu().numpy()
-    win, lr = metrics.pair_counts(gids, w)
+    if m == 1:
+        win, lr = metrics.pair_counts(gids, w)
+        lr_visited = lr
+    else:
+        win, lr, lr_visited = metrics.pair_counts_multi(gids, w)
     pairs = win + lr
     flops = metrics.attn_flops(pairs, Hq, d)
     attn_ms = phase["window"] + phase["long_range_merge"]
@@ -250,12 +282,13 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "n": n, "d_head": d,
                    "d_model": wl.d_model, "d_proj": wl.d_proj, "K": K, "window": w,
-                   "out_dtype": "bf16",
+                   "groups_per_token": m, "out_dtype": "bf16",
                    "streams": "window pass overlapped with assign+sort" if overlap
                    else "one stream"},
         "visited_pairs_per_head": pairs,
         "window_pairs_per_head": win,
         "long_range_pairs_per_head": lr,
+        "long_range_pairs_visited_per_head": lr_visited,
         "phase_ms": phase,
         "attn_ms": attn_ms,
         "attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
@@ -267,7 +300,8 @@ def main():
     kern = max(("long_range_merge", "window"), key=lambda nm: phase[nm])
     kflops = metrics.attn_flops(lr if kern == "long_range_merge" else win, Hq, d)
     ach = kflops / (phase[kern] * 1e-3) / 1e12
-    kname = f"attn_kernel<{d},1>" if kern == "long_range_merge" else f"attn_kernel<{d},0>"
+    kname = (f"attn_kernel<{d},{1 if m == 1 else 3}>" if kern == "long_range_merge"
+             else f"attn_kernel<{d},0>")
     res["roofline"] = {"kernel": kname + (" (long-range pass + merge)" if kern == "long_range_merge"
                                           else " (window pass)"),
                        "bound": "mfma", "achieved": ach,

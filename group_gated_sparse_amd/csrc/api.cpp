@@ -61,6 +61,7 @@ constexpr int64_t kMaxGrid = 2147483647;
 
 struct AttnShape {
     int B, Hq, Hkv, n, d, K, w;
+    int m = 1;   // groups per token
 };
 
 focus_status check_attn_shape(const AttnShape& s, bool needs_groups) {
@@ -75,11 +76,19 @@ focus_status check_attn_shape(const AttnShape& s, bool needs_groups) {
         REQUIRE(s.K >= 1 && s.K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED,
                 "K must be in [1, %d] (got %d)", FOCUS_MAX_GROUPS, s.K);
         REQUIRE(s.w >= 0, FOCUS_ERR_INVALID_ARGUMENT, "window must be >= 0 (got %d)", s.w);
+        REQUIRE(s.m >= 1 && s.m <= FOCUS_MAX_MEMBERSHIPS, FOCUS_ERR_UNSUPPORTED,
+                "m must be in [1, %d] (got %d)", FOCUS_MAX_MEMBERSHIPS, s.m);
+        REQUIRE(s.m <= s.K, FOCUS_ERR_INVALID_ARGUMENT, "m (%d) must be <= K (%d)", s.m, s.K);
+        // entries of the sorted order: positions are packed with 6 bits of
+        // group beside them when m = 2
+        REQUIRE((int64_t)s.n * s.m <= (s.m == 1 ? (int64_t)INT32_MAX - 4096 : (int64_t)1 << 24),
+                FOCUS_ERR_UNSUPPORTED, "n * m too large (n=%d, m=%d)", s.n, s.m);
     }
     const int64_t rows = (int64_t)s.B * s.Hq * s.n;
     REQUIRE(rows / s.Hq / s.B == s.n, FOCUS_ERR_INVALID_ARGUMENT, "B*Hq*n overflows");
-    // Workgroup count of the attention grids: B * Hq * ceil(n / 16) / 8 at most.
-    REQUIRE((int64_t)s.B * s.Hq * ((s.n + 15) / 16) <= kMaxGrid, FOCUS_ERR_UNSUPPORTED,
+    // Workgroup count of the attention grids: B * Hq * ceil(n * m / 16) / 8 at most.
+    REQUIRE((int64_t)s.B * s.Hq * (((int64_t)s.n * s.m + 15) / 16) <= kMaxGrid,
+            FOCUS_ERR_UNSUPPORTED,
             "problem too large for one launch grid");
     REQUIRE((int64_t)s.B * s.Hkv <= 65535, FOCUS_ERR_UNSUPPORTED, "B*Hkv must be <= 65535");
     return ok();
@@ -116,10 +125,10 @@ enum class AttnPart { kAll, kWindow, kLongRangeMerge };
 
 focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* group_ids, const int32_t* perm,
-                        const int32_t* group_offsets, int B, int Hq, int Hkv, int n, int d, int K, int w, float scale, void* out,
-                        focus_dtype out_dtype, float* lse, void* workspace, size_t ws_bytes,
-                        focus_stream_t stream) {
-    const AttnShape s{B, Hq, Hkv, n, d, K, w};
+                        const int32_t* group_offsets, int B, int Hq, int Hkv, int n, int d, int K,
+                        int m, int w, float scale, void* out, focus_dtype out_dtype, float* lse,
+                        void* workspace, size_t ws_bytes, focus_stream_t stream) {
+    const AttnShape s{B, Hq, Hkv, n, d, K, w, m};
     focus_status st = check_attn_shape(s, true);
     if (st != FOCUS_OK) return st;
     st = check_attn_buffers(q, k, v, s, out, out_dtype, lse, scale);
@@ -129,7 +138,9 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
         REQUIRE_PTR(perm, 4);
         REQUIRE_PTR(group_offsets, 4);
     }
-    const size_t need = focus::attn_workspace(B, Hq, Hkv, n, d, w);
+    // the window pass only uses the leading part of the workspace, which
+    // is laid out the same for every m
+    const size_t need = focus::attn_workspace(B, Hq, Hkv, n, d, w, part == AttnPart::kWindow ? 1 : m);
     if (need > 0) {
         REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -137,7 +148,8 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
                 "workspace too small: %zu bytes given, %zu required", ws_bytes, need);
     }
     focus::AttnProblem p{q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n, d, K, w, scale,
-                         out, out_dtype == FOCUS_F32 ? 1 : 0, lse, need > 0 ? workspace : nullptr};
+                         out, out_dtype == FOCUS_F32 ? 1 : 0, lse, need > 0 ? workspace : nullptr,
+                         m};
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (part != AttnPart::kLongRangeMerge) {
         hipError_t e = focus::launch_attn_window(p, hs);
@@ -148,6 +160,43 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
         if (e != hipSuccess) return device_status(e, "long-range attention launch");
     }
     return ok();
+}
+
+focus_status assign_entry(const float* hidden, const float* P, const float* C, const float* bias,
+                          int B, int n, int d_model, int d_proj, int K, int m,
+                          int32_t* group_ids, float* margin, void* workspace,
+                          size_t workspace_bytes, focus_stream_t stream) {
+    REQUIRE(B >= 1 && n >= 1, FOCUS_ERR_INVALID_ARGUMENT, "B and n must be >= 1 (got B=%d n=%d)",
+            B, n);
+    REQUIRE(d_model >= 1 && d_proj >= 1, FOCUS_ERR_INVALID_ARGUMENT,
+            "d_model and d_proj must be >= 1");
+    REQUIRE(d_model % 4 == 0, FOCUS_ERR_UNSUPPORTED, "d_model must be a multiple of 4 (got %d)",
+            d_model);
+    REQUIRE(K >= 1 && K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)",
+            FOCUS_MAX_GROUPS, K);
+    REQUIRE(m >= 1 && m <= FOCUS_MAX_MEMBERSHIPS, FOCUS_ERR_UNSUPPORTED,
+            "m must be in [1, %d] (got %d)", FOCUS_MAX_MEMBERSHIPS, m);
+    REQUIRE(m <= K, FOCUS_ERR_INVALID_ARGUMENT, "m (%d) must be <= K (%d)", m, K);
+    REQUIRE_PTR(hidden, 16);
+    REQUIRE_PTR(P, 4);
+    REQUIRE_PTR(C, 4);
+    if (bias) REQUIRE(aligned(bias, 4), FOCUS_ERR_INVALID_ARGUMENT, "bias must be 4-byte aligned");
+    REQUIRE_PTR(group_ids, 4);
+    if (margin) REQUIRE(aligned(margin, 4), FOCUS_ERR_INVALID_ARGUMENT, "margin must be 4-byte aligned");
+    const int64_t ntok = (int64_t)B * n;
+    REQUIRE((ntok + 31) / 32 <= kMaxGrid, FOCUS_ERR_UNSUPPORTED, "too many tokens for one launch");
+    const size_t need = focus::assign_workspace(d_model, K);
+    REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    REQUIRE(workspace_bytes >= need, FOCUS_ERR_WORKSPACE,
+            "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+    const size_t hbytes = (size_t)ntok * d_model * 4;
+    REQUIRE(!overlaps(group_ids, (size_t)ntok * m * 4, hidden, hbytes),
+            FOCUS_ERR_INVALID_ARGUMENT, "group_ids must not overlap hidden");
+    return device_status(focus::launch_assign(hidden, P, C, bias, B, n, d_model, d_proj, K, m,
+                                              group_ids, margin, workspace,
+                                              static_cast<hipStream_t>(stream)),
+                         "assign launch");
 }
 
 }  // namespace
@@ -167,34 +216,16 @@ focus_status focus_assign(const float* hidden, const float* P, const float* C, c
                           int B, int n, int d_model, int d_proj, int K, int32_t* group_ids,
                           float* margin, void* workspace, size_t workspace_bytes,
                           focus_stream_t stream) {
-    REQUIRE(B >= 1 && n >= 1, FOCUS_ERR_INVALID_ARGUMENT, "B and n must be >= 1 (got B=%d n=%d)",
-            B, n);
-    REQUIRE(d_model >= 1 && d_proj >= 1, FOCUS_ERR_INVALID_ARGUMENT,
-            "d_model and d_proj must be >= 1");
-    REQUIRE(d_model % 4 == 0, FOCUS_ERR_UNSUPPORTED, "d_model must be a multiple of 4 (got %d)",
-            d_model);
-    REQUIRE(K >= 1 && K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)",
-            FOCUS_MAX_GROUPS, K);
-    REQUIRE_PTR(hidden, 16);
-    REQUIRE_PTR(P, 4);
-    REQUIRE_PTR(C, 4);
-    if (bias) REQUIRE(aligned(bias, 4), FOCUS_ERR_INVALID_ARGUMENT, "bias must be 4-byte aligned");
-    REQUIRE_PTR(group_ids, 4);
-    if (margin) REQUIRE(aligned(margin, 4), FOCUS_ERR_INVALID_ARGUMENT, "margin must be 4-byte aligned");
-    const int64_t ntok = (int64_t)B * n;
-    REQUIRE((ntok + 31) / 32 <= kMaxGrid, FOCUS_ERR_UNSUPPORTED, "too many tokens for one launch");
-    const size_t need = focus::assign_workspace(d_model, K);
-    REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
-    REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    REQUIRE(workspace_bytes >= need, FOCUS_ERR_WORKSPACE,
-            "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
-    const size_t hbytes = (size_t)ntok * d_model * 4;
-    REQUIRE(!overlaps(group_ids, (size_t)ntok * 4, hidden, hbytes), FOCUS_ERR_INVALID_ARGUMENT,
-            "group_ids must not overlap hidden");
-    return device_status(focus::launch_assign(hidden, P, C, bias, B, n, d_model, d_proj, K,
-                                              group_ids, margin, workspace,
-                                              static_cast<hipStream_t>(stream)),
-                         "assign launch");
+    return assign_entry(hidden, P, C, bias, B, n, d_model, d_proj, K, 1, group_ids, margin,
+                        workspace, workspace_bytes, stream);
+}
+
+focus_status focus_assign_topk(const float* hidden, const float* P, const float* C,
+                               const float* bias, int B, int n, int d_model, int d_proj, int K,
+                               int m, int32_t* group_ids, float* margin, void* workspace,
+                               size_t workspace_bytes, focus_stream_t stream) {
+    return assign_entry(hidden, P, C, bias, B, n, d_model, d_proj, K, m, group_ids, margin,
+                        workspace, workspace_bytes, stream);
 }
 
 size_t focus_group_sort_workspace_bytes(int B, int n, int K) {
@@ -242,7 +273,7 @@ focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                             focus_dtype out_dtype, float* lse, void* workspace,
                             size_t workspace_bytes, focus_stream_t stream) {
     return attn_entry(AttnPart::kAll, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n,
-                      d_head, K, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
+                      d_head, K, 1, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
                       stream);
 }
 
@@ -253,7 +284,7 @@ focus_status focus_attn_window(const uint16_t* q, const uint16_t* k, const uint1
                                focus_dtype out_dtype, float* lse, void* workspace,
                                size_t workspace_bytes, focus_stream_t stream) {
     return attn_entry(AttnPart::kWindow, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n,
-                      d_head, K, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
+                      d_head, K, 1, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
                       stream);
 }
 
@@ -265,7 +296,40 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
                                          void* workspace, size_t workspace_bytes,
                                          focus_stream_t stream) {
     return attn_entry(AttnPart::kLongRangeMerge, q, k, v, group_ids, perm, group_offsets, B, Hq,
-                      Hkv, n, d_head, K, window, scale, out, out_dtype, lse, workspace,
+                      Hkv, n, d_head, K, 1, window, scale, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+size_t focus_attn_topk_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int m,
+                                       int window) {
+    (void)K;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;
+    if (d_head != 32 && d_head != 64 && d_head != 128) return 0;
+    if (m < 1 || m > FOCUS_MAX_MEMBERSHIPS || (int64_t)n * m > ((int64_t)1 << 24)) return 0;
+    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, m);
+}
+
+focus_status focus_attn_topk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* group_ids, const int32_t* perm,
+                                 const int32_t* group_offsets, int B, int Hq, int Hkv, int n,
+                                 int d_head, int K, int m, int window, float scale, void* out,
+                                 focus_dtype out_dtype, float* lse, void* workspace,
+                                 size_t workspace_bytes, focus_stream_t stream) {
+    return attn_entry(AttnPart::kAll, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n,
+                      d_head, K, m, window, scale, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t* k,
+                                              const uint16_t* v, const int32_t* group_ids,
+                                              const int32_t* perm, const int32_t* group_offsets,
+                                              int B, int Hq, int Hkv, int n, int d_head, int K,
+                                              int m, int window, float scale, void* out,
+                                              focus_dtype out_dtype, float* lse,
+                                              void* workspace, size_t workspace_bytes,
+                                              focus_stream_t stream) {
+    return attn_entry(AttnPart::kLongRangeMerge, q, k, v, group_ids, perm, group_offsets, B, Hq,
+                      Hkv, n, d_head, K, m, window, scale, out, out_dtype, lse, workspace,
                       workspace_bytes, stream);
 }
 

@@ -1,8 +1,10 @@
-// Hard group assignment: group_ids[t] = argmax_k (h_t · P) · C_k + bias_k.
+// Hard group assignment: the top-M groups of each token by the scores
+// s_k = (h_t · P) · C_k + bias_k (M = 1: group_ids[t] = argmax_k s_k).
 //
 // Focus ("Focus: Learning Which Attention Pairs Matter", technical summary
 // §2.1: the hidden state is projected and compared with K centroids in
-// centroid space; §2.2: a hard top-k assignment at inference, k = 1 here).
+// centroid space; §2.2: a hard top-k assignment at inference, k = 1 or 2
+// here; the Korean page §2.3 and §3.4 give the k = 2 variant).
 //
 // (h P) C^T is regrouped as h (P C^T): a tiny prologue forms W^T = C P^T
 // (K x d_model, fp32) once per call, so the streaming pass does d_model*K
@@ -115,7 +117,32 @@ struct WRegs {
     bf16x8 f[NB][4][2];
 };
 
-template <int NB>
+// Running top list of (score, group), best first; the order is score
+// descending, then group ascending, so exact ties go to the lowest index.
+template <int M>
+struct TopList {
+    float v[M + 1];
+    int g[M + 1];
+};
+__device__ __forceinline__ bool ranks_before(float a, int ga, float b, int gb) {
+    return a > b || (a == b && ga < gb);
+}
+template <int M>
+__device__ __forceinline__ void top_insert(TopList<M>& t, float x, int gx) {
+#pragma unroll
+    for (int p = 0; p <= M; ++p) {
+        if (ranks_before(x, gx, t.v[p], t.g[p])) {
+            const float tv = t.v[p];
+            const int tg = t.g[p];
+            t.v[p] = x;
+            t.g[p] = gx;
+            x = tv;
+            gx = tg;
+        }
+    }
+}
+
+template <int NB, int M>
 __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
     const float* __restrict__ hidden, const __bf16* __restrict__ wfrag,
     const float* __restrict__ bias, int64_t ntok, int d_model, int dpad, int K,
@@ -220,44 +247,44 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
                           red[((1 * NB + mb) * 16 + e) * 64 + lane]) +
                          red[((2 * NB + mb) * 16 + e) * 64 + lane];
 
-    // Lane holds scores of groups k = mb*32 + 8*i + 4*hh + j (e = 4*i + j),
-    // visited in increasing k. Top-2 with exact ties resolved to the lowest k.
-    float b1 = kNegInf, b2 = kNegInf;
-    int i1 = 0x7fffffff;
+    // Lane holds scores of groups k = mb*32 + 8*i + 4*hh + j (e = 4*i + j).
+    // Each lane half keeps the top M+1 of its groups; the halves then swap
+    // lists and both merge them, so both hold the top M+1 over all groups.
+    TopList<M> top;
+#pragma unroll
+    for (int p = 0; p <= M; ++p) {
+        top.v[p] = kNegInf;
+        top.g[p] = 0x7fffffff;
+    }
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int k = mb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
             if (k >= K) continue;
-            const float sc = bias ? acc[mb][e] + bias[k] : acc[mb][e];
-            if (sc > b1) {
-                b2 = b1;
-                b1 = sc;
-                i1 = k;
-            } else if (sc > b2) {
-                b2 = sc;
-            }
+            top_insert(top, bias ? acc[mb][e] + bias[k] : acc[mb][e], k);
         }
-    const float ob1 = other_half(b1), ob2 = other_half(b2);
-    const int oi1 = other_half_i(i1);
-    float m1, m2;
-    int mi;
-    if (b1 > ob1 || (b1 == ob1 && i1 < oi1)) {
-        m1 = b1; mi = i1; m2 = fmaxf(b2, ob1);
-    } else {
-        m1 = ob1; mi = oi1; m2 = fmaxf(ob2, b1);
+    float ov[M + 1];
+    int og[M + 1];
+#pragma unroll
+    for (int p = 0; p <= M; ++p) {
+        ov[p] = other_half(top.v[p]);
+        og[p] = other_half_i(top.g[p]);
     }
+#pragma unroll
+    for (int p = 0; p <= M; ++p) top_insert(top, ov[p], og[p]);
     if (hh == 0 && tvalid) {
-        ids[tok] = mi;
-        if (margin) margin[tok] = m1 - m2;
+#pragma unroll
+        for (int c = 0; c < M; ++c) ids[tok * M + c] = top.g[c];
+        // score gap deciding the M-th membership (+inf when K == M)
+        if (margin) margin[tok] = top.v[M - 1] - top.v[M];
     }
 }
 
 }  // namespace
 
 hipError_t launch_assign(const float* hidden, const float* P, const float* C, const float* bias,
-                         int B, int n, int d_model, int d_proj, int K, int32_t* ids,
+                         int B, int n, int d_model, int d_proj, int K, int M, int32_t* ids,
                          float* margin, void* workspace, hipStream_t stream) {
     const int KP = assign_kpad(K), dpad = assign_dpad(d_model);
     __bf16* wfrag = static_cast<__bf16*>(workspace);
@@ -267,12 +294,15 @@ hipError_t launch_assign(const float* hidden, const float* P, const float* C, co
     if (e != hipSuccess) return e;
     const int64_t ntok = (int64_t)B * n;
     const dim3 grid((unsigned)((ntok + 31) / 32));
-    if (KP == 32)
-        hipLaunchKernelGGL(assign_argmax_kernel<1>, grid, dim3(256), 0, stream, hidden, wfrag,
-                           bias, ntok, d_model, dpad, K, ids, margin);
-    else
-        hipLaunchKernelGGL(assign_argmax_kernel<2>, grid, dim3(256), 0, stream, hidden, wfrag,
-                           bias, ntok, d_model, dpad, K, ids, margin);
+#define FOCUS_ASSIGN_LAUNCH(NB_, M_)                                                          \
+    hipLaunchKernelGGL((assign_argmax_kernel<NB_, M_>), grid, dim3(256), 0, stream, hidden,   \
+                       wfrag, bias, ntok, d_model, dpad, K, ids, margin)
+    if (KP == 32 && M == 1) FOCUS_ASSIGN_LAUNCH(1, 1);
+    else if (KP == 32 && M == 2) FOCUS_ASSIGN_LAUNCH(1, 2);
+    else if (M == 1) FOCUS_ASSIGN_LAUNCH(2, 1);
+    else if (M == 2) FOCUS_ASSIGN_LAUNCH(2, 2);
+    else return hipErrorInvalidValue;
+#undef FOCUS_ASSIGN_LAUNCH
     return hipGetLastError();
 }
 

@@ -55,6 +55,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -66,7 +67,8 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kProbSumCap = 256.0f;  // a lane's probability sum that triggers a rescale
 constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 
-enum { kWindow = 0, kLongRange = 1, kDense = 2 };
+// kLongMulti: the long-range pass over membership entries, two groups per token.
+enum { kWindow = 0, kLongRange = 1, kDense = 2, kLongMulti = 3 };
 
 struct AttnArgs {
     const uint16_t* q;
@@ -82,6 +84,7 @@ struct AttnArgs {
     void* out;
     float* lse;
     int B, Hq, Hkv, n, K, w;
+    int ne;        // slots of the tiled order: n, or n*m entries in the multi pass
     int hpk;       // Hq / Hkv
     int G;         // query heads packed per workgroup
     int TT;        // tokens per workgroup tile (ROWS / G)
@@ -167,15 +170,18 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
 }
 
 // ---------------------------------------------------------------------------
-// Sorted copies for the long-range pass: k_s[b][h][s] = k[b][h][perm[b][s]]
-// (same for v), one 16-byte chunk per thread, and spos[b][s] = perm[b][s]
-// followed by KPOS_PAD padding slots (kNoPos), written by the kv-head-0 grid
-// row.
+// Sorted copies for the long-range pass: k_s[b][h][s] = k[b][h][pos(s)]
+// (same for v), one 16-byte chunk per thread, and spos[b][s] followed by
+// KPOS_PAD padding slots (kNoPos), written by the kv-head-0 grid row. Slot s
+// holds entry e = perm[b][s] of token pos(s) = e / m. With one group per
+// token spos is the position; with two it is position * 64 + the token's
+// other group (the pair rule needs both).
 __global__ __launch_bounds__(256) void attn_gather_kernel(const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v,
                                                           const int32_t* __restrict__ perm,
-                                                          int n, int Hkv, int D,
-                                                          uint16_t* __restrict__ ks,
+                                                          const int32_t* __restrict__ ids,
+                                                          int n, int ne, int m, int K, int Hkv,
+                                                          int D, uint16_t* __restrict__ ks,
                                                           uint16_t* __restrict__ vs,
                                                           int32_t* __restrict__ spos) {
     const int nch = D / 8;
@@ -183,18 +189,22 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(const uint16_t* __rest
     const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const int64_t s = x / nch;
     const int c = (int)(x % nch);
-    if (s >= n + KPOS_PAD) return;
-    if (s >= n) {
-        if (h == 0 && c == 0) spos[(int64_t)b * (n + KPOS_PAD) + s] = kNoPos;
+    if (s >= ne + KPOS_PAD) return;
+    if (s >= ne) {
+        if (h == 0 && c == 0) spos[(int64_t)b * (ne + KPOS_PAD) + s] = kNoPos;
         return;
     }
-    const int pos = clampi(perm[(int64_t)b * n + s], 0, n - 1);
-    if (h == 0 && c == 0) spos[(int64_t)b * (n + KPOS_PAD) + s] = pos;
-    const int64_t base = (int64_t)bh * n * D;
-    *reinterpret_cast<u32x4*>(ks + base + s * D + c * 8) =
-        *reinterpret_cast<const u32x4*>(k + base + (int64_t)pos * D + c * 8);
-    *reinterpret_cast<u32x4*>(vs + base + s * D + c * 8) =
-        *reinterpret_cast<const u32x4*>(v + base + (int64_t)pos * D + c * 8);
+    const int e = clampi(perm[(int64_t)b * ne + s], 0, ne - 1);
+    const int pos = e / m;
+    if (h == 0 && c == 0) {
+        int val = pos;
+        if (m == 2) val = (pos << 6) | clampi(ids[(int64_t)b * ne + (e ^ 1)], 0, K - 1);
+        spos[(int64_t)b * (ne + KPOS_PAD) + s] = val;
+    }
+    const int64_t src = (int64_t)bh * n * D + (int64_t)pos * D + c * 8;
+    const int64_t dst = ((int64_t)bh * ne + s) * D + c * 8;
+    *reinterpret_cast<u32x4*>(ks + dst) = *reinterpret_cast<const u32x4*>(k + src);
+    *reinterpret_cast<u32x4*>(vs + dst) = *reinterpret_cast<const u32x4*>(v + src);
 }
 
 // Key slots [ob, kend) that group g contributes to the long-range pass of
@@ -203,7 +213,8 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(const uint16_t* __rest
 // tile) - w. Positions increase inside a segment, so that cut is a binary
 // search, and no later slot of the segment can pair with any query of g here.
 // kfull: slots below it pair with every query of g in the tile (position
-// below (smallest query position) - w).
+// below (smallest query position) - w). Slots hold entries e of position
+// e / m, and e / m < bound exactly when e < m * bound.
 __device__ __forceinline__ int first_slot_at_or_above(const int32_t* perm_b, int lo, int hi,
                                                       int bound) {
     while (lo < hi) {
@@ -212,19 +223,19 @@ __device__ __forceinline__ int first_slot_at_or_above(const int32_t* perm_b, int
     }
     return lo;
 }
-__device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32_t* offb, int n,
-                                              int w, int s0, int s1, int g, int& ob, int& kend,
-                                              int& kfull) {
-    ob = clampi(offb[g], 0, n);
-    const int oe = clampi(offb[g + 1], ob, n);
+__device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32_t* offb, int ne,
+                                              int m, int w, int s0, int s1, int g, int& ob,
+                                              int& kend, int& kfull) {
+    ob = clampi(offb[g], 0, ne);
+    const int oe = clampi(offb[g + 1], ob, ne);
     const int qlo = max(s0, ob), qhi = min(s1, oe);
     kend = ob;
     kfull = ob;
     if (qlo < qhi) {
-        const int maxpos = clampi(perm_b[qhi - 1], 0, n - 1);
-        const int minpos = clampi(perm_b[qlo], 0, n - 1);
-        kend = first_slot_at_or_above(perm_b, ob, qhi, maxpos - w);
-        kfull = first_slot_at_or_above(perm_b, ob, kend, minpos - w);
+        const int maxpos = clampi(perm_b[qhi - 1], 0, ne - 1) / m;
+        const int minpos = clampi(perm_b[qlo], 0, ne - 1) / m;
+        kend = first_slot_at_or_above(perm_b, ob, qhi, m * (maxpos - w));
+        kfull = first_slot_at_or_above(perm_b, ob, kend, m * (minpos - w));
     }
 }
 
@@ -236,17 +247,19 @@ __device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32
 __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restrict__ ids,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets,
-                                                        int n, int K, int w, int TT, int ntiles,
-                                                        int bn_keys, int32_t* __restrict__ plan) {
+                                                        int ne, int m, int K, int w, int TT,
+                                                        int ntiles, int bn_keys,
+                                                        int32_t* __restrict__ plan) {
     const int b = blockIdx.y;
     const int tile = blockIdx.x * 256 + threadIdx.x;
     if (tile >= ntiles) return;
-    const int64_t bn = (int64_t)b * n;
-    const int32_t* perm_b = perm + bn;
+    const int64_t bne = (int64_t)b * ne;
+    const int32_t* perm_b = perm + bne;
     const int32_t* offb = offsets + (int64_t)b * (K + 1);
-    const int s0 = tile * TT, s1 = min(n, s0 + TT);
-    const int gf = clampi(ids[bn + clampi(perm_b[s0], 0, n - 1)], 0, K - 1);
-    const int gl = clampi(ids[bn + clampi(perm_b[s1 - 1], 0, n - 1)], gf, K - 1);
+    const int s0 = tile * TT, s1 = min(ne, s0 + TT);
+    // ids [B][n][m] read flat: entry e of batch b is ids[b * ne + e]
+    const int gf = clampi(ids[bne + clampi(perm_b[s0], 0, ne - 1)], 0, K - 1);
+    const int gl = clampi(ids[bne + clampi(perm_b[s1 - 1], 0, ne - 1)], gf, K - 1);
     const int nseg = gl - gf + 1;
     int32_t* rec = plan + ((int64_t)b * ntiles + tile) * PLAN_INTS;
     if (nseg > SEGCAP) {
@@ -256,14 +269,14 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
     int run = 0;
     for (int t = 0; t < nseg; ++t) {
         int ob, kend, kfull;
-        segment_range(perm_b, offb, n, w, s0, s1, gf + t, ob, kend, kfull);
+        segment_range(perm_b, offb, ne, m, w, s0, s1, gf + t, ob, kend, kfull);
         rec[4 + 4 * t] = ob;
         rec[5 + 4 * t] = kend;
         rec[6 + 4 * t] = run;
         rec[7 + 4 * t] = kfull;
         run += (kend - ob + bn_keys - 1) / bn_keys;
     }
-    const int ob0 = clampi(offb[gf], 0, n), oe0 = clampi(offb[gf + 1], ob0, n);
+    const int ob0 = clampi(offb[gf], 0, ne), oe0 = clampi(offb[gf + 1], ob0, ne);
     rec[0] = nseg;
     rec[1] = gf;
     rec[2] = (s0 >= ob0 && s1 <= oe0) ? 1 : 0;
@@ -275,7 +288,10 @@ template <int D, int PHASE>
 __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(AttnArgs a) {
     using G = Geom<D, attn_tile_keys(D, PHASE)>;
     constexpr int BN = G::BN;
-    constexpr bool SORTED = PHASE == kLongRange;
+    constexpr bool SORTED = PHASE == kLongRange || PHASE == kLongMulti;
+    constexpr bool MULTI = PHASE == kLongMulti;   // entries of two groups per token
+    // slots of the tiled order (n except in the multi pass)
+    const int ne = MULTI ? a.ne : a.n;
     // smem = [K/V buffer 0 | K/V buffer 1]; buffer 1 also stages the Q tile in
     // the prologue, and the whole block stages the output rows in the epilogue.
     __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
@@ -283,7 +299,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     unsigned char* const buf1 = smem + 2 * G::TILEB;
     __shared__ __attribute__((aligned(1024))) int kpos0[KPOS_PAD], kpos1[KPOS_PAD];
     __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1], seg_kfull[MAXSEG];
-    __shared__ int rowpos[ROWS];  // sequence position of each query row (sorted pass)
+    __shared__ int rowpos[ROWS];  // entry (= position with one group) of each query row (sorted pass)
+    __shared__ int excl_any;      // multi pass: some row can meet a pair shared twice
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int rl = lane & 31, hh = lane >> 5;
@@ -306,21 +323,27 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     const int R = wave * 32 + rl;
     const int hslot = R / a.TT, tok = R % a.TT;
     const int h = kvh * a.hpk + slice * a.G + hslot;
-    const int64_t bn = (int64_t)b * a.n;
+    const int64_t bne = (int64_t)b * ne;
     const int s_row = tile * a.TT + tok;
-    const bool rvalid = s_row < a.n;
-    int pos_i = rvalid ? s_row : 0;
-    if (SORTED && rvalid) pos_i = clampi(a.perm[bn + s_row], 0, a.n - 1);
+    const bool rvalid = s_row < ne;
+    // entry of the row (sorted passes: perm holds entries t*m + c; m = 1
+    // makes the entry the position) and its sequence position
+    int ent_i = rvalid ? s_row : 0;
+    if (SORTED && rvalid) ent_i = clampi(a.perm[bne + s_row], 0, ne - 1);
+    const int pos_i = MULTI ? (ent_i >> 1) : ent_i;
+    // multi pass: the row token's other group
+    const int oth_i = (MULTI && rvalid) ? clampi(a.ids[bne + (ent_i ^ 1)], 0, a.K - 1) : 0;
 
-    const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * a.n * D;
-    const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * a.n * D;
+    const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * ne * D;
+    const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * ne * D;
 
     // ---- the key tiles this workgroup visits: ntl tiles, tile tau at key
     // ---- slot kt0(tau), valid slots below kend(tau).
     int ntl = 0;
     int kstart = 0, kend0 = 0;               // sequence-order passes
     int gfirst = 0, g_i = -1;                // long-range pass
-    bool rows_one_group = false;
+    int x_i = -1;                            // multi pass: excluded key group, or -1
+    bool rows_one_group = false, rows_excl = false;
     if (!SORTED) {
         const int q0 = tile * a.TT;
         const int qlast = min(a.n, q0 + a.TT) - 1;
@@ -329,9 +352,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         ntl = (kend0 - kstart + BN - 1) / BN;
     } else {
         const int s0 = tile * a.TT;
-        const int s1 = min(a.n, s0 + a.TT);
+        const int s1 = min(ne, s0 + a.TT);
         const int32_t* rec = a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS;
-        if (hh == 0) rowpos[R] = pos_i;  // published by the barrier below
+        if (hh == 0) rowpos[R] = ent_i;  // published by the barrier below
+        if (MULTI && tid == 0) excl_any = 0;
         // plan values are uniform: readfirstlane keeps them in scalar registers
         int nseg = __builtin_amdgcn_readfirstlane(rec[0]);
         if (nseg >= 0) {
@@ -339,8 +363,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             gfirst = clampi(__builtin_amdgcn_readfirstlane(rec[1]), 0, a.K - 1);
             rows_one_group = __builtin_amdgcn_readfirstlane(rec[2]) != 0;
             if (tid < nseg) {
-                const int ob = clampi(rec[4 + 4 * tid], 0, a.n);
-                const int kend = clampi(rec[5 + 4 * tid], ob, a.n);
+                const int ob = clampi(rec[4 + 4 * tid], 0, ne);
+                const int kend = clampi(rec[5 + 4 * tid], ob, ne);
                 seg_ob[tid] = ob;
                 seg_kend[tid] = kend;
                 seg_t0[tid] = rec[6 + 4 * tid];
@@ -353,13 +377,14 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             // segments here (every tile of them is treated as partial).
             const int32_t* offb = a.offsets + (int64_t)b * (a.K + 1);
             gfirst = __builtin_amdgcn_readfirstlane(
-                clampi(a.ids[bn + clampi(a.perm[bn + s0], 0, a.n - 1)], 0, a.K - 1));
+                clampi(a.ids[bne + clampi(a.perm[bne + s0], 0, ne - 1)], 0, a.K - 1));
             const int glast = __builtin_amdgcn_readfirstlane(
-                clampi(a.ids[bn + clampi(a.perm[bn + s1 - 1], 0, a.n - 1)], gfirst, a.K - 1));
+                clampi(a.ids[bne + clampi(a.perm[bne + s1 - 1], 0, ne - 1)], gfirst, a.K - 1));
             nseg = glast - gfirst + 1;
             if (tid < nseg) {
                 int ob, kend, kfull;
-                segment_range(a.perm + bn, offb, a.n, a.w, s0, s1, gfirst + tid, ob, kend, kfull);
+                segment_range(a.perm + bne, offb, ne, MULTI ? 2 : 1, a.w, s0, s1, gfirst + tid,
+                              ob, kend, kfull);
                 seg_ob[tid] = ob;
                 seg_kend[tid] = kend;
                 seg_kfull[tid] = ob;
@@ -382,6 +407,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             while (t + 1 < nseg && seg_ob[t + 1] <= s_row) ++t;
             g_i = gfirst + t;
         }
+        if (MULTI) {
+            // A pair of tokens sharing both their groups meets in both
+            // segments; it is kept only in the segment of the lower group.
+            // Row i in segment g skips keys whose other group equals its own
+            // other group when that group is below g.
+            x_i = (rvalid && oth_i < g_i) ? oth_i : -1;
+            if (x_i >= 0) excl_any = 1;
+            __syncthreads();
+            rows_excl = __builtin_amdgcn_readfirstlane(excl_any) != 0;
+        }
     }
 
     // Tile tau -> (segment, first key slot, end of valid slots, all pairs kept).
@@ -399,7 +434,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             kt0 = __builtin_amdgcn_readfirstlane(seg_ob[seg]) +
                   (tau - __builtin_amdgcn_readfirstlane(seg_t0[seg])) * BN;
             kend = __builtin_amdgcn_readfirstlane(seg_kend[seg]);
-            full = rows_one_group && (kt0 + BN <= __builtin_amdgcn_readfirstlane(seg_kfull[seg]));
+            full = rows_one_group && !rows_excl &&
+                   (kt0 + BN <= __builtin_amdgcn_readfirstlane(seg_kfull[seg]));
         }
     };
 
@@ -422,7 +458,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         bool full;
         locate(tau, seg_issue, kt0, kend, full);
         unsigned char* dst = bufp + wave_s * G::NI * 1024;
-        if (kt0 + BN <= a.n) {
+        if (kt0 + BN <= ne) {
             // the whole tile lies inside the sequence: a scalar tile base plus
             // fixed per-lane offsets (rows past kend are read but masked)
             const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)kt0 * D);
@@ -443,7 +479,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         }
         // positions of the tile's key slots, for the mask of a partial tile
         if (SORTED && !full && wave == 0)
-            copy16(a.spos + (int64_t)b * (a.n + KPOS_PAD) + kt0 + 4 * lane, kposp);
+            copy16(a.spos + (int64_t)b * (ne + KPOS_PAD) + kt0 + 4 * lane, kposp);
     };
 
     // LDS offsets of this lane's operand reads (tile-relative).
@@ -517,8 +553,11 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                         bool ok;
                         if (!SORTED) {
                             ok = (key < kend) & (key <= pos_i) & (pos_i - key <= a.w);
-                        } else {
+                        } else if (!MULTI) {
                             ok = row_ok & (key < kend) & (pos_i - kp[j] > a.w);
+                        } else {   // kp = position * 64 + the key token's other group
+                            ok = row_ok & (key < kend) & (pos_i - (kp[j] >> 6) > a.w) &
+                                 ((kp[j] & 63) != x_i);
                         }
                         st[kb][4 * e4 + j] = ok ? st[kb][4 * e4 + j] : kNegInf;
                     }
@@ -633,7 +672,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             l_run = (hh == 0) ? __builtin_ldexpf(1.0f, -(int)le[1]) : 0.0f;
         }
     }
-    auto row_of = [&](int r, int& hr, int& pr) {   // query row r -> (head, position)
+    // query row r -> (head, entry); the entry is the position except in
+    // the multi pass (position = entry / 2)
+    auto row_of = [&](int r, int& hr, int& pr) {
         hr = kvh * a.hpk + slice * a.G + r / a.TT;
         if (SORTED) {
             pr = rowpos[r];
@@ -651,7 +692,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             int hr, pr;
             row_of(r, hr, pr);
             const int ch = logical_chunk<D>(r, (o % G::ROWB) / 16);
-            copy16(a.q + (((int64_t)b * a.Hq + hr) * a.n + pr) * D + ch * 8,
+            copy16(a.q + (((int64_t)b * a.Hq + hr) * a.n + (MULTI ? pr >> 1 : pr)) * D + ch * 8,
                    buf1 + (wave * 2 * G::NI + c) * 1024);
         }
         wait_vm();
@@ -689,7 +730,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // written to LDS (chunk slots XOR-swizzled by row) and stored as whole
     // contiguous rows.
     const float l_tot = l_run + other_half(l_run);
-    const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
+    const int64_t row = ((int64_t)b * a.Hq + h) * ne + ent_i;   // output row
     float scale_o = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     int esize;
     if (a.partial) {
@@ -750,15 +791,76 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         for (int idx = tid; idx < rpp * nchk; idx += NT) {
             const int rs = idx / nchk, c = idx % nchk;
             const int r = r0 + rs;
-            if (tile * a.TT + r % a.TT >= a.n) continue;   // rows past the sequence end
+            if (tile * a.TT + r % a.TT >= ne) continue;   // rows past the sequence end
             int hr, pr;
             row_of(r, hr, pr);
             u32x4 val = *reinterpret_cast<const u32x4*>(smem + rs * RB + ((c ^ (rs & cmask)) << 4));
             if (esize == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
-            *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * a.n + pr) * RB) + c * 16) =
+            *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * ne + pr) * RB) + c * 16) =
                 val;
         }
     }
+}
+
+// Final merge of the multi pass: per row (b, h, i), the window partial and
+// the row's m entry partials (each O~ = O * 2^-e in fp16 with (L, e), L the
+// log2-sum-exp of its keys, -inf for none) are combined by log-sum-exp:
+// out = sum_c 2^(L_c - L) O_c, L = log2 sum_c 2^(L_c). The parts cover
+// disjoint key sets whose union is the row's pattern, so this is exact.
+// D/8 threads per row, one 8-element chunk each.
+template <int D, int MM>
+__global__ __launch_bounds__(256) void attn_merge_entries_kernel(
+    const _Float16* __restrict__ og, const f32x2* __restrict__ lseg,
+    const _Float16* __restrict__ oge, const f32x2* __restrict__ lsege, int64_t rows, int n,
+    void* __restrict__ out, int out_f32, float* __restrict__ lse) {
+    constexpr int TPR = D / 8;
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = x / TPR;
+    const int c = (int)(x % TPR);
+    if (row >= rows) return;
+    const int64_t bh = row / n;
+    const int pos = (int)(row % n);
+    f32x2 le[MM + 1];
+    const _Float16* src[MM + 1];
+    le[0] = lseg[row];
+    src[0] = og + row * D + c * 8;
+#pragma unroll
+    for (int e = 0; e < MM; ++e) {
+        const int64_t er = (bh * n + pos) * MM + e;   // entry row: [b][h][t * MM + e]
+        le[e + 1] = lsege[er];
+        src[e + 1] = oge + er * D + c * 8;
+    }
+    float lmax = kNegInf;
+#pragma unroll
+    for (int p = 0; p <= MM; ++p) lmax = fmaxf(lmax, le[p][0]);
+    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float tot = 0.0f;
+    if (lmax != kNegInf) {
+#pragma unroll
+        for (int p = 0; p <= MM; ++p) {
+            if (le[p][0] == kNegInf) continue;
+            const float wgt = __builtin_amdgcn_exp2f(le[p][0] - lmax);
+            tot += wgt;
+            const float f = __builtin_ldexpf(wgt, (int)le[p][1]);
+            const f16x8 hv = *reinterpret_cast<const f16x8*>(src[p]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(f, (float)hv[j], o[j]);
+        }
+    }
+    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
+    if (out_f32) {
+        float* dst = static_cast<float*>(out) + row * D + c * 8;
+        const f32x4 a0 = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+        const f32x4 a1 = {o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+        *reinterpret_cast<f32x4*>(dst) = a0;
+        *reinterpret_cast<f32x4*>(dst + 4) = a1;
+    } else {
+        bf16x8 ob;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ob[j] = (__bf16)(o[j] * inv);
+        *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(out) + row * D + c * 8) = ob;
+    }
+    if (c == 0 && lse) lse[row] = tot > 0.0f ? (lmax + __log2f(tot)) * kLn2 : kNegInf;
 }
 
 AttnArgs make_args(const AttnProblem& p) {
@@ -781,12 +883,13 @@ AttnArgs make_args(const AttnProblem& p) {
     a.G = attn_heads_per_wg(a.hpk);
     a.TT = ROWS / a.G;
     a.nslices = a.hpk / a.G;
+    a.ne = p.n;
     a.ntiles = (p.n + a.TT - 1) / a.TT;
     a.total = p.B * p.Hkv * a.nslices * a.ntiles;
     a.sl2 = p.scale * 1.44269504088896340736f;
     a.out_f32 = p.out_f32;
     if (p.workspace) {
-        const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d);
+        const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
         char* base = static_cast<char*>(p.workspace);
         a.og = reinterpret_cast<_Float16*>(base + ws.og);
         a.lseg = reinterpret_cast<f32x2*>(base + ws.lseg);
@@ -821,27 +924,65 @@ int attn_heads_per_wg(int hpk) {
 
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
+    if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
     AttnArgs a = make_args(p);
-    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d);
+    // the sorted order lists n*m entries
+    a.ne = p.n * p.m;
+    a.ntiles = (a.ne + a.TT - 1) / a.TT;
+    a.total = p.B * p.Hkv * a.nslices * a.ntiles;
+    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
     char* base = static_cast<char*>(p.workspace);
     uint16_t* ks = reinterpret_cast<uint16_t*>(base + ws.ks);
     uint16_t* vs = reinterpret_cast<uint16_t*>(base + ws.vs);
-    const int64_t chunks = (int64_t)(p.n + KPOS_PAD) * (p.d / 8);
+    const int64_t chunks = (int64_t)(a.ne + KPOS_PAD) * (p.d / 8);
     hipLaunchKernelGGL(attn_gather_kernel, dim3((unsigned)((chunks + 255) / 256), p.B * p.Hkv),
-                       dim3(256), 0, stream, p.k, p.v, p.perm, p.n, p.Hkv, p.d, ks, vs, a.spos);
+                       dim3(256), 0, stream, p.k, p.v, p.perm, p.ids, p.n, a.ne, p.m, p.K,
+                       p.Hkv, p.d, ks, vs, a.spos);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
-                       p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT, a.ntiles,
+                       p.ids, p.perm, p.offsets, a.ne, p.m, p.K, p.w, a.TT, a.ntiles,
                        attn_tile_keys(p.d, kLongRange),
                        const_cast<int32_t*>(a.plan));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.k = ks;
     a.v = vs;
-    a.merge = 1;     // start from the window partial, write the final output
-    a.partial = 0;
-    return launch<kLongRange>(a, p.d, stream);
+    if (p.m == 1) {
+        a.merge = 1;     // start from the window partial, write the final output
+        a.partial = 0;
+        return launch<kLongRange>(a, p.d, stream);
+    }
+    // Two groups per token: one partial per entry, then the merge.
+    _Float16* oge = reinterpret_cast<_Float16*>(base + ws.oge);
+    f32x2* lsege = reinterpret_cast<f32x2*>(base + ws.lsege);
+    const _Float16* og = a.og;
+    const f32x2* lseg = a.lseg;
+    a.og = oge;
+    a.lseg = lsege;
+    a.merge = 0;
+    a.partial = 1;
+    e = launch<kLongMulti>(a, p.d, stream);
+    if (e != hipSuccess) return e;
+    const int64_t rows = (int64_t)p.B * p.Hq * p.n;
+    const int64_t threads = rows * (p.d / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    switch (p.d) {
+        case 32:
+            hipLaunchKernelGGL((attn_merge_entries_kernel<32, 2>), grid, dim3(256), 0, stream, og,
+                               lseg, oge, lsege, rows, p.n, p.out, p.out_f32, p.lse);
+            break;
+        case 64:
+            hipLaunchKernelGGL((attn_merge_entries_kernel<64, 2>), grid, dim3(256), 0, stream, og,
+                               lseg, oge, lsege, rows, p.n, p.out, p.out_f32, p.lse);
+            break;
+        case 128:
+            hipLaunchKernelGGL((attn_merge_entries_kernel<128, 2>), grid, dim3(256), 0, stream, og,
+                               lseg, oge, lsege, rows, p.n, p.out, p.out_f32, p.lse);
+            break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream) {

@@ -18,8 +18,10 @@ inline int assign_kpad(int K) { return K <= 32 ? 32 : 64; }
 inline size_t assign_workspace(int d_model, int K) {
     return 2 * align_up((size_t)assign_kpad(K) * assign_dpad(d_model) * 2);
 }
+// M = groups kept per token (1 or 2): ids [B][n][M], best first; margin =
+// (M-th score) - ((M+1)-th score).
 hipError_t launch_assign(const float* hidden, const float* P, const float* C, const float* bias,
-                         int B, int n, int d_model, int d_proj, int K, int32_t* ids,
+                         int B, int n, int d_model, int d_proj, int K, int M, int32_t* ids,
                          float* margin, void* workspace, hipStream_t stream);
 
 // ---- grouping ---------------------------------------------------------------
@@ -42,6 +44,7 @@ struct AttnProblem {
     int out_f32;
     float* lse;
     void* workspace;
+    int m = 1;     // groups per token: ids [B][n][m]; perm holds entries t*m + c
 };
 
 // True when some pair further apart than the window can exist (n - 1 > w).
@@ -57,27 +60,33 @@ inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_w
 // Attention workspace, byte offsets: the window partial output (fp16
 // [B][Hq][n][d], scaled per row), its log2-sum-exp and scale exponent (fp32
 // pairs [B][Hq][n]), the tile plan, group-sorted copies of K and V (bf16
-// [B][Hkv][n][d]) and the sorted positions (int32 [B][n + pad]).
+// [B][Hkv][n*m][d]) and the sorted positions (int32 [B][n*m + pad]). With m
+// groups per token (m > 1) the sorted order lists n*m membership entries,
+// and the long-range pass writes one partial per entry (fp16
+// [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge.
 struct AttnWorkspace {
-    size_t og, lseg, plan, ks, vs, spos, total;
+    size_t og, lseg, plan, ks, vs, spos, oge, lsege, total;
 };
-inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d) {
+inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m = 1) {
     AttnWorkspace w{};
     const int TT = attn_tokens_per_tile(Hq, Hkv);
-    const size_t ntiles = (size_t)(n + TT - 1) / TT;
+    const size_t ne = (size_t)n * m;
+    const size_t ntiles = (ne + TT - 1) / TT;
     size_t off = 0;
     w.og = off;   off += align_up((size_t)B * Hq * n * d * 2);
     w.lseg = off; off += align_up((size_t)B * Hq * n * 8);
     w.plan = off; off += align_up((size_t)B * ntiles * PLAN_INTS * 4);
-    w.ks = off;   off += align_up((size_t)B * Hkv * n * d * 2);
-    w.vs = off;   off += align_up((size_t)B * Hkv * n * d * 2);
-    w.spos = off; off += align_up((size_t)B * (n + KPOS_PAD) * 4);
+    w.ks = off;   off += align_up((size_t)B * Hkv * ne * d * 2);
+    w.vs = off;   off += align_up((size_t)B * Hkv * ne * d * 2);
+    w.spos = off; off += align_up((size_t)B * (ne + KPOS_PAD) * 4);
+    w.oge = off;  off += m > 1 ? align_up((size_t)B * Hq * ne * d * 2) : 0;
+    w.lsege = off; off += m > 1 ? align_up((size_t)B * Hq * ne * 8) : 0;
     w.total = off;
     return w;
 }
-inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w) {
+inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w, int m = 1) {
     if (!attn_has_long_range(n, w)) return 0;
-    return attn_workspace_layout(B, Hq, Hkv, n, d).total;
+    return attn_workspace_layout(B, Hq, Hkv, n, d, m).total;
 }
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream);

@@ -43,6 +43,12 @@ _SIGNATURES = {
     "focus_attn_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
                                  _i, _p, _p, _sz, _p], _i),
     "dense_causal_attn_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p], _i),
+    "focus_assign_topk": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
+    "focus_attn_topk_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i, _i], _sz),
+    "focus_attn_topk_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
+                             _p, _p, _sz, _p], _i),
+    "focus_attn_topk_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                          _f, _p, _i, _p, _p, _sz, _p], _i),
 }
 
 _lib = None
@@ -114,6 +120,19 @@ def focus_assign(hidden: torch.Tensor, P: torch.Tensor, C: torch.Tensor,
                  want_margin: bool = True, workspace=None, stream=None
                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Group id per token: argmax_k (h P) C_k^T + bias_k. hidden (B, n, d_model) fp32."""
+    return _assign(hidden, P, C, bias, 1, group_ids, margin, want_margin, workspace, stream)
+
+
+def focus_assign_topk(hidden: torch.Tensor, P: torch.Tensor, C: torch.Tensor, m: int,
+                      bias: Optional[torch.Tensor] = None, *, group_ids=None, margin=None,
+                      want_margin: bool = True, workspace=None, stream=None
+                      ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Top-m groups per token, best first: group_ids (B, n, m); margin = m-th
+    minus (m+1)-th score."""
+    return _assign(hidden, P, C, bias, m, group_ids, margin, want_margin, workspace, stream)
+
+
+def _assign(hidden, P, C, bias, m, group_ids, margin, want_margin, workspace, stream):
     B, n, d_model = hidden.shape
     d_proj = P.shape[1]
     K = C.shape[0]
@@ -123,18 +142,20 @@ def focus_assign(hidden: torch.Tensor, P: torch.Tensor, C: torch.Tensor,
     if bias is not None:
         _need(bias, "bias", torch.float32, (K,))
     dev = hidden.device
+    ids_shape = (B, n) if m == 1 else (B, n, m)
     if group_ids is None:
-        group_ids = torch.empty((B, n), dtype=torch.int32, device=dev)
-    _need(group_ids, "group_ids", torch.int32, (B, n))
+        group_ids = torch.empty(ids_shape, dtype=torch.int32, device=dev)
+    _need(group_ids, "group_ids", torch.int32, ids_shape)
     if margin is None and want_margin:
         margin = torch.empty((B, n), dtype=torch.float32, device=dev)
     if margin is not None:
         _need(margin, "margin", torch.float32, (B, n))
     nbytes = focus_assign_workspace_bytes(d_model, K)
     ws = _workspace(nbytes, dev, workspace)
-    _check_status(lib().focus_assign(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n, d_model,
-                                     d_proj, K, _ptr(group_ids), _ptr(margin), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(stream)))
+    _check_status(lib().focus_assign_topk(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n,
+                                          d_model, d_proj, K, int(m), _ptr(group_ids),
+                                          _ptr(margin), _ptr(ws),
+                                          0 if ws is None else ws.numel(), _stream(stream)))
     return group_ids, margin
 
 
@@ -144,9 +165,13 @@ def focus_group_sort_workspace_bytes(B: int, n: int, K: int) -> int:
 
 def focus_group_sort(group_ids: torch.Tensor, K: int, *, perm=None, group_offsets=None,
                      workspace=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Stable grouping: (perm (B, n) sorted slot -> position, group_offsets (B, K+1))."""
-    B, n = group_ids.shape
+    """Stable grouping: (perm (B, n) sorted slot -> position, group_offsets (B, K+1)).
+    Top-m ids (B, n, m) are sorted as their n*m membership entries t*m + c:
+    perm (B, n*m) then holds entries."""
     _need(group_ids, "group_ids", torch.int32)
+    if group_ids.dim() == 3:
+        group_ids = group_ids.view(group_ids.shape[0], -1)
+    B, n = group_ids.shape
     dev = group_ids.device
     if perm is None:
         perm = torch.empty((B, n), dtype=torch.int32, device=dev)
@@ -167,17 +192,23 @@ def focus_attn_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K
     return int(lib().focus_attn_workspace_bytes(B, Hq, Hkv, n, d_head, K, window))
 
 
+def focus_attn_topk_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K: int,
+                                    m: int, window: int) -> int:
+    return int(lib().focus_attn_topk_workspace_bytes(B, Hq, Hkv, n, d_head, K, m, window))
+
+
 def _attn_call(fn_name, q, k, v, group_ids, perm, group_offsets, K, window, scale, out,
-               out_dtype, lse, want_lse, workspace, stream, needs_groups=True):
+               out_dtype, lse, want_lse, workspace, stream, needs_groups=True, m=None):
     B, Hq, n, d = q.shape
     Hkv = k.shape[1]
     _need(q, "q", torch.bfloat16)
     _need(k, "k", torch.bfloat16, (B, Hkv, n, d))
     _need(v, "v", torch.bfloat16, (B, Hkv, n, d))
+    mm = 1 if m is None else m
     if needs_groups or group_ids is not None:
-        _need(group_ids, "group_ids", torch.int32, (B, n))
+        _need(group_ids, "group_ids", torch.int32, (B, n) if m is None else (B, n, m))
     if needs_groups or perm is not None:
-        _need(perm, "perm", torch.int32, (B, n))
+        _need(perm, "perm", torch.int32, (B, n * mm))
     if needs_groups or group_offsets is not None:
         _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
     if out is None:
@@ -189,12 +220,16 @@ def _attn_call(fn_name, q, k, v, group_ids, perm, group_offsets, K, window, scal
         lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, n))
-    nbytes = focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, window)
+    if m is None:
+        nbytes = focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, window)
+    else:
+        nbytes = focus_attn_topk_workspace_bytes(B, Hq, Hkv, n, d, K, m, window)
     ws = _workspace(nbytes, q.device, workspace)
     dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
     fn = getattr(lib(), fn_name)
+    shape_args = (B, Hq, Hkv, n, d, K) if m is None else (B, Hq, Hkv, n, d, K, int(m))
     _check_status(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(group_ids), _ptr(perm), _ptr(group_offsets),
-                     B, Hq, Hkv, n, d, K, window, float(scale), _ptr(out), dt, _ptr(lse),
+                     *shape_args, window, float(scale), _ptr(out), dt, _ptr(lse),
                      _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
     return out, lse, ws
 
@@ -228,6 +263,30 @@ def focus_attn_long_range_merge(q, k, v, group_ids, perm, group_offsets, K: int,
                       window, scale, out, out_dtype, lse, want_lse, workspace, stream)
 
 
+def focus_attn_topk_fwd(q, k, v, group_ids, perm, group_offsets, K: int, m: int, window: int,
+                        scale: float, *, out=None, out_dtype=torch.bfloat16, lse=None,
+                        want_lse: bool = False, workspace=None, stream=None):
+    """Focus attention with m groups per token: far pairs are kept when the
+    tokens share any group. group_ids (B, n, m); perm (B, n*m) of entries.
+    Returns (out, lse or None)."""
+    out, lse, _ = _attn_call("focus_attn_topk_fwd", q, k, v, group_ids, perm, group_offsets, K,
+                             window, scale, out, out_dtype, lse, want_lse, workspace, stream,
+                             m=m)
+    return out, lse
+
+
+def focus_attn_topk_long_range_merge(q, k, v, group_ids, perm, group_offsets, K: int, m: int,
+                                     window: int, scale: float, *, workspace, out=None,
+                                     out_dtype=torch.bfloat16, lse=None, want_lse: bool = False,
+                                     stream=None):
+    """Second pass of focus_attn_topk_fwd (after focus_attn_window with the
+    same workspace): shared-group pairs beyond the window, one partial per
+    membership entry, and the merge into out (and lse)."""
+    return _attn_call("focus_attn_topk_long_range_merge", q, k, v, group_ids, perm,
+                      group_offsets, K, window, scale, out, out_dtype, lse, want_lse, workspace,
+                      stream, m=m)
+
+
 def dense_causal_attn_fwd(q, k, v, scale: float, *, out=None, out_dtype=torch.bfloat16,
                           lse=None, want_lse: bool = False, stream=None):
     """Plain causal attention baseline. Returns (out, lse or None)."""
@@ -250,12 +309,19 @@ def dense_causal_attn_fwd(q, k, v, scale: float, *, out=None, out_dtype=torch.bf
     return out, lse
 
 
-def focus_forward(hidden, P, C, bias, q, k, v, window: int, scale: float, *,
+def focus_forward(hidden, P, C, bias, q, k, v, window: int, scale: float, *, m: int = 1,
                   out_dtype=torch.bfloat16, want_lse: bool = False, stream=None):
-    """The whole forward pass: assign -> group sort -> attention."""
+    """The whole forward pass: assign -> group sort -> attention (m groups
+    per token; m = 1 is the plain top-1 pattern)."""
     K = C.shape[0]
-    ids, _ = focus_assign(hidden, P, C, bias, want_margin=False, stream=stream)
-    perm, offs = focus_group_sort(ids, K, stream=stream)
-    out, lse = focus_attn_fwd(q, k, v, ids, perm, offs, K, window, scale, out_dtype=out_dtype,
-                              want_lse=want_lse, stream=stream)
+    if m == 1:
+        ids, _ = focus_assign(hidden, P, C, bias, want_margin=False, stream=stream)
+        perm, offs = focus_group_sort(ids, K, stream=stream)
+        out, lse = focus_attn_fwd(q, k, v, ids, perm, offs, K, window, scale,
+                                  out_dtype=out_dtype, want_lse=want_lse, stream=stream)
+    else:
+        ids, _ = focus_assign_topk(hidden, P, C, m, bias, want_margin=False, stream=stream)
+        perm, offs = focus_group_sort(ids, K, stream=stream)
+        out, lse = focus_attn_topk_fwd(q, k, v, ids, perm, offs, K, m, window, scale,
+                                       out_dtype=out_dtype, want_lse=want_lse, stream=stream)
     return out, lse, ids, perm, offs

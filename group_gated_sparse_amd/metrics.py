@@ -37,5 +37,44 @@ def pair_counts(ids: np.ndarray, w: int):
     return win, lr
 
 
+def long_range_pairs_multi(ids_tok: np.ndarray, w: int):
+    """Top-m membership, one sequence (ids_tok [n][m], distinct groups per
+    token): (kept far pairs, far pairs visited). A far pair is kept when the
+    tokens share a group; the long-range pass visits every far pair inside
+    each group's segment, so a pair sharing s groups is visited s times and
+    kept once. For m <= 2, kept = visited - (far pairs whose tokens have the
+    same two groups)."""
+    n, m = ids_tok.shape
+    if m > 2:
+        raise ValueError("m <= 2")
+    visited = 0
+    for g in np.unique(ids_tok):
+        seg = np.flatnonzero((ids_tok == g).any(axis=1))
+        visited += int(np.searchsorted(seg, seg - w, side="left").sum())
+    if m == 1:
+        return visited, visited
+    key = np.sort(ids_tok, axis=1).astype(np.int64)
+    code = key[:, 0] * 1024 + key[:, 1]
+    order = np.argsort(code, kind="stable")
+    c = code[order]
+    twice = 0
+    for seg in np.split(order, np.flatnonzero(np.diff(c)) + 1):
+        twice += int(np.searchsorted(seg, seg - w, side="left").sum())
+    return visited - twice, visited
+
+
+def pair_counts_multi(ids: np.ndarray, w: int):
+    """(window pairs, kept long-range pairs, visited long-range pairs) over
+    the batch, per query head; ids [B][n][m]."""
+    B, n, _ = ids.shape
+    win = B * window_pairs(n, w)
+    kept = visited = 0
+    for b in range(B):
+        k, v = long_range_pairs_multi(ids[b], w)
+        kept += k
+        visited += v
+    return win, kept, visited
+
+
 def attn_flops(pairs: int, Hq: int, d: int) -> float:
     return 4.0 * d * pairs * Hq

@@ -26,6 +26,7 @@ class Workload:
     d_proj: int       # width of the centroid space (projection output)
     K: int            # number of groups / centroids
     w: int            # local window: pairs with 0 <= i-j <= w are always kept
+    m: int = 1        # groups per token (top-m membership; far pairs sharing any group are kept)
     # how P and C are drawn: "gauss" = P ~ N(0, 1/d_model), C = row-normalised
     # N(0,1); "orthonormal" = P with orthonormal columns and C with orthonormal
     # rows, which makes the K centroid logits i.i.d. N(0,1) per token so that a
@@ -68,5 +69,13 @@ LONG1M = Workload("long_n1048576", B=1, Hq=8, Hkv=8, n=1 << 20, d=128, d_model=1
                   d_proj=128, K=64, w=1024, pc_kind="orthonormal",
                   q_prescale=1.0 / 128 ** 0.5, scale=1.0, seed=1005)
 
-ALL = [TINY, GPT2, ZIPF7B, LONG64K, GQA70B, LONG1M]
+# Top-2 membership at K = 4, the pages' top-k setting (Korean page §3.4,
+# Japanese page §3.3), on the 70B attention layer shape; and the same rule at
+# K = 32, where it is much sparser.
+TOP2_K4 = Workload("70b_gqa_top2_k4_n32768", B=1, Hq=64, Hkv=8, n=32768, d=128, d_model=8192,
+                   d_proj=128, K=4, w=1024, m=2, seed=1006)
+TOP2_K32 = Workload("70b_gqa_top2_k32_n32768", B=1, Hq=64, Hkv=8, n=32768, d=128,
+                    d_model=8192, d_proj=128, K=32, w=1024, m=2, seed=1007)
+
+ALL = [TINY, GPT2, ZIPF7B, LONG64K, GQA70B, LONG1M, TOP2_K4, TOP2_K32]
 BY_NAME = {w.name: w for w in ALL}

@@ -55,8 +55,9 @@ typedef enum {
 
 typedef enum { FOCUS_BF16 = 0, FOCUS_F32 = 1 } focus_dtype;
 
-#define FOCUS_ABI_VERSION 1
+#define FOCUS_ABI_VERSION 2
 #define FOCUS_MAX_GROUPS 64
+#define FOCUS_MAX_MEMBERSHIPS 2 /* groups per token (m) of the top-k variant */
 
 int focus_abi_version(void);
 const char* focus_last_error(void);
@@ -85,6 +86,22 @@ focus_status focus_assign(const float* hidden, const float* P, const float* C, c
                           void* workspace, size_t workspace_bytes, focus_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Top-k variant (Korean page §2.3 and §3.4, Japanese page §2.2 and §3.3: at
+ * inference a token may join its top-k groups; the pages' runs use k = 2
+ * with K = 4). Same scores; m = k groups per token:
+ *   group_ids[t][0..m-1] = the m highest-scoring groups, best first (exact
+ *                          ties -> lowest k)
+ *   margin[t]            = m-th score - (m+1)-th score (+inf when K == m)
+ * group_ids [B][n][m] int32 (out). Limits: 1 <= m <= FOCUS_MAX_MEMBERSHIPS,
+ * m <= K; otherwise as focus_assign, with the same workspace size.
+ * focus_assign_topk with m = 1 is focus_assign.
+ * ---------------------------------------------------------------------- */
+focus_status focus_assign_topk(const float* hidden, const float* P, const float* C,
+                               const float* bias, int B, int n, int d_model, int d_proj, int K,
+                               int m, int32_t* group_ids, float* margin,
+                               void* workspace, size_t workspace_bytes, focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Step 2: stable grouping of tokens (counting sort per batch element).
  *
  * group_offsets[b][k] = number of tokens of batch b whose id is < k (K+1
@@ -96,6 +113,10 @@ focus_status focus_assign(const float* hidden, const float* P, const float* C, c
  * perm [B][n] int32 (out), group_offsets [B][K+1] int32 (out)
  * workspace: per-block group counts, focus_group_sort_workspace_bytes() bytes
  * Limits: 1 <= K <= 64; 1 <= B <= 65535; n >= 1.
+ * Top-k variant: pass the [B][n][m] ids of focus_assign_topk with n*m in
+ * place of n. The sort then orders membership entries e = t*m + c (token t's
+ * c-th group): perm [B][n*m] holds entries, each group's segment lists its
+ * tokens once each in increasing position t = e / m.
  * ---------------------------------------------------------------------- */
 size_t focus_group_sort_workspace_bytes(int B, int n, int K);
 focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K,
@@ -161,6 +182,51 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
                                          int window, float scale, void* out,
                                          focus_dtype out_dtype, float* lse, void* workspace,
                                          size_t workspace_bytes, focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Step 3, top-k variant (Korean page §2.3 and §3.4; Japanese page §2.2 and
+ * §3.3): each token belongs to m groups (m = 2 in the pages' runs), and a far
+ * pair is kept when the two tokens share at least one group:
+ *
+ *   A_i = { j : 0 <= i - j <= window }  U  { j : j < i - window,
+ *           groups(i) and groups(j) intersect },  groups(t) = group_ids[b][t][*]
+ *
+ * with out and lse as for focus_attn_fwd. Each kept pair is counted once: a
+ * pair sharing two groups meets in both groups' segments and is kept in the
+ * segment of the lower group only. The long-range pass visits every group
+ * segment of both tokens, writes one partial result per membership entry,
+ * and a final kernel merges the window partial and the m entry partials by
+ * log-sum-exp.
+ *
+ * group_ids [B][n][m] (distinct groups per token, as from focus_assign_topk),
+ * perm [B][n*m] and group_offsets [B][K+1] from focus_group_sort over the
+ * n*m entries. Other arguments and layouts as focus_attn_fwd.
+ * Limits: 1 <= m <= FOCUS_MAX_MEMBERSHIPS, m <= K, n*m <= 2^24; otherwise as
+ *   focus_attn_fwd. With m = 1 the calls equal focus_attn_fwd and
+ *   focus_attn_long_range_merge.
+ *
+ * focus_attn_topk_fwd == focus_attn_window then
+ * focus_attn_topk_long_range_merge on one stream, with the workspace of
+ * focus_attn_topk_workspace_bytes() passed to both (the window pass uses its
+ * leading part, laid out as for m = 1).
+ * ---------------------------------------------------------------------- */
+size_t focus_attn_topk_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int m,
+                                       int window);
+focus_status focus_attn_topk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                 const int32_t* group_ids, const int32_t* perm,
+                                 const int32_t* group_offsets,
+                                 int B, int Hq, int Hkv, int n, int d_head, int K, int m,
+                                 int window, float scale, void* out, focus_dtype out_dtype,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 focus_stream_t stream);
+focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t* k,
+                                              const uint16_t* v, const int32_t* group_ids,
+                                              const int32_t* perm, const int32_t* group_offsets,
+                                              int B, int Hq, int Hkv, int n, int d_head, int K,
+                                              int m, int window, float scale, void* out,
+                                              focus_dtype out_dtype, float* lse,
+                                              void* workspace, size_t workspace_bytes,
+                                              focus_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Baseline: plain causal attention (every pair j <= i), the "full attention"

@@ -40,13 +40,13 @@ def test_header_is_plain_c():
 def test_library_exports_every_declared_symbol():
     lib = focus.lib()
     names = declared_functions()
-    assert len(names) >= 11
+    assert len(names) >= 15
     out = subprocess.check_output(["nm", "-D", "--defined-only", focus.LIB_PATH], text=True)
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     for name in names:
         assert name in exported, f"{name} is declared but not exported"
         assert getattr(lib, name) is not None
-    assert lib.focus_abi_version() == 1
+    assert lib.focus_abi_version() == 2
 
 
 def _err():
@@ -83,6 +83,30 @@ def test_assign_rejects(kw, code, msg):
     assert msg in _err()
 
 
+def _assign_topk(m, **kw):
+    args = dict(hidden=A, P=Bp, C=C_, bias=None, B=1, n=8, d_model=64, d_proj=16, K=4,
+                ids=D_, margin=None, ws=E_, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return focus.lib().focus_assign_topk(args["hidden"], args["P"], args["C"], args["bias"],
+                                         args["B"], args["n"], args["d_model"], args["d_proj"],
+                                         args["K"], m, args["ids"], args["margin"], args["ws"],
+                                         args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("m,kw,code,msg", [
+    (0, {}, UNSUPPORTED, "m must be"),
+    (3, dict(K=8), UNSUPPORTED, "m must be"),
+    (2, dict(K=1), INVALID, "must be <= K"),
+    (2, dict(hidden=None), INVALID, "hidden"),
+    (2, dict(wsb=16), WORKSPACE, "too small"),
+    # ids [B][n][2] = 64 bytes from D_ - 48 reach into hidden at D_
+    (2, dict(hidden=D_, ids=D_ - 48), INVALID, "overlap"),
+])
+def test_assign_topk_rejects(m, kw, code, msg):
+    assert _assign_topk(m, **kw) == code
+    assert msg in _err()
+
+
 def test_workspace_sizes():
     lib = focus.lib()
     # two bf16 tables of [32 or 64][d_model rounded up to 64], each 256-byte aligned
@@ -100,6 +124,16 @@ def test_workspace_sizes():
     # no pair can be further apart than the window: no partial needed
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
+    # top-k, m = 1: the same layout
+    assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 1, 32) == \
+        lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32)
+    # m = 2: plan over 512 entries (8 tiles), sorted K, V and positions over 512 entries, then
+    # per-entry fp16 partials [B][Hq][512][d] and their pairs [B][Hq][512]
+    assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 2, 32) == (
+        256 * 2 * 32 * 2 + 4096 + 8 * 128 + 2 * (512 * 32 * 2) + 768 * 4
+        + 512 * 2 * 32 * 2 + 512 * 2 * 8)
+    assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 3, 32) == 0
+    assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 2, 255) == 0
 
 
 def _sort(**kw):
@@ -171,6 +205,40 @@ def test_attn_rejects(fn, kw, code, msg):
                                     (dict(offs=None), "group_offsets")])
 def test_attn_passes_needing_groups_reject_missing_group_data(fn, kw, msg):
     assert _attn(fn, **kw) == INVALID
+    assert msg in _err()
+
+
+def _attn_topk(fn="focus_attn_topk_fwd", m=2, **kw):
+    args = dict(q=A, k=Bp, v=C_, ids=D_, perm=E_, offs=F_, B=1, Hq=4, Hkv=2, n=256, d=64, K=4,
+                w=16, scale=0.125, out=G_, dt=0, lse=None, ws=H_, wsb=1 << 30, stream=None)
+    args.update(kw)
+    f = getattr(focus.lib(), fn)
+    return f(args["q"], args["k"], args["v"], args["ids"], args["perm"], args["offs"], args["B"],
+             args["Hq"], args["Hkv"], args["n"], args["d"], args["K"], m, args["w"],
+             args["scale"], args["out"], args["dt"], args["lse"], args["ws"], args["wsb"],
+             args["stream"])
+
+
+@pytest.mark.parametrize("fn", ["focus_attn_topk_fwd", "focus_attn_topk_long_range_merge"])
+@pytest.mark.parametrize("m,kw,code,msg", [
+    (0, {}, UNSUPPORTED, "m must be"),
+    (3, dict(K=8), UNSUPPORTED, "m must be"),
+    (2, dict(K=1), INVALID, "must be <= K"),
+    (2, dict(n=(1 << 23) + 1), UNSUPPORTED, "n * m"),
+    (2, dict(ids=None), INVALID, "group_ids"),
+    (2, dict(perm=None), INVALID, "perm"),
+    (2, dict(d=48), UNSUPPORTED, "d_head"),
+    (2, dict(scale=0.0), INVALID, "scale"),
+    (2, dict(ws=None), WORKSPACE, "workspace"),
+    # enough for m = 1 but not for the per-entry partials of m = 2
+    (2, dict(wsb=400000), WORKSPACE, "too small"),
+])
+def test_attn_topk_rejects(fn, m, kw, code, msg):
+    if kw.get("wsb") == 400000:
+        need1 = focus.lib().focus_attn_workspace_bytes(1, 4, 2, 256, 64, 4, 16)
+        need2 = focus.lib().focus_attn_topk_workspace_bytes(1, 4, 2, 256, 64, 4, 2, 16)
+        assert need1 <= 400000 < need2
+    assert _attn_topk(fn, m, **kw) == code
     assert msg in _err()
 
 
