@@ -66,6 +66,11 @@ def configure(lib):
     lib.oracle_attn_multi.restype = ctypes.c_int
     lib.oracle_pair_count_multi.argtypes = [_p, _i64, _i64, _i64, _i64, ctypes.c_int]
     lib.oracle_pair_count_multi.restype = _i64
+    lib.oracle_assign_scores.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _p,
+                                         ctypes.c_int]
+    lib.oracle_assign_scores.restype = ctypes.c_int
+    lib.oracle_sinkhorn.argtypes = [_p, _i64, _i64, _i64, ctypes.c_double, _i64, _p]
+    lib.oracle_sinkhorn.restype = ctypes.c_int
     return lib
 
 
@@ -309,3 +314,37 @@ def pair_count_multi(ids, w: int, nthreads: int = 0) -> int:
     if r < 0:
         raise ValueError("oracle_pair_count_multi rejected its arguments")
     return int(r)
+
+
+# ---- soft assignment with Sinkhorn normalisation (training-time step) -------
+# Korean page §2.2 and Japanese page §2.1 / §2.3: the token-to-group
+# assignment matrix is made doubly stochastic (rows sum to 1, every group gets
+# the same total n / K).
+
+def assign_scores(hidden, P, C, bias=None, nthreads: int = 0):
+    """Raw fp32 scores (h P) C^T + bias, (B, n, K), summed as in assign()."""
+    hidden = _c(hidden, np.float32)
+    P = _c(P, np.float32)
+    C = _c(C, np.float32)
+    bias = _c(bias, np.float32)
+    B, n, d_model = hidden.shape
+    d_proj = P.shape[1]
+    K = C.shape[0]
+    assert P.shape == (d_model, d_proj) and C.shape == (K, d_proj)
+    S = np.empty((B, n, K), dtype=np.float32)
+    rc = _load().oracle_assign_scores(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n, d_model,
+                                      d_proj, K, _ptr(S), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_assign_scores rejected its arguments")
+    return S
+
+
+def sinkhorn(scores, tau: float, iters: int):
+    """Sinkhorn-Knopp soft assignment G (B, n, K) fp64 of A = exp(scores/tau):
+    rows first, then `iters` rounds of (columns to n/K, rows to 1)."""
+    scores = _c(scores, np.float32)
+    B, n, K = scores.shape
+    G = np.empty((B, n, K), dtype=np.float64)
+    if _load().oracle_sinkhorn(_ptr(scores), B, n, K, float(tau), int(iters), _ptr(G)) != 0:
+        raise ValueError("oracle_sinkhorn rejected its arguments")
+    return G

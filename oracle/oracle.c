@@ -23,6 +23,11 @@
  *   ties go to the lowest group index; the window is the causal band
  *   0 <= i-j <= w; long-range pairs are causal (j <= i); an allowed pair is
  *   counted once; the softmax is renormalised over the allowed set.
+ *   Sinkhorn (training-time soft assignment): Sinkhorn-Knopp on exp(scores /
+ *   tau), rows first, then a caller-given number of (column, row) rounds;
+ *   every column's target is n / K (only its being equal matters: the final
+ *   row step cancels a common factor); tau and the number of rounds are not
+ *   given by the pages and are arguments.
  *   Multi-membership (top-m groups per token, m = 2 in the pages' runs): a far
  *   pair is kept when the tokens share at least one group, and still counted
  *   once; the top-m groups are the m highest scores, ties to the lowest index.
@@ -490,4 +495,78 @@ int64_t oracle_pair_count_multi(const int32_t* ids, int64_t m, int64_t B, int64_
         }
     }
     return total;
+}
+
+/* ------------------------------------------------------------------------
+ * Soft assignment with Sinkhorn normalisation (training-time step; Korean
+ * page §2.2 and Japanese page §2.1 / §2.3): the n x K assignment matrix of
+ * one sequence is made doubly stochastic, i.e. every token's row sums to 1
+ * and every group's column sums to the same total n / K.
+ * ---------------------------------------------------------------------- */
+
+/* Raw scores s[t][k] = (h_t . P) . C_k + bias_k, fp32, as in oracle_assign. */
+int oracle_assign_scores(const float* hidden, const float* P, const float* C, const float* bias,
+                         int64_t B, int64_t n, int64_t d_model, int64_t d_proj, int64_t K,
+                         float* scores, int nthreads) {
+    if (!hidden || !P || !C || !scores || B < 1 || n < 1 || d_model < 1 || d_proj < 1 || K < 1)
+        return -1;
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        float* z = (float*)malloc(sizeof(float) * (size_t)d_proj);
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < B * n; ++t)
+            token_scores(hidden + t * d_model, P, C, bias, d_model, d_proj, K, z, scores + t * K);
+        free(z);
+    }
+    return 0;
+}
+
+/*
+ * Sinkhorn-Knopp on A = exp(scores / tau) for each batch element, fp64, in
+ * the plain scaling-vector form G[t][k] = A[t][k] * u[t] * v[k]:
+ *   u = 1 / (row sums of A)                                 (rows first)
+ *   repeat iters times:
+ *     v[k] = (n / K) / sum_t A[t][k] u[t]                     (columns)
+ *     u[t] = 1 / sum_k A[t][k] v[k]                           (rows)
+ * so every row of G sums to 1 and, as iters grows, every column to n / K.
+ * v starts at 1. scores [B][n][K] fp32 -> G [B][n][K] fp64. The exponent is
+ * taken as written, so |scores / tau| must stay below ~700.
+ */
+int oracle_sinkhorn(const float* scores, int64_t B, int64_t n, int64_t K, double tau,
+                    int64_t iters, double* G) {
+    if (!scores || !G || B < 1 || n < 1 || K < 1 || !(tau > 0.0) || iters < 0) return -1;
+    double* A = (double*)malloc(sizeof(double) * (size_t)(n * K));
+    double* u = (double*)malloc(sizeof(double) * (size_t)n);
+    double* v = (double*)malloc(sizeof(double) * (size_t)K);
+    double* col = (double*)malloc(sizeof(double) * (size_t)K);
+    for (int64_t b = 0; b < B; ++b) {
+        const float* S = scores + b * n * K;
+        for (int64_t x = 0; x < n * K; ++x) A[x] = exp((double)S[x] / tau);
+        for (int64_t k = 0; k < K; ++k) v[k] = 1.0;
+        for (int64_t t = 0; t < n; ++t) {
+            double r = 0.0;
+            for (int64_t k = 0; k < K; ++k) r += A[t * K + k] * v[k];
+            u[t] = 1.0 / r;
+        }
+        for (int64_t it = 0; it < iters; ++it) {
+            for (int64_t k = 0; k < K; ++k) col[k] = 0.0;
+            for (int64_t t = 0; t < n; ++t)
+                for (int64_t k = 0; k < K; ++k) col[k] += A[t * K + k] * u[t];
+            for (int64_t k = 0; k < K; ++k) v[k] = ((double)n / (double)K) / col[k];
+            for (int64_t t = 0; t < n; ++t) {
+                double r = 0.0;
+                for (int64_t k = 0; k < K; ++k) r += A[t * K + k] * v[k];
+                u[t] = 1.0 / r;
+            }
+        }
+        double* Gb = G + b * n * K;
+        for (int64_t t = 0; t < n; ++t)
+            for (int64_t k = 0; k < K; ++k) Gb[t * K + k] = A[t * K + k] * u[t] * v[k];
+    }
+    free(A);
+    free(u);
+    free(v);
+    free(col);
+    return 0;
 }

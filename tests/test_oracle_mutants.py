@@ -17,6 +17,7 @@ import test_golden
 import test_oracle_assign_sort as tas
 import test_oracle_attn as tat
 import test_oracle_multi as tmu
+import test_oracle_sinkhorn as tsk
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -44,6 +45,16 @@ MUTANTS = {
                                      "if (i - j < w || share_group(g + i * m, g + j * m, m)) keys"),
     "multi pair count adds both tests": ("cnt += (i - j <= w) || share_group(",
                                          "cnt += (i - j <= w) + share_group("),
+    # (a uniform column target of any size is equivalent: the last row step
+    # cancels it; unequal targets are the mistake to catch)
+    "sinkhorn unequal column targets": ("v[k] = ((double)n / (double)K) / col[k];",
+                                        "v[k] = ((double)(n + k) / (double)K) / col[k];"),
+    "sinkhorn temperature dropped": ("A[x] = exp((double)S[x] / tau);", "A[x] = exp((double)S[x]);"),
+    "sinkhorn last column scale dropped": ("Gb[t * K + k] = A[t * K + k] * u[t] * v[k];",
+                                           "Gb[t * K + k] = A[t * K + k] * u[t];"),
+    "sinkhorn rows-first step skipped": ("u[t] = 1.0 / r;\n        }\n        for (int64_t it",
+                                         "u[t] = 1.0;\n        }\n        for (int64_t it"),
+    "sinkhorn column sum misses u": ("col[k] += A[t * K + k] * u[t];", "col[k] += A[t * K + k];"),
 }
 
 PINS = [
@@ -66,6 +77,12 @@ PINS = [
     lambda: tmu.test_all_groups_is_dense_causal(5),
     lambda: tmu.test_brute_force_set_enumeration(*tmu.CASES[2]),
     lambda: tmu.test_pair_count_inclusion_exclusion(300, 11, 4),
+    tsk.test_zero_iterations_is_row_softmax,
+    tsk.test_additive_scores_give_uniform_assignment,
+    tsk.test_two_by_two_limit_closed_form,
+    tsk.test_cross_ratios_are_those_of_exp_scores,
+    tsk.test_marginals_rows_exact_columns_converge,
+    tsk.test_row_shift_and_column_permutation,
 ]
 
 
