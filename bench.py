@@ -53,6 +53,11 @@ def parse():
                     help="target CPU time of the oracle attention sample")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the window pass on the main stream, after the sort")
+    ap.add_argument("--op", default="attn", choices=["attn", "sinkhorn"],
+                    help="attn: the inference forward step (default); sinkhorn: the "
+                         "training-time soft assignment (scores + Sinkhorn rounds)")
+    ap.add_argument("--iters", type=int, default=10, help="Sinkhorn rounds (--op sinkhorn)")
+    ap.add_argument("--tau", type=float, default=1.0, help="Sinkhorn temperature (--op sinkhorn)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch for calibrating HBM byte counters)")
@@ -142,6 +147,91 @@ def cpu_baseline(x, wl, target_s):
     }
 
 
+def bench_sinkhorn(args, wl):
+    """Soft assignment step: focus_assign_scores then focus_sinkhorn (iters
+    rounds), timed with HIP events per call; one JSON line."""
+    import torch
+    from group_gated_sparse_amd import focus, metrics, synth
+    log(f"workload {wl.name}: generating hidden states")
+    x = synth.make_inputs(wl, with_qkv=False)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    hidden, P, C = dev(x["hidden"]), dev(x["P"]), dev(x["C"])
+    bias = None if x["bias"] is None else dev(x["bias"])
+    B, n, K, T = wl.B, wl.n, wl.K, args.iters
+    S = torch.empty((B, n, K), dtype=torch.float32, device="cuda")
+    G = torch.empty_like(S)
+    ws_a = torch.empty(focus.focus_assign_workspace_bytes(wl.d_model, K), dtype=torch.uint8,
+                       device="cuda")
+    ws_s = torch.empty(focus.focus_sinkhorn_workspace_bytes(B, n, K, T), dtype=torch.uint8,
+                       device="cuda")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        focus.focus_assign_scores(hidden, P, C, bias, scores=S, workspace=ws_a)
+        if ev is not None:
+            ev[1].record()
+        focus.focus_sinkhorn(S, args.tau, T, G=G, workspace=ws_s)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    sc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms = max(wall_ms, sc_ms + sk_ms)
+    log(f"step {ms:.4f} ms: scores {sc_ms:.4f} ms, sinkhorn {sk_ms:.4f} ms ({T} rounds)")
+    # algorithmic bytes of one Sinkhorn call: every pass reads the scores once,
+    # the last also writes G
+    sk_bytes = (T + 1) * B * n * K * 4 + B * n * K * 4
+    res = {
+        "metric": "Sinkhorn soft assignment (scores + rounds), tokens/s, 1 GPU",
+        "value": B * n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "op": "sinkhorn", "B": B, "n": n, "K": K,
+                   "d_model": wl.d_model, "d_proj": wl.d_proj, "iters": T, "tau": args.tau},
+        "phase_ms": {"scores": sc_ms, "sinkhorn": sk_ms},
+        "roofline": {"kernel": "assign_argmax_kernel (scores)", "bound": "hbm",
+                     "achieved": B * n * wl.d_model * 4 / (sc_ms * 1e-3) / 1e9,
+                     "peak": metrics.MI355X_HBM_GBPS, "unit": "GB/s",
+                     "frac": B * n * wl.d_model * 4 / (sc_ms * 1e-3) / 1e9 / metrics.MI355X_HBM_GBPS,
+                     "traffic": None},
+        "sinkhorn_roofline": {"kernel": "sinkhorn_pass_kernel x (iters + 1)", "bound": "hbm",
+                              "achieved": sk_bytes / (sk_ms * 1e-3) / 1e9,
+                              "peak": metrics.MI355X_HBM_GBPS, "unit": "GB/s",
+                              "frac": sk_bytes / (sk_ms * 1e-3) / 1e9 / metrics.MI355X_HBM_GBPS,
+                              "bytes_per_call": sk_bytes},
+    }
+    if not args.skip_cpu_baseline:
+        import oracle
+        t0 = time.perf_counter()
+        rows = min(n, 4096)
+        Sh = S.cpu().numpy()[:, :rows]
+        oracle.sinkhorn(Sh, args.tau, T)
+        t_s = (time.perf_counter() - t0) * n / rows
+        t0 = time.perf_counter()
+        oracle.assign_scores(x["hidden"][:, :rows], x["P"], x["C"], x["bias"])
+        t_a = (time.perf_counter() - t0) * n / rows
+        res["cpu_baseline"] = {"value": B * n / (t_s + t_a), "unit": "tokens/s",
+                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"oracle scores and Sinkhorn ({T} rounds) on the first "
+                                         f"{rows} tokens of each sequence, scaled by n / {rows}"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -157,6 +247,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     wl = workloads.BY_NAME[args.workload]
+    if args.op == "sinkhorn":
+        return bench_sinkhorn(args, wl)
     log(f"workload {wl.name}: generating seeded inputs")
     t0 = time.perf_counter()
     x = synth.make_inputs(wl)

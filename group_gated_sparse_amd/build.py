@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libfocus.so")
-SOURCES = ["api.cpp", "assign.hip", "sort.hip", "attn.hip"]
+SOURCES = ["api.cpp", "assign.hip", "sort.hip", "attn.hip", "sinkhorn.hip"]
 
 ARCH = "gfx950"
 FLAGS = [

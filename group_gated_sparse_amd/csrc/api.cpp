@@ -162,9 +162,10 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     return ok();
 }
 
+// m >= 1: top-m ids (and margin); m == 0: the raw scores [B][n][K].
 focus_status assign_entry(const float* hidden, const float* P, const float* C, const float* bias,
                           int B, int n, int d_model, int d_proj, int K, int m,
-                          int32_t* group_ids, float* margin, void* workspace,
+                          int32_t* group_ids, float* margin, float* scores, void* workspace,
                           size_t workspace_bytes, focus_stream_t stream) {
     REQUIRE(B >= 1 && n >= 1, FOCUS_ERR_INVALID_ARGUMENT, "B and n must be >= 1 (got B=%d n=%d)",
             B, n);
@@ -174,15 +175,22 @@ focus_status assign_entry(const float* hidden, const float* P, const float* C, c
             d_model);
     REQUIRE(K >= 1 && K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)",
             FOCUS_MAX_GROUPS, K);
-    REQUIRE(m >= 1 && m <= FOCUS_MAX_MEMBERSHIPS, FOCUS_ERR_UNSUPPORTED,
-            "m must be in [1, %d] (got %d)", FOCUS_MAX_MEMBERSHIPS, m);
-    REQUIRE(m <= K, FOCUS_ERR_INVALID_ARGUMENT, "m (%d) must be <= K (%d)", m, K);
+    if (m != 0) {
+        REQUIRE(m >= 1 && m <= FOCUS_MAX_MEMBERSHIPS, FOCUS_ERR_UNSUPPORTED,
+                "m must be in [1, %d] (got %d)", FOCUS_MAX_MEMBERSHIPS, m);
+        REQUIRE(m <= K, FOCUS_ERR_INVALID_ARGUMENT, "m (%d) must be <= K (%d)", m, K);
+    }
     REQUIRE_PTR(hidden, 16);
     REQUIRE_PTR(P, 4);
     REQUIRE_PTR(C, 4);
     if (bias) REQUIRE(aligned(bias, 4), FOCUS_ERR_INVALID_ARGUMENT, "bias must be 4-byte aligned");
-    REQUIRE_PTR(group_ids, 4);
-    if (margin) REQUIRE(aligned(margin, 4), FOCUS_ERR_INVALID_ARGUMENT, "margin must be 4-byte aligned");
+    if (m != 0) {
+        REQUIRE_PTR(group_ids, 4);
+        if (margin)
+            REQUIRE(aligned(margin, 4), FOCUS_ERR_INVALID_ARGUMENT, "margin must be 4-byte aligned");
+    } else {
+        REQUIRE_PTR(scores, 4);
+    }
     const int64_t ntok = (int64_t)B * n;
     REQUIRE((ntok + 31) / 32 <= kMaxGrid, FOCUS_ERR_UNSUPPORTED, "too many tokens for one launch");
     const size_t need = focus::assign_workspace(d_model, K);
@@ -191,10 +199,14 @@ focus_status assign_entry(const float* hidden, const float* P, const float* C, c
     REQUIRE(workspace_bytes >= need, FOCUS_ERR_WORKSPACE,
             "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
     const size_t hbytes = (size_t)ntok * d_model * 4;
-    REQUIRE(!overlaps(group_ids, (size_t)ntok * m * 4, hidden, hbytes),
-            FOCUS_ERR_INVALID_ARGUMENT, "group_ids must not overlap hidden");
+    if (m != 0)
+        REQUIRE(!overlaps(group_ids, (size_t)ntok * m * 4, hidden, hbytes),
+                FOCUS_ERR_INVALID_ARGUMENT, "group_ids must not overlap hidden");
+    else
+        REQUIRE(!overlaps(scores, (size_t)ntok * K * 4, hidden, hbytes),
+                FOCUS_ERR_INVALID_ARGUMENT, "scores must not overlap hidden");
     return device_status(focus::launch_assign(hidden, P, C, bias, B, n, d_model, d_proj, K, m,
-                                              group_ids, margin, workspace,
+                                              group_ids, margin, scores, workspace,
                                               static_cast<hipStream_t>(stream)),
                          "assign launch");
 }
@@ -217,15 +229,61 @@ focus_status focus_assign(const float* hidden, const float* P, const float* C, c
                           float* margin, void* workspace, size_t workspace_bytes,
                           focus_stream_t stream) {
     return assign_entry(hidden, P, C, bias, B, n, d_model, d_proj, K, 1, group_ids, margin,
-                        workspace, workspace_bytes, stream);
+                        nullptr, workspace, workspace_bytes, stream);
 }
 
 focus_status focus_assign_topk(const float* hidden, const float* P, const float* C,
                                const float* bias, int B, int n, int d_model, int d_proj, int K,
                                int m, int32_t* group_ids, float* margin, void* workspace,
                                size_t workspace_bytes, focus_stream_t stream) {
+    if (m == 0) return fail(FOCUS_ERR_UNSUPPORTED, "m must be in [1, %d] (got 0)",
+                            FOCUS_MAX_MEMBERSHIPS);
     return assign_entry(hidden, P, C, bias, B, n, d_model, d_proj, K, m, group_ids, margin,
-                        workspace, workspace_bytes, stream);
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+focus_status focus_assign_scores(const float* hidden, const float* P, const float* C,
+                                 const float* bias, int B, int n, int d_model, int d_proj, int K,
+                                 float* scores, void* workspace, size_t workspace_bytes,
+                                 focus_stream_t stream) {
+    return assign_entry(hidden, P, C, bias, B, n, d_model, d_proj, K, 0, nullptr, nullptr,
+                        scores, workspace, workspace_bytes, stream);
+}
+
+size_t focus_sinkhorn_workspace_bytes(int B, int n, int K, int iters) {
+    if (B < 1 || n < 1 || K < 1 || K > FOCUS_MAX_GROUPS || iters < 0) return 0;
+    return focus::sinkhorn_layout(B, n, K, iters).total;
+}
+
+focus_status focus_sinkhorn(const float* scores, int B, int n, int K, float tau, int iters,
+                            float* G, void* workspace, size_t workspace_bytes,
+                            focus_stream_t stream) {
+    REQUIRE(B >= 1 && n >= 1, FOCUS_ERR_INVALID_ARGUMENT, "B and n must be >= 1 (got B=%d n=%d)",
+            B, n);
+    REQUIRE(B <= 65535, FOCUS_ERR_UNSUPPORTED, "B must be <= 65535 (got %d)", B);
+    REQUIRE(K >= 1 && K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)",
+            FOCUS_MAX_GROUPS, K);
+    REQUIRE(iters >= 0 && iters <= FOCUS_MAX_SINKHORN_ITERS, FOCUS_ERR_INVALID_ARGUMENT,
+            "iters must be in [0, %d] (got %d)", FOCUS_MAX_SINKHORN_ITERS, iters);
+    REQUIRE(std::isfinite(tau) && tau > 0.0f, FOCUS_ERR_INVALID_ARGUMENT,
+            "tau must be finite and > 0");
+    REQUIRE((int64_t)B * iters <= kMaxGrid && (int64_t)n * K <= ((int64_t)1 << 40),
+            FOCUS_ERR_UNSUPPORTED, "problem too large");
+    REQUIRE_PTR(scores, 4);
+    REQUIRE_PTR(G, 4);
+    const size_t bytes = (size_t)B * n * K * 4;
+    REQUIRE(!overlaps(scores, bytes, G, bytes), FOCUS_ERR_INVALID_ARGUMENT,
+            "G must not overlap scores");
+    const size_t need = focus::sinkhorn_layout(B, n, K, iters).total;
+    REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    REQUIRE(workspace_bytes >= need, FOCUS_ERR_WORKSPACE,
+            "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+    REQUIRE(!overlaps(workspace, need, scores, bytes) && !overlaps(workspace, need, G, bytes),
+            FOCUS_ERR_INVALID_ARGUMENT, "workspace must not overlap scores or G");
+    return device_status(focus::launch_sinkhorn(scores, B, n, K, tau, iters, G, workspace,
+                                                static_cast<hipStream_t>(stream)),
+                         "sinkhorn launch");
 }
 
 size_t focus_group_sort_workspace_bytes(int B, int n, int K) {

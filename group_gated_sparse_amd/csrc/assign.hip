@@ -142,11 +142,12 @@ __device__ __forceinline__ void top_insert(TopList<M>& t, float x, int gx) {
     }
 }
 
+// M >= 1: top-M groups (ids, margin); M == 0: the raw scores [ntok][K].
 template <int NB, int M>
 __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
     const float* __restrict__ hidden, const __bf16* __restrict__ wfrag,
     const float* __restrict__ bias, int64_t ntok, int d_model, int dpad, int K,
-    int32_t* __restrict__ ids, float* __restrict__ margin) {
+    int32_t* __restrict__ ids, float* __restrict__ margin, float* __restrict__ scores) {
     // [wave][buffer][8 KB]; reused for the cross-wave reduction at the end.
     __shared__ __attribute__((aligned(1024))) unsigned char hbuf[4 * 2 * HSTEPB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -248,9 +249,21 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
                          red[((2 * NB + mb) * 16 + e) * 64 + lane];
 
     // Lane holds scores of groups k = mb*32 + 8*i + 4*hh + j (e = 4*i + j).
+    if constexpr (M == 0) {
+        if (tvalid) {
+#pragma unroll
+            for (int mb = 0; mb < NB; ++mb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int k = mb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                    if (k < K) scores[tok * K + k] = bias ? acc[mb][e] + bias[k] : acc[mb][e];
+                }
+        }
+        return;
+    }
     // Each lane half keeps the top M+1 of its groups; the halves then swap
     // lists and both merge them, so both hold the top M+1 over all groups.
-    TopList<M> top;
+    TopList<(M > 0 ? M : 1)> top;
 #pragma unroll
     for (int p = 0; p <= M; ++p) {
         top.v[p] = kNegInf;
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
 
 hipError_t launch_assign(const float* hidden, const float* P, const float* C, const float* bias,
                          int B, int n, int d_model, int d_proj, int K, int M, int32_t* ids,
-                         float* margin, void* workspace, hipStream_t stream) {
+                         float* margin, float* scores, void* workspace, hipStream_t stream) {
     const int KP = assign_kpad(K), dpad = assign_dpad(d_model);
     __bf16* wfrag = static_cast<__bf16*>(workspace);
     hipLaunchKernelGGL(assign_prep_kernel, dim3(dpad / (256 / KP)), dim3(256), 0, stream, P, C,
@@ -296,9 +309,11 @@ hipError_t launch_assign(const float* hidden, const float* P, const float* C, co
     const dim3 grid((unsigned)((ntok + 31) / 32));
 #define FOCUS_ASSIGN_LAUNCH(NB_, M_)                                                          \
     hipLaunchKernelGGL((assign_argmax_kernel<NB_, M_>), grid, dim3(256), 0, stream, hidden,   \
-                       wfrag, bias, ntok, d_model, dpad, K, ids, margin)
-    if (KP == 32 && M == 1) FOCUS_ASSIGN_LAUNCH(1, 1);
+                       wfrag, bias, ntok, d_model, dpad, K, ids, margin, scores)
+    if (KP == 32 && M == 0) FOCUS_ASSIGN_LAUNCH(1, 0);
+    else if (KP == 32 && M == 1) FOCUS_ASSIGN_LAUNCH(1, 1);
     else if (KP == 32 && M == 2) FOCUS_ASSIGN_LAUNCH(1, 2);
+    else if (M == 0) FOCUS_ASSIGN_LAUNCH(2, 0);
     else if (M == 1) FOCUS_ASSIGN_LAUNCH(2, 1);
     else if (M == 2) FOCUS_ASSIGN_LAUNCH(2, 2);
     else return hipErrorInvalidValue;

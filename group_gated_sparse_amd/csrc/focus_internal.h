@@ -19,10 +19,23 @@ inline size_t assign_workspace(int d_model, int K) {
     return 2 * align_up((size_t)assign_kpad(K) * assign_dpad(d_model) * 2);
 }
 // M = groups kept per token (1 or 2): ids [B][n][M], best first; margin =
-// (M-th score) - ((M+1)-th score).
+// (M-th score) - ((M+1)-th score). M = 0: the raw scores [B][n][K] instead.
 hipError_t launch_assign(const float* hidden, const float* P, const float* C, const float* bias,
                          int B, int n, int d_model, int d_proj, int K, int M, int32_t* ids,
-                         float* margin, void* workspace, hipStream_t stream);
+                         float* margin, float* scores, void* workspace, hipStream_t stream);
+
+// ---- Sinkhorn soft assignment -------------------------------------------------
+// Workspace: column scales v [B][K] and per-workgroup column sums
+// [B][nblk][K] (256-byte aligned).
+struct SinkhornLayout {
+    int lpr;      // lanes per score row: K rounded up to a power of two
+    int rpb;      // rows per workgroup
+    int nblk;     // workgroups per sequence
+    size_t v, partial, total;
+};
+SinkhornLayout sinkhorn_layout(int B, int n, int K, int iters);
+hipError_t launch_sinkhorn(const float* scores, int B, int n, int K, float tau, int iters,
+                           float* G, void* workspace, hipStream_t stream);
 
 // ---- grouping ---------------------------------------------------------------
 constexpr int SORT_BLOCK_TOKENS = 2048;  // tokens per workgroup of the two sort passes

@@ -49,6 +49,9 @@ _SIGNATURES = {
                              _p, _p, _sz, _p], _i),
     "focus_attn_topk_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                                           _f, _p, _i, _p, _p, _sz, _p], _i),
+    "focus_assign_scores": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
+    "focus_sinkhorn_workspace_bytes": ([_i, _i, _i, _i], _sz),
+    "focus_sinkhorn": ([_p, _i, _i, _i, _f, _i, _p, _p, _sz, _p], _i),
 }
 
 _lib = None
@@ -157,6 +160,48 @@ def _assign(hidden, P, C, bias, m, group_ids, margin, want_margin, workspace, st
                                           _ptr(margin), _ptr(ws),
                                           0 if ws is None else ws.numel(), _stream(stream)))
     return group_ids, margin
+
+
+def focus_assign_scores(hidden: torch.Tensor, P: torch.Tensor, C: torch.Tensor,
+                        bias: Optional[torch.Tensor] = None, *, scores=None, workspace=None,
+                        stream=None) -> torch.Tensor:
+    """Raw scores (h P) C^T + bias, (B, n, K) fp32."""
+    B, n, d_model = hidden.shape
+    d_proj = P.shape[1]
+    K = C.shape[0]
+    _need(hidden, "hidden", torch.float32)
+    _need(P, "P", torch.float32, (d_model, d_proj))
+    _need(C, "C", torch.float32, (K, d_proj))
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (K,))
+    if scores is None:
+        scores = torch.empty((B, n, K), dtype=torch.float32, device=hidden.device)
+    _need(scores, "scores", torch.float32, (B, n, K))
+    ws = _workspace(focus_assign_workspace_bytes(d_model, K), hidden.device, workspace)
+    _check_status(lib().focus_assign_scores(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n,
+                                            d_model, d_proj, K, _ptr(scores), _ptr(ws),
+                                            0 if ws is None else ws.numel(), _stream(stream)))
+    return scores
+
+
+def focus_sinkhorn_workspace_bytes(B: int, n: int, K: int, iters: int) -> int:
+    return int(lib().focus_sinkhorn_workspace_bytes(B, n, K, iters))
+
+
+def focus_sinkhorn(scores: torch.Tensor, tau: float, iters: int, *, G=None, workspace=None,
+                   stream=None) -> torch.Tensor:
+    """Sinkhorn soft assignment of exp(scores / tau): rows first, then
+    `iters` rounds of (columns to n/K, rows to 1). scores (B, n, K) fp32."""
+    _need(scores, "scores", torch.float32)
+    B, n, K = scores.shape
+    if G is None:
+        G = torch.empty_like(scores)
+    _need(G, "G", torch.float32, (B, n, K))
+    ws = _workspace(focus_sinkhorn_workspace_bytes(B, n, K, iters), scores.device, workspace)
+    _check_status(lib().focus_sinkhorn(_ptr(scores), B, n, K, float(tau), int(iters), _ptr(G),
+                                       _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(stream)))
+    return G
 
 
 def focus_group_sort_workspace_bytes(B: int, n: int, K: int) -> int:

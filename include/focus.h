@@ -58,6 +58,7 @@ typedef enum { FOCUS_BF16 = 0, FOCUS_F32 = 1 } focus_dtype;
 #define FOCUS_ABI_VERSION 2
 #define FOCUS_MAX_GROUPS 64
 #define FOCUS_MAX_MEMBERSHIPS 2 /* groups per token (m) of the top-k variant */
+#define FOCUS_MAX_SINKHORN_ITERS 10000
 
 int focus_abi_version(void);
 const char* focus_last_error(void);
@@ -100,6 +101,39 @@ focus_status focus_assign_topk(const float* hidden, const float* P, const float*
                                const float* bias, int B, int n, int d_model, int d_proj, int K,
                                int m, int32_t* group_ids, float* margin,
                                void* workspace, size_t workspace_bytes, focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Training-time soft assignment (Korean page §2.2; Japanese page §2.1 and
+ * §2.3): tokens are assigned softly to the K groups, and the assignment
+ * matrix of each sequence is made doubly stochastic by Sinkhorn
+ * normalisation (every group receives the same number of tokens).
+ *
+ * focus_assign_scores writes the raw scores of focus_assign:
+ *   scores[t][k] = (h_t · P) · C_k + bias[k]                 [B][n][K] fp32
+ * (same arithmetic, limits and workspace as focus_assign).
+ *
+ * focus_sinkhorn: with A = exp(scores / tau) per sequence,
+ *   G[t][k] = A[t][k] u[t] v[k], where the rows are normalised first
+ *   (v = 1, u[t] = 1 / sum_k A[t][k]) and then `iters` rounds set
+ *     v[k] = (n / K) / sum_t A[t][k] u[t]      (every group's total = n / K)
+ *     u[t] = 1 / sum_k A[t][k] v[k]            (every token's row = 1)
+ * so each row of G sums to 1 and, as iters grows, each column to n / K.
+ * scores [B][n][K] fp32 (not modified), G [B][n][K] fp32 (out, must not
+ * overlap scores). tau and iters are the caller's: the pages give neither.
+ * Computed in fp32 (row max subtracted before the exponent, which cancels
+ * exactly in u), one pass over the scores per round; sums in a fixed order,
+ * so results are bitwise reproducible.
+ * Limits: 1 <= K <= 64; 1 <= B <= 65535; n >= 1; 0 <= iters <= 10000;
+ *   tau finite and > 0.
+ * ---------------------------------------------------------------------- */
+focus_status focus_assign_scores(const float* hidden, const float* P, const float* C,
+                                 const float* bias, int B, int n, int d_model, int d_proj, int K,
+                                 float* scores, void* workspace, size_t workspace_bytes,
+                                 focus_stream_t stream);
+size_t focus_sinkhorn_workspace_bytes(int B, int n, int K, int iters);
+focus_status focus_sinkhorn(const float* scores, int B, int n, int K, float tau, int iters,
+                            float* G, void* workspace, size_t workspace_bytes,
+                            focus_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Step 2: stable grouping of tokens (counting sort per batch element).

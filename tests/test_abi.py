@@ -40,7 +40,7 @@ def test_header_is_plain_c():
 def test_library_exports_every_declared_symbol():
     lib = focus.lib()
     names = declared_functions()
-    assert len(names) >= 15
+    assert len(names) >= 18
     out = subprocess.check_output(["nm", "-D", "--defined-only", focus.LIB_PATH], text=True)
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     for name in names:
@@ -240,6 +240,55 @@ def test_attn_topk_rejects(fn, m, kw, code, msg):
         assert need1 <= 400000 < need2
     assert _attn_topk(fn, m, **kw) == code
     assert msg in _err()
+
+
+def _sink(**kw):
+    args = dict(S=A, B=1, n=100, K=8, tau=1.0, iters=5, G=Bp, ws=C_, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return focus.lib().focus_sinkhorn(args["S"], args["B"], args["n"], args["K"], args["tau"],
+                                      args["iters"], args["G"], args["ws"], args["wsb"],
+                                      args["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(S=None), INVALID, "scores"),
+    (dict(G=None), INVALID, "G"),
+    (dict(G=A + 64), INVALID, "overlap"),
+    (dict(K=0), UNSUPPORTED, "K"),
+    (dict(K=65), UNSUPPORTED, "K"),
+    (dict(n=0), INVALID, "n"),
+    (dict(B=70000), UNSUPPORTED, "B must be"),
+    (dict(iters=-1), INVALID, "iters"),
+    (dict(iters=10001), INVALID, "iters"),
+    (dict(tau=0.0), INVALID, "tau"),
+    (dict(tau=float("nan")), INVALID, "tau"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(wsb=16), WORKSPACE, "too small"),
+    (dict(ws=A + 256), INVALID, "overlap"),
+])
+def test_sinkhorn_rejects(kw, code, msg):
+    assert _sink(**kw) == code
+    assert msg in _err()
+
+
+def test_sinkhorn_workspace_size():
+    lib = focus.lib()
+    # column scales [B][K] + per-workgroup column sums [B][nblk][K] (128 rows per
+    # workgroup, at most 2048 workgroups), each region 256-byte aligned
+    assert lib.focus_sinkhorn_workspace_bytes(1, 100, 8, 5) == 2 * 256
+    assert lib.focus_sinkhorn_workspace_bytes(2, 32768, 32, 10) == 256 + 2 * 256 * 32 * 4
+    # 1M rows: 512-row workgroups, 2048 of them
+    assert lib.focus_sinkhorn_workspace_bytes(1, 1 << 20, 64, 10) == 256 + 2048 * 64 * 4
+    assert lib.focus_sinkhorn_workspace_bytes(1, 100, 0, 5) == 0
+
+
+def test_assign_scores_rejects():
+    f = focus.lib().focus_assign_scores
+    assert f(A, Bp, C_, None, 1, 8, 64, 16, 4, None, E_, 1 << 20, None) == INVALID
+    assert "scores" in _err()
+    assert f(A, Bp, C_, None, 1, 8, 64, 16, 4, A + 64, E_, 1 << 20, None) == INVALID
+    assert "overlap" in _err()
+    assert f(A, Bp, C_, None, 1, 8, 64, 16, 0, D_, E_, 1 << 20, None) == UNSUPPORTED
 
 
 def test_window_pass_takes_no_group_data():
