@@ -28,7 +28,6 @@ hipError_t launch_assign(const float* hidden, const float* P, const float* C, co
 // Workspace: column scales v [B][K] and per-workgroup column sums
 // [B][nblk][K] (256-byte aligned).
 struct SinkhornLayout {
-    int lpr;      // lanes per score row: K rounded up to a power of two
     int rpb;      // rows per workgroup
     int nblk;     // workgroups per sequence
     size_t v, partial, total;

@@ -16,9 +16,9 @@
 //                 v[k] = (n / K) / column sum for the next pass
 //     p = iters:  G[t][k] = A[t][k] u[t] v[k]
 //
-// A row's K scores sit in LPR lanes (K rounded up to a power of two), one
-// score per lane, so a row is one coalesced read and its max and sum are
-// lane-group reductions. A is recomputed from the scores on every pass with
+// A row's K scores sit in lpr lanes, four per lane when K is a multiple of
+// 4 (one per lane otherwise), so a row is one coalesced read and its max
+// and sum are a few in-lane steps plus lane-group reductions. A is recomputed from the scores on every pass with
 // the row max subtracted (exp2((s - max) log2(e) / tau)); the per-row factor
 // that this drops is absorbed by u exactly. Every sum is taken in a fixed
 // order, so results are bitwise reproducible.
@@ -82,46 +82,79 @@ struct SinkArgs {
 
 constexpr int UNROLL = 8;   // row chunks in flight per wave
 
+// VPL scores per lane: 1, or 4 (one 16-byte load) when K is a multiple of
+// 4; a row then spans lpr = next power of two >= K / VPL lanes.
+template <int VPL>
 __global__ __launch_bounds__(NT) void sinkhorn_pass_kernel(SinkArgs a, int pass) {
-    __shared__ float wsum[4][64];
+    typedef float vecf __attribute__((ext_vector_type(VPL)));
+    __shared__ float wsum[4][64 * VPL];
     const int b = blockIdx.y, blk = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lpr = a.lpr, rpw = 64 / lpr;
-    const int c = lane & (lpr - 1);          // column of this lane
-    const bool cvalid = c < a.K;
+    const int c = lane & (lpr - 1);          // this lane's scores: columns VPL*c .. VPL*c + VPL-1
+    const bool cvalid = VPL * c < a.K;
     const bool final_pass = pass == a.iters;
-    const float vc = (pass == 0 || !cvalid) ? 1.0f : a.v[(int64_t)b * a.K + c];
+    float vc[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+        vc[j] = (pass == 0 || !cvalid) ? 1.0f : a.v[(int64_t)b * a.K + VPL * c + j];
     const float* Sb = a.S + (int64_t)b * a.n * a.K;
     const int r0 = blk * a.rpb, r1 = min(a.n, r0 + a.rpb);
-    float colacc = 0.0f;
+    float colacc[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) colacc[j] = 0.0f;
     // wave-row chunks of rpw rows: chunk q of a trip covers rows
     // base + q * 4 * rpw + lane / lpr; a trip covers 4 * UNROLL * rpw rows
     for (int base = r0 + wave * rpw; base < r1; base += 4 * UNROLL * rpw) {
-        float s[UNROLL];
+        vecf s[UNROLL];
 #pragma unroll
         for (int q = 0; q < UNROLL; ++q) {
             const int t = base + q * 4 * rpw + lane / lpr;
-            s[q] = (t < r1 && cvalid) ? Sb[(int64_t)t * a.K + c] : kNegInf;
+            if (t < r1 && cvalid) {
+                s[q] = *reinterpret_cast<const vecf*>(Sb + (int64_t)t * a.K + VPL * c);
+            } else {
+#pragma unroll
+                for (int j = 0; j < VPL; ++j) s[q][j] = kNegInf;
+            }
         }
 #pragma unroll
         for (int q = 0; q < UNROLL; ++q) {
             const int t = base + q * 4 * rpw + lane / lpr;
-            const float m = lane_group_max(s[q], lpr);
-            const float e = (s[q] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((s[q] - m) * a.sl2);
-            const float rs = lane_group_sum(e * vc, lpr);
+            float m = s[q][0];
+#pragma unroll
+            for (int j = 1; j < VPL; ++j) m = fmaxf(m, s[q][j]);
+            m = lane_group_max(m, lpr);
+            float e[VPL], rs = 0.0f;
+#pragma unroll
+            for (int j = 0; j < VPL; ++j) {
+                e[j] = (s[q][j] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f((s[q][j] - m) * a.sl2);
+                rs += e[j] * vc[j];
+            }
+            rs = lane_group_sum(rs, lpr);
             const float u = rs > 0.0f ? 1.0f / rs : 0.0f;
             if (final_pass) {
-                if (t < r1 && cvalid) a.G[((int64_t)b * a.n + t) * a.K + c] = e * u * vc;
+                if (t < r1 && cvalid) {
+                    vecf g;
+#pragma unroll
+                    for (int j = 0; j < VPL; ++j) g[j] = e[j] * u * vc[j];
+                    *reinterpret_cast<vecf*>(a.G + ((int64_t)b * a.n + t) * a.K + VPL * c) = g;
+                }
             } else {
-                colacc += e * u;
+#pragma unroll
+                for (int j = 0; j < VPL; ++j) colacc[j] += e[j] * u;
             }
         }
     }
     if (final_pass) return;
-    // Column sums of this workgroup: lanes of one column (lane xor multiples
-    // of lpr), then the four waves in order.
-    for (int o = lpr; o < 64; o <<= 1) colacc += __shfl_xor(colacc, o);
-    if (lane < lpr) wsum[wave][lane] = colacc;
+    // Column sums of this workgroup: lanes of one column chunk (lane xor
+    // multiples of lpr), then the four waves in order.
+#pragma unroll
+    for (int j = 0; j < VPL; ++j)
+        for (int o = lpr; o < 64; o <<= 1) colacc[j] += __shfl_xor(colacc[j], o);
+    if (lane < lpr) {
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) wsum[wave][VPL * lane + j] = colacc[j];
+    }
     __syncthreads();
     if (tid < a.K)
         a.partial[((int64_t)b * a.nblk + blk) * a.K + tid] =
@@ -159,8 +192,6 @@ __global__ __launch_bounds__(NT) void sinkhorn_reduce_kernel(const float* __rest
 SinkhornLayout sinkhorn_layout(int B, int n, int K, int iters) {
     (void)iters;
     SinkhornLayout L{};
-    L.lpr = 1;
-    while (L.lpr < K) L.lpr <<= 1;
     // rows per workgroup: at least 128, and at most 2048 workgroups per sequence
     L.rpb = 128;
     while ((n + L.rpb - 1) / L.rpb > 2048) L.rpb <<= 1;
@@ -182,9 +213,14 @@ hipError_t launch_sinkhorn(const float* scores, int B, int n, int K, float tau, 
     a.G = G;
     a.v = v;
     a.partial = reinterpret_cast<float*>(base + L.partial);
+    // four scores per lane (16-byte loads) when every row starts on 16 bytes
+    const bool a16 = ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(G)) & 15) == 0;
+    const int vpl = (K % 4 == 0 && a16) ? 4 : 1;
+    int lpr = 1;
+    while (lpr * vpl < K) lpr <<= 1;
     a.n = n;
     a.K = K;
-    a.lpr = L.lpr;
+    a.lpr = lpr;
     a.rpb = L.rpb;
     a.nblk = L.nblk;
     a.iters = iters;
@@ -192,7 +228,10 @@ hipError_t launch_sinkhorn(const float* scores, int B, int n, int K, float tau, 
     const float target = (float)n / (float)K;
     const dim3 grid((unsigned)L.nblk, (unsigned)B);
     for (int p = 0; p <= iters; ++p) {
-        hipLaunchKernelGGL(sinkhorn_pass_kernel, grid, dim3(NT), 0, stream, a, p);
+        if (vpl == 4)
+            hipLaunchKernelGGL(sinkhorn_pass_kernel<4>, grid, dim3(NT), 0, stream, a, p);
+        else
+            hipLaunchKernelGGL(sinkhorn_pass_kernel<1>, grid, dim3(NT), 0, stream, a, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (p == iters) break;

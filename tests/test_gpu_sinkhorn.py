@@ -64,6 +64,10 @@ SINK_CASES = [
     ("k3_many_blocks", 1, 300001, 3, 1.0, 4, 1.0),
     ("k33_small_n", 2, 17, 33, 2.0, 20, 3.0),
     ("k16_long", 1, 70000, 16, 1.0, 30, 1.0),
+    # long sequences (one thread per row): 16-, 32- and 64-wide rows, ragged ends
+    ("rows_k20", 1, 300007, 20, 1.0, 5, 1.0),
+    ("rows_k50_b2", 2, 140001, 50, 0.8, 3, 1.5),
+    ("rows_k64", 1, 262144, 64, 1.0, 8, 1.0),
 ]
 
 
@@ -77,6 +81,23 @@ def test_sinkhorn_matches_oracle(case):
     torch.cuda.synchronize()
     ref = oracle.sinkhorn(S, tau, iters)
     check_G(host(G), ref, name)
+
+
+def test_sinkhorn_unaligned_rows():
+    """Scores and G that start 4 bytes off a 16-byte boundary (one score per
+    lane instead of four) give the oracle's result too."""
+    say("[sinkhorn] 4-byte aligned buffers")
+    rng = np.random.default_rng(6)
+    B, n, K = 1, 3000, 32
+    S = _scores(rng, B, n, K, 1.0)
+    buf = torch.empty(B * n * K + 1, dtype=torch.float32, device="cuda")
+    out = torch.empty(B * n * K + 1, dtype=torch.float32, device="cuda")
+    s_view = buf[1:].view(B, n, K)
+    g_view = out[1:].view(B, n, K)
+    s_view.copy_(dev(S))
+    focus.focus_sinkhorn(s_view, 1.0, 6, G=g_view)
+    torch.cuda.synchronize()
+    check_G(host(g_view), oracle.sinkhorn(S, 1.0, 6), "unaligned")
 
 
 def test_sinkhorn_is_deterministic_and_workspace_reusable():
