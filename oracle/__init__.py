@@ -71,6 +71,10 @@ def configure(lib):
     lib.oracle_assign_scores.restype = ctypes.c_int
     lib.oracle_sinkhorn.argtypes = [_p, _i64, _i64, _i64, ctypes.c_double, _i64, _p]
     lib.oracle_sinkhorn.restype = ctypes.c_int
+    lib.oracle_soft_gate_attn.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                          ctypes.c_double, ctypes.c_double, _p, _i64, _p, _p,
+                                          ctypes.c_int]
+    lib.oracle_soft_gate_attn.restype = ctypes.c_int
     return lib
 
 
@@ -348,3 +352,34 @@ def sinkhorn(scores, tau: float, iters: int):
     if _load().oracle_sinkhorn(_ptr(scores), B, n, K, float(tau), int(iters), _ptr(G)) != 0:
         raise ValueError("oracle_sinkhorn rejected its arguments")
     return G
+
+
+def soft_gate_attn(q, k, v, G, w: int, scale: float, lam: float, rows=None, nthreads: int = 0):
+    """Training-time soft-gated attention (Japanese page §2.1-§2.2, Korean
+    page §2.1): every causal pair, weight gate_ij * exp(scale q_i.k_j) with
+    gate 1 inside the window (i - j <= w) and sigmoid(lam * g_i.g_j) beyond.
+    G (B, n, K) fp32 soft assignments. Returns (out, lse) like attn()."""
+    q = _c(q, np.uint16)
+    k = _c(k, np.uint16)
+    v = _c(v, np.uint16)
+    G = _c(G, np.float32)
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    K = G.shape[2]
+    assert k.shape == (B, Hkv, n, d) and v.shape == k.shape and G.shape[:2] == (B, n)
+    if rows is not None:
+        rows = _c(rows, np.int64).ravel()
+        count = rows.size
+    else:
+        count = B * Hq * n
+    out = np.empty((count, d), dtype=np.float64)
+    lse = np.empty(count, dtype=np.float64)
+    rc = _load().oracle_soft_gate_attn(_ptr(q), _ptr(k), _ptr(v), _ptr(G), B, Hq, Hkv, n, d, K,
+                                       int(w), float(scale), float(lam), _ptr(rows),
+                                       count if rows is not None else 0, _ptr(out), _ptr(lse),
+                                       nthreads)
+    if rc != 0:
+        raise ValueError("oracle_soft_gate_attn rejected its arguments")
+    if rows is None:
+        return out.reshape(B, Hq, n, d), lse.reshape(B, Hq, n)
+    return out, lse

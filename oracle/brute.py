@@ -97,3 +97,35 @@ def attention_sets(q, k, v, groups, w, scale):
         out.append(oh)
         counts.append(ch)
     return out, counts
+
+
+def soft_gate_attention(q, k, v, G, w, scale, lam):
+    """Training-time soft gate (Japanese page §2.1-§2.2, Korean page §2.1),
+    pair by pair: every causal pair is kept; a pair further apart than the
+    window is weighted by the logistic function of lam times the dot product
+    of the two tokens' soft assignments; the softmax is renormalised over the
+    weighted pairs. G: [n][K] floats. Returns out [Hq][n][d]."""
+    Hq, Hkv = len(q), len(k)
+    n, d = len(q[0]), len(q[0][0])
+    share = Hq // Hkv
+    out = []
+    for h in range(Hq):
+        kv = h // share
+        Kf = [[bf16_to_float(x) for x in row] for row in k[kv]]
+        Vf = [[bf16_to_float(x) for x in row] for row in v[kv]]
+        oh = []
+        for i in range(n):
+            qi = [bf16_to_float(x) for x in q[h][i]]
+            logits = [scale * math.fsum(a * b for a, b in zip(qi, Kf[j])) for j in range(i + 1)]
+            top = max(logits)
+            wts = []
+            for j in range(i + 1):
+                g = 1.0
+                if i - j > w:
+                    aff = math.fsum(x * y for x, y in zip(G[i], G[j]))
+                    g = 1.0 / (1.0 + math.exp(-lam * aff))
+                wts.append(g * math.exp(logits[j] - top))
+            tot = math.fsum(wts)
+            oh.append([math.fsum(wts[j] / tot * Vf[j][c] for j in range(i + 1)) for c in range(d)])
+        out.append(oh)
+    return out

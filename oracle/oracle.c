@@ -28,6 +28,10 @@
  *   every column's target is n / K (only its being equal matters: the final
  *   row step cancels a common factor); tau and the number of rounds are not
  *   given by the pages and are arguments.
+ *   Soft gate (training): every causal pair is computed; pairs beyond the
+ *   window are weighted by sigmoid(lambda * g_i . g_j) inside an exact,
+ *   renormalised softmax (the pages' "product of the local mask and the
+ *   gate" read as: the window passes unchanged, the gate scales the rest).
  *   Multi-membership (top-m groups per token, m = 2 in the pages' runs): a far
  *   pair is kept when the tokens share at least one group, and still counted
  *   once; the top-m groups are the m highest scores, ties to the lowest index.
@@ -569,4 +573,76 @@ int oracle_sinkhorn(const float* scores, int64_t B, int64_t n, int64_t K, double
     free(v);
     free(col);
     return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Training-time soft-gated attention (Japanese page §2.1: group affinity
+ * a_ij = g_i . g_j of the soft assignments and a gate sigma(lambda a_ij);
+ * §2.2: in training the gate is soft and every pair is computed, so the
+ * cost stays O(n^2); Korean page §2.1: pairs inside the local window are
+ * attended at full resolution, far pairs are controlled by the group gate,
+ * and the softmax is kept exact). Reading: every causal pair enters the
+ * softmax with weight gate_ij * exp(scale q_i . k_j), where gate_ij = 1 for
+ * 0 <= i - j <= w and sigma(lambda a_ij) for i - j > w:
+ *   out_i = sum_j gate_ij exp(s_ij) v_j / sum_j gate_ij exp(s_ij)
+ *   lse_i = log sum_j gate_ij exp(s_ij)
+ * G [B][n][K] fp32 soft assignments; everything else as oracle_attn.
+ * ---------------------------------------------------------------------- */
+int oracle_soft_gate_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                          const float* G, int64_t B, int64_t Hq, int64_t Hkv, int64_t n,
+                          int64_t d, int64_t K, int64_t w, double scale, double lambda,
+                          const int64_t* rows, int64_t nrows, double* out, double* lse,
+                          int nthreads) {
+    if (!q || !k || !v || !G || !out || B < 1 || Hq < 1 || Hkv < 1 || n < 1 || d < 1 || K < 1 ||
+        w < 0 || Hq % Hkv)
+        return -1;
+    int64_t count = rows ? nrows : B * Hq * n;
+    int64_t group = Hq / Hkv;
+    set_threads(nthreads);
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)n);
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t r = 0; r < count; ++r) {
+            int64_t row = rows ? rows[r] : r;
+            if (row < 0 || row >= B * Hq * n) {
+#pragma omp atomic write
+                bad = 1;
+                continue;
+            }
+            int64_t i = row % n, bh = row / n, h = bh % Hq, b = bh / Hq;
+            int64_t kvh = h / group;
+            const uint16_t* qrow = q + row * d;
+            const uint16_t* kb = k + (b * Hkv + kvh) * n * d;
+            const uint16_t* vb = v + (b * Hkv + kvh) * n * d;
+            const float* gi = G + (b * n + i) * K;
+            double m = -INFINITY;
+            for (int64_t j = 0; j <= i; ++j) {
+                double dot = 0.0;
+                for (int64_t c = 0; c < d; ++c) dot += bf16_value(qrow[c]) * bf16_value(kb[j * d + c]);
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            double* o = out + r * d;
+            for (int64_t c = 0; c < d; ++c) o[c] = 0.0;
+            double l = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                double gate = 1.0;
+                if (i - j > w) {
+                    const float* gj = G + (b * n + j) * K;
+                    double a = 0.0;
+                    for (int64_t x = 0; x < K; ++x) a += (double)gi[x] * (double)gj[x];
+                    gate = 1.0 / (1.0 + exp(-lambda * a));
+                }
+                double p = gate * exp(s[j] - m);
+                l += p;
+                for (int64_t c = 0; c < d; ++c) o[c] += p * bf16_value(vb[j * d + c]);
+            }
+            for (int64_t c = 0; c < d; ++c) o[c] /= l;
+            if (lse) lse[r] = m + log(l);
+        }
+        free(s);
+    }
+    return bad ? -1 : 0;
 }

@@ -18,6 +18,7 @@ import test_oracle_assign_sort as tas
 import test_oracle_attn as tat
 import test_oracle_multi as tmu
 import test_oracle_sinkhorn as tsk
+import test_oracle_soft_gate as tsg
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
 
@@ -55,6 +56,13 @@ MUTANTS = {
     "sinkhorn rows-first step skipped": ("u[t] = 1.0 / r;\n        }\n        for (int64_t it",
                                          "u[t] = 1.0;\n        }\n        for (int64_t it"),
     "sinkhorn column sum misses u": ("col[k] += A[t * K + k] * u[t];", "col[k] += A[t * K + k];"),
+    "soft gate reaches into the window": ("if (i - j > w) {\n                    const float* gj",
+                                          "if (i - j >= w) {\n                    const float* gj"),
+    "soft gate sign flipped": ("gate = 1.0 / (1.0 + exp(-lambda * a));",
+                               "gate = 1.0 / (1.0 + exp(lambda * a));"),
+    "soft gate affinity of the row with itself": ("a += (double)gi[x] * (double)gj[x];",
+                                                  "a += (double)gi[x] * (double)gi[x];"),
+    "soft gate dropped": ("double p = gate * exp(s[j] - m);", "double p = exp(s[j] - m);"),
 }
 
 PINS = [
@@ -83,6 +91,11 @@ PINS = [
     tsk.test_cross_ratios_are_those_of_exp_scores,
     tsk.test_marginals_rows_exact_columns_converge,
     tsk.test_row_shift_and_column_permutation,
+    tsg.test_wide_window_is_causal_attention,
+    tsg.test_zero_lambda_halves_far_pairs,
+    lambda: tsg.test_uniform_assignment_gives_a_constant_gate(4, 3.0),
+    tsg.test_general_gate_against_sdpa_with_affinity_bias,
+    lambda: tsg.test_brute_force(17, 3, -2.0, 3),
 ]
 
 
