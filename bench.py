@@ -53,9 +53,11 @@ def parse():
                     help="target CPU time of the oracle attention sample")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the window pass on the main stream, after the sort")
-    ap.add_argument("--op", default="attn", choices=["attn", "sinkhorn"],
+    ap.add_argument("--op", default="attn", choices=["attn", "sinkhorn", "soft_gate"],
                     help="attn: the inference forward step (default); sinkhorn: the "
-                         "training-time soft assignment (scores + Sinkhorn rounds)")
+                         "training-time soft assignment (scores + Sinkhorn rounds); "
+                         "soft_gate: the training-time soft-gated attention forward")
+    ap.add_argument("--lam", type=float, default=8.0, help="gate slope (--op soft_gate)")
     ap.add_argument("--iters", type=int, default=10, help="Sinkhorn rounds (--op sinkhorn)")
     ap.add_argument("--tau", type=float, default=1.0, help="Sinkhorn temperature (--op sinkhorn)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -232,6 +234,100 @@ def bench_sinkhorn(args, wl):
     print(json.dumps(res), flush=True)
 
 
+def bench_soft_gate(args, wl):
+    """Training-time soft-gated attention forward on the workload's shape,
+    with G = Sinkhorn soft assignments of its hidden states (computed once,
+    outside the timed region); one JSON line, dense causal beside it."""
+    import torch
+    from group_gated_sparse_amd import focus, metrics, synth
+    log(f"workload {wl.name}: generating seeded inputs")
+    x = synth.make_inputs(wl)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    def dev16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    S = focus.focus_assign_scores(dev(x["hidden"]), dev(x["P"]), dev(x["C"]),
+                                  None if x["bias"] is None else dev(x["bias"]))
+    G = focus.focus_sinkhorn(S, args.tau, args.iters)
+    del S
+    q, k, v = dev16(x["q"]), dev16(x["k"]), dev16(x["v"])
+    B, n, d, Hq, K, w = wl.B, wl.n, wl.d, wl.Hq, wl.K, wl.w
+    out = torch.empty((B, Hq, n, d), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(focus.focus_soft_gate_attn_workspace_bytes(B, n, K), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        focus.focus_soft_gate_attn_fwd(q, k, v, G, w, wl.softmax_scale, args.lam, out=out,
+                                       workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    ms = max(wall_ms, ev_ms)
+    pairs = B * (n * (n + 1) // 2)
+    flops = metrics.attn_flops(pairs, Hq, d)
+    ww = min(w, n - 1)
+    far = pairs - B * (n * (ww + 1) - ww * (ww + 1) // 2)
+    KG = 16 if K <= 16 else (32 if K <= 32 else 64)
+    log(f"soft gate {ms:.3f} ms ({flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s on causal pairs)")
+    res = {
+        "metric": "Soft-gated attention forward TFLOP/s (causal pairs), 1 GPU",
+        "value": flops / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "op": "soft_gate", "B": B, "Hq": Hq, "Hkv": wl.Hkv,
+                   "n": n, "d_head": d, "K": K, "window": w, "lambda": args.lam,
+                   "sinkhorn_iters": args.iters, "tau": args.tau, "out_dtype": "bf16"},
+        "causal_pairs_per_head": pairs, "far_pairs_per_head": far,
+        "affinity_flops": 3 * 2 * KG * far * Hq,
+        "roofline": {"kernel": f"attn_kernel<{d},{4 + (KG // 32)}> (soft-gated pass)",
+                     "bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
+                     "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ms * 1e-3) / 1e12 / metrics.MI355X_BF16_DENSE_TFLOPS,
+                     "traffic": None, "flops_per_launch": flops, "avg_launch_ms": ev_ms},
+    }
+    if not args.skip_dense:
+        focus.dense_causal_attn_fwd(q, k, v, wl.softmax_scale, out=out)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.dense_iters):
+            focus.dense_causal_attn_fwd(q, k, v, wl.softmax_scale, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        res["dense_ms"] = e0.elapsed_time(e1) / args.dense_iters
+        res["gate_overhead_vs_dense"] = ms / res["dense_ms"]
+        log(f"dense {res['dense_ms']:.3f} ms")
+    if not args.skip_cpu_baseline:
+        import oracle
+        rng = np.random.default_rng(7)
+        rows = rng.integers(0, B * Hq * n, size=4096)
+        g_host = G.cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.soft_gate_attn(x["q"], x["k"], x["v"], g_host, w, wl.softmax_scale, args.lam,
+                              rows=rows)
+        t = time.perf_counter() - t0
+        i = rows % n
+        done = int((i + 1).sum())
+        res["cpu_baseline"] = {"value": metrics.attn_flops(done, 1, d) / t / 1e12,
+                               "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+                               "sample": f"fp64 oracle on 4096 random query rows ({done} causal "
+                                         f"pairs, {t:.1f} s)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -249,6 +345,8 @@ def main():
     wl = workloads.BY_NAME[args.workload]
     if args.op == "sinkhorn":
         return bench_sinkhorn(args, wl)
+    if args.op == "soft_gate":
+        return bench_soft_gate(args, wl)
     log(f"workload {wl.name}: generating seeded inputs")
     t0 = time.perf_counter()
     x = synth.make_inputs(wl)

@@ -358,6 +358,41 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
                       workspace_bytes, stream);
 }
 
+size_t focus_soft_gate_attn_workspace_bytes(int B, int n, int K) {
+    if (B < 1 || n < 1 || K < 1 || K > FOCUS_MAX_GROUPS) return 0;
+    return focus::soft_gate_workspace(B, n, K);
+}
+
+focus_status focus_soft_gate_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      const float* G, int B, int Hq, int Hkv, int n, int d_head,
+                                      int K, int window, float scale, float lambda, void* out,
+                                      focus_dtype out_dtype, float* lse, void* workspace,
+                                      size_t workspace_bytes, focus_stream_t stream) {
+    const AttnShape s{B, Hq, Hkv, n, d_head, K, window};
+    focus_status st = check_attn_shape(s, true);
+    if (st != FOCUS_OK) return st;
+    st = check_attn_buffers(q, k, v, s, out, out_dtype, lse, scale);
+    if (st != FOCUS_OK) return st;
+    REQUIRE(std::isfinite(lambda), FOCUS_ERR_INVALID_ARGUMENT, "lambda must be finite");
+    REQUIRE_PTR(G, 4);
+    const size_t gbytes = (size_t)B * n * K * 4;
+    const size_t obytes = (size_t)B * Hq * n * d_head * (out_dtype == FOCUS_F32 ? 4 : 2);
+    REQUIRE(!overlaps(out, obytes, G, gbytes), FOCUS_ERR_INVALID_ARGUMENT,
+            "out must not overlap G");
+    const size_t need = focus::soft_gate_workspace(B, n, K);
+    REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    REQUIRE(workspace_bytes >= need, FOCUS_ERR_WORKSPACE,
+            "workspace too small: %zu bytes given, %zu required", workspace_bytes, need);
+    REQUIRE(!overlaps(workspace, need, G, gbytes) && !overlaps(workspace, need, out, obytes),
+            FOCUS_ERR_INVALID_ARGUMENT, "workspace must not overlap G or out");
+    focus::AttnProblem p{q, k, v, nullptr, nullptr, nullptr, B, Hq, Hkv, n, d_head, K, window,
+                         scale, out, out_dtype == FOCUS_F32 ? 1 : 0, lse, workspace};
+    return device_status(focus::launch_attn_soft_gate(p, G, lambda,
+                                                      static_cast<hipStream_t>(stream)),
+                         "soft-gated attention launch");
+}
+
 size_t focus_attn_topk_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int m,
                                        int window) {
     (void)K;

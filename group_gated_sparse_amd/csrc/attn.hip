@@ -68,7 +68,10 @@ constexpr float kProbSumCap = 256.0f;  // a lane's probability sum that triggers
 constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 
 // kLongMulti: the long-range pass over membership entries, two groups per token.
-enum { kWindow = 0, kLongRange = 1, kDense = 2, kLongMulti = 3 };
+// kSoftGate + s (s = 0, 1, 2): the training-time soft-gated pass over every
+// causal pair, with soft assignments of KG = 16 << s columns (zero-padded).
+enum { kWindow = 0, kLongRange = 1, kDense = 2, kLongMulti = 3, kSoftGate = 4 };
+constexpr bool attn_gated(int PHASE) { return PHASE >= kSoftGate; }
 
 struct AttnArgs {
     const uint16_t* q;
@@ -92,6 +95,9 @@ struct AttnArgs {
     int ntiles;    // ceil(n / TT)
     int total;     // workgroups
     float sl2;     // scale * log2(e)
+    const uint16_t* gs;   // soft-gated pass: bf16 hi/lo split of the soft assignments,
+                          // [B][n][2][KG] (hi row, then lo row)
+    float nl2;            // soft-gated pass: -lambda * log2(e)
     int out_f32;
     int merge;     // start from the partial in og/lseg (row of the original position)
     int partial;   // write the normalised partial to og/lseg instead of out/lse
@@ -101,8 +107,11 @@ struct AttnArgs {
 // wait on memory while two compute) wherever the registers fit, i.e. all but
 // the dense pass at d = 128. Keys per tile: 32 at three workgroups per CU
 // for d = 64/128 (LDS and registers), 64 otherwise.
-constexpr int attn_occupancy(int D, int PHASE) { return (D == 128 && PHASE == kDense) ? 2 : 3; }
+constexpr int attn_occupancy(int D, int PHASE) {
+    return attn_gated(PHASE) ? 2 : ((D == 128 && PHASE == kDense) ? 2 : 3);
+}
 constexpr int attn_tile_keys(int D, int PHASE) {
+    if (attn_gated(PHASE)) return D == 32 ? 64 : 32;   // registers for the gate operands
     return (D != 32 && attn_occupancy(D, PHASE) == 3) ? 32 : 64;
 }
 
@@ -143,6 +152,14 @@ __device__ __forceinline__ int lds_off(int row, int ch) {
 template <int D>
 __device__ __forceinline__ int logical_chunk(int row, int pc) {
     return pc ^ swz<D>(row);
+}
+
+// Swizzle of the soft-gated pass's assignment rows in LDS (GNCH 16-byte
+// chunks per row): the 16 consecutive rows that one quarter-wave reads at
+// the same logical chunk land in 16 distinct bank groups.
+template <int GNCH>
+__device__ __forceinline__ int gswz(int r) {
+    return GNCH >= 16 ? (r & 15) : ((r * GNCH / 16) & (GNCH - 1));
 }
 
 __device__ __forceinline__ float other_half(float x) {
@@ -290,6 +307,14 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     constexpr int BN = G::BN;
     constexpr bool SORTED = PHASE == kLongRange || PHASE == kLongMulti;
     constexpr bool MULTI = PHASE == kLongMulti;   // entries of two groups per token
+    constexpr bool GATED = attn_gated(PHASE);
+    constexpr bool CAUSAL_ALL = PHASE == kDense || GATED;   // key range [0, last row]
+    // soft-gated pass: assignment columns (padded), bytes per key row of the
+    // hi/lo split, 16-byte chunks per row, 1 KB copies per key tile
+    constexpr int KG = GATED ? (16 << (PHASE - kSoftGate)) : 16;
+    constexpr int GROWB = 4 * KG;
+    constexpr int GNCH = GROWB / 16;
+    constexpr int GNC = BN * GROWB / 1024;
     // slots of the tiled order (n except in the multi pass)
     const int ne = MULTI ? a.ne : a.n;
     // smem = [K/V buffer 0 | K/V buffer 1]; buffer 1 also stages the Q tile in
@@ -298,6 +323,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     unsigned char* const buf0 = smem;
     unsigned char* const buf1 = smem + 2 * G::TILEB;
     __shared__ __attribute__((aligned(1024))) int kpos0[KPOS_PAD], kpos1[KPOS_PAD];
+    // soft-gated pass: the key tile's assignment rows, one buffer per K/V buffer
+    __shared__ __attribute__((aligned(1024))) unsigned char gk_lds[GATED ? 2 * BN * GROWB : 16];
     __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1], seg_kfull[MAXSEG];
     __shared__ int rowpos[ROWS];  // entry (= position with one group) of each query row (sorted pass)
     __shared__ int excl_any;      // multi pass: some row can meet a pair shared twice
@@ -347,7 +374,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     if (!SORTED) {
         const int q0 = tile * a.TT;
         const int qlast = min(a.n, q0 + a.TT) - 1;
-        kstart = (PHASE == kDense) ? 0 : max(0, q0 - a.w);
+        kstart = CAUSAL_ALL ? 0 : max(0, q0 - a.w);
         kend0 = qlast + 1;
         ntl = (kend0 - kstart + BN - 1) / BN;
     } else {
@@ -427,7 +454,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             kend = kend0;
             const int q0 = tile * a.TT;
             full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
-                   (PHASE == kDense || kend - 1 - kt0 <= a.w);
+                   (CAUSAL_ALL || kend - 1 - kt0 <= a.w);
         } else {
             // segment values are uniform (LDS, written by one thread each)
             while (__builtin_amdgcn_readfirstlane(seg_t0[seg + 1]) <= tau) ++seg;
@@ -453,6 +480,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     }
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave index in a scalar register
     int seg_issue = 0, seg_cur = 0;
+    // soft-gated pass: this lane's share of the assignment-row copies (1 KB
+    // copies wave, wave + 4, ...): key row within the tile and logical chunk
+    constexpr int GCPW = (GNC + 3) / 4;
+    int g_row[GCPW], g_chunk[GCPW];
+#pragma unroll
+    for (int i = 0; i < GCPW; ++i) {
+        const int o = (wave + 4 * i) * 1024 + 16 * lane;
+        g_row[i] = o / GROWB;
+        g_chunk[i] = ((o % GROWB) / 16) ^ gswz<GNCH>(g_row[i]);
+    }
     auto issue = [&](int tau, unsigned char* bufp, int* kposp) {
         int kt0, kend;
         bool full;
@@ -480,6 +517,19 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         // positions of the tile's key slots, for the mask of a partial tile
         if (SORTED && !full && wave == 0)
             copy16(a.spos + (int64_t)b * (ne + KPOS_PAD) + kt0 + 4 * lane, kposp);
+        if constexpr (GATED) {
+            // the key tile's assignment rows (hi and lo), row-clamped at the end
+            unsigned char* gd = gk_lds + (bufp == buf0 ? 0 : BN * GROWB);
+            const char* gbase = reinterpret_cast<const char*>(a.gs) + (int64_t)b * a.n * GROWB;
+#pragma unroll
+            for (int i = 0; i < GCPW; ++i) {
+                if (wave_s + 4 * i < GNC) {
+                    const int key = min(kt0 + g_row[i], a.n - 1);
+                    copy16(gbase + (int64_t)key * GROWB + g_chunk[i] * 16,
+                           gd + (wave_s + 4 * i) * 1024);
+                }
+            }
+        }
     };
 
     // LDS offsets of this lane's operand reads (tile-relative).
@@ -497,6 +547,15 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             voff[db][s] = G::TILEB + lds_off<D>(4 * hh + (m16 >> 2) + 8 * s, col >> 3) + (col & 7) * 2;
         }
 
+    // soft-gated pass: LDS offsets of this lane's assignment-row reads
+    // (key rl, columns 16*ks + 8*hh .. +8 of the hi (part 0) or lo (part 1) half)
+    int goff[KG / 16][2];
+#pragma unroll
+    for (int ks = 0; ks < KG / 16; ++ks)
+#pragma unroll
+        for (int part = 0; part < 2; ++part)
+            goff[ks][part] = rl * GROWB + (((part * KG / 8) + 2 * ks + hh) ^ gswz<GNCH>(rl)) * 16;
+
     f32x16 acc[G::DB];
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
@@ -504,6 +563,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
     float m_ref = kNegInf, l_run = 0.0f;
     bf16x8 qf[G::KS];  // Q^T fragments, loaded once the first key tile is in flight
+    bf16x8 gq[KG / 16][2];  // soft-gated pass: the row's assignment (hi, lo) fragments
 
     auto compute = [&](int tau, const unsigned char* bufp, const int* kposp) {
         int kt0, kend;
@@ -552,7 +612,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                         const int key = kt0 + k0 + j;
                         bool ok;
                         if (!SORTED) {
-                            ok = (key < kend) & (key <= pos_i) & (pos_i - key <= a.w);
+                            // (the dense pass runs with w = n; the gated pass
+                            // keeps far keys and gates them instead)
+                            ok = (key < kend) & (key <= pos_i) & (GATED || pos_i - key <= a.w);
                         } else if (!MULTI) {
                             ok = row_ok & (key < kend) & (pos_i - kp[j] > a.w);
                         } else {   // kp = position * 64 + the key token's other group
@@ -562,6 +624,47 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                         st[kb][4 * e4 + j] = ok ? st[kb][4 * e4 + j] : kNegInf;
                     }
                 }
+        }
+
+        // Soft-gated pass: for a tile with some pair further apart than the
+        // window, the group affinity a = g_key . g_row of every pair comes
+        // from three MFMAs on the bf16 hi/lo split (hi*hi + hi*lo + lo*hi),
+        // and far pairs get the gate sigmoid(lambda a) = 1 / (1 + 2^(-lambda
+        // log2(e) a)); pairs inside the window keep gate 1.
+        float gate[G::KB][16];
+        bool gated_tile = false;
+        if constexpr (GATED) {
+            const int q0 = tile * a.TT;
+            const int qlast = min(a.n, q0 + a.TT) - 1;
+            gated_tile = qlast - kt0 > a.w;
+            if (gated_tile) {
+                const bool all_far = q0 - (kt0 + BN - 1) > a.w;
+                const unsigned char* gkb = gk_lds + (bufp == buf0 ? 0 : BN * GROWB);
+#pragma unroll
+                for (int kb = 0; kb < G::KB; ++kb) {
+                    f32x16 at;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) at[e] = 0.0f;
+#pragma unroll
+                    for (int ks = 0; ks < KG / 16; ++ks) {
+                        const bf16x8 ghi =
+                            *reinterpret_cast<const bf16x8*>(gkb + kb * 32 * GROWB + goff[ks][0]);
+                        const bf16x8 glo =
+                            *reinterpret_cast<const bf16x8*>(gkb + kb * 32 * GROWB + goff[ks][1]);
+                        at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ghi, gq[ks][0], at, 0, 0, 0);
+                        at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ghi, gq[ks][1], at, 0, 0, 0);
+                        at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(glo, gq[ks][0], at, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
+                        const bool far = all_far || (pos_i - key > a.w);
+                        gate[kb][e] = far ? __builtin_amdgcn_rcpf(
+                                                1.0f + __builtin_amdgcn_exp2f(at[e] * a.nl2))
+                                          : 1.0f;
+                    }
+                }
+            }
         }
 
         // Online softmax with a lagging reference max m_ref. Probabilities
@@ -579,7 +682,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
+                    float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][e], a.sl2, -m_use));
+                    if constexpr (GATED) {
+                        if (gated_tile) p *= gate[kb][e];
+                    }
                     ps2[e & 1] += p;
                     pf[kb][e >> 3][e & 7] = (__bf16)p;
                 }
@@ -654,7 +760,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // (The long-range pass merges the window partial; the window pass never
     // merges, but keeping the path in its code gives both kernels a far
     // better register allocation at three workgroups per CU.)
-    if (PHASE != kDense && a.merge && rvalid) {
+    if (!CAUSAL_ALL && a.merge && rvalid) {
         const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
         const f32x2 le = a.lseg[row];
         if (le[0] != kNegInf) {
@@ -709,6 +815,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
 #pragma unroll
         for (int ks = 0; ks < G::KS; ++ks)
             qf[ks] = *reinterpret_cast<const bf16x8*>(a.q + qrow_off + 16 * ks + 8 * hh);
+    }
+
+    if constexpr (GATED) {
+        // the row's assignment fragments: columns 16*ks + 8*hh .. +8 of hi and lo
+        const uint16_t* gr = a.gs + ((int64_t)b * a.n + pos_i) * 2 * KG;
+#pragma unroll
+        for (int ks = 0; ks < KG / 16; ++ks)
+#pragma unroll
+            for (int part = 0; part < 2; ++part)
+                gq[ks][part] =
+                    *reinterpret_cast<const bf16x8*>(gr + part * KG + 16 * ks + 8 * hh);
     }
 
     // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
@@ -863,6 +980,23 @@ __global__ __launch_bounds__(256) void attn_merge_entries_kernel(
     if (c == 0 && lse) lse[row] = tot > 0.0f ? (lmax + __log2f(tot)) * kLn2 : kNegInf;
 }
 
+// Soft-gated pass operand: gs[t][0][k] = bf16(G[t][k]) (round to nearest
+// even), gs[t][1][k] = bf16(G[t][k] - gs[t][0][k]), zero for k >= K; one
+// thread per (token, column of KG).
+__global__ __launch_bounds__(256) void gate_split_kernel(const float* __restrict__ G,
+                                                         int64_t ntok, int K, int KG,
+                                                         uint16_t* __restrict__ gs) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= ntok * KG) return;
+    const int64_t t = x / KG;
+    const int k = (int)(x % KG);
+    const float g = k < K ? G[t * K + k] : 0.0f;
+    const __bf16 hi = (__bf16)g;
+    const __bf16 lo = (__bf16)(g - (float)hi);
+    gs[t * 2 * KG + k] = __builtin_bit_cast(uint16_t, hi);
+    gs[t * 2 * KG + KG + k] = __builtin_bit_cast(uint16_t, lo);
+}
+
 AttnArgs make_args(const AttnProblem& p) {
     AttnArgs a{};
     a.q = p.q;
@@ -991,6 +1125,27 @@ hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream) {
     // with a long-range part to come, the window result is a partial
     a.partial = attn_has_long_range(p.n, p.w) ? 1 : 0;
     return launch<kWindow>(a, p.d, stream);
+}
+
+hipError_t launch_attn_soft_gate(const AttnProblem& p, const float* G, float lambda,
+                                 hipStream_t stream) {
+    const int KG = soft_gate_columns(p.K);
+    uint16_t* gs = static_cast<uint16_t*>(p.workspace);
+    const int64_t threads = (int64_t)p.B * p.n * KG;
+    hipLaunchKernelGGL(gate_split_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       stream, G, (int64_t)p.B * p.n, p.K, KG, gs);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AttnProblem q = p;
+    q.workspace = nullptr;   // none of the two-pass buffers
+    AttnArgs a = make_args(q);
+    a.gs = gs;
+    a.nl2 = -lambda * 1.44269504088896340736f;
+    a.merge = 0;
+    a.partial = 0;
+    if (KG == 16) return launch<kSoftGate>(a, p.d, stream);
+    if (KG == 32) return launch<kSoftGate + 1>(a, p.d, stream);
+    return launch<kSoftGate + 2>(a, p.d, stream);
 }
 
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream) {

@@ -104,4 +104,14 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream);
 
+// Training-time soft-gated attention: every causal pair, far pairs weighted by
+// sigmoid(lambda g_i . g_j). Workspace: the bf16 hi/lo split of the soft
+// assignments G, [B][n][2][KG] with KG = K padded to 16, 32 or 64.
+inline int soft_gate_columns(int K) { return K <= 16 ? 16 : (K <= 32 ? 32 : 64); }
+inline size_t soft_gate_workspace(int B, int n, int K) {
+    return align_up((size_t)B * n * 4 * soft_gate_columns(K));
+}
+hipError_t launch_attn_soft_gate(const AttnProblem& p, const float* G, float lambda,
+                                 hipStream_t stream);
+
 }  // namespace focus

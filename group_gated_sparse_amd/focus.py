@@ -52,6 +52,9 @@ _SIGNATURES = {
     "focus_assign_scores": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
     "focus_sinkhorn_workspace_bytes": ([_i, _i, _i, _i], _sz),
     "focus_sinkhorn": ([_p, _i, _i, _i, _f, _i, _p, _p, _sz, _p], _i),
+    "focus_soft_gate_attn_workspace_bytes": ([_i, _i, _i], _sz),
+    "focus_soft_gate_attn_fwd": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _f, _p, _i, _p,
+                                  _p, _sz, _p], _i),
 }
 
 _lib = None
@@ -351,6 +354,44 @@ def dense_causal_attn_fwd(q, k, v, scale: float, *, out=None, out_dtype=torch.bf
     _check_status(lib().dense_causal_attn_fwd(_ptr(q), _ptr(k), _ptr(v), B, Hq, Hkv, n, d,
                                               float(scale), _ptr(out), dt, _ptr(lse),
                                               _stream(stream)))
+    return out, lse
+
+
+def focus_soft_gate_attn_workspace_bytes(B: int, n: int, K: int) -> int:
+    return int(lib().focus_soft_gate_attn_workspace_bytes(B, n, K))
+
+
+def focus_soft_gate_attn_fwd(q, k, v, G, window: int, scale: float, lam: float, *, out=None,
+                             out_dtype=torch.bfloat16, lse=None, want_lse: bool = False,
+                             workspace=None, stream=None):
+    """Training-time soft-gated attention: every causal pair; pairs beyond the
+    window weighted by sigmoid(lam * g_i . g_j) inside the softmax. G (B, n, K)
+    fp32 soft assignments. Returns (out, lse or None)."""
+    B, Hq, n, d = q.shape
+    Hkv = k.shape[1]
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16, (B, Hkv, n, d))
+    _need(v, "v", torch.bfloat16, (B, Hkv, n, d))
+    _need(G, "G", torch.float32)
+    if G.dim() != 3 or tuple(G.shape[:2]) != (B, n):
+        raise ValueError(f"G must have shape (B, n, K) = ({B}, {n}, K)")
+    K = G.shape[2]
+    if out is None:
+        out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    _need(out, "out", out.dtype, (B, Hq, n, d))
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (B, Hq, n))
+    ws = _workspace(focus_soft_gate_attn_workspace_bytes(B, n, K), q.device, workspace)
+    dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
+    _check_status(lib().focus_soft_gate_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(G), B, Hq, Hkv,
+                                                 n, d, K, window, float(scale), float(lam),
+                                                 _ptr(out), dt, _ptr(lse), _ptr(ws),
+                                                 0 if ws is None else ws.numel(),
+                                                 _stream(stream)))
     return out, lse
 
 

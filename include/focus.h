@@ -263,6 +263,33 @@ focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t*
                                               focus_stream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Training-time soft-gated attention (Japanese page §2.1: group affinity
+ * a_ij = g_i . g_j of the soft assignments and the gate sigmoid(lambda a_ij);
+ * §2.2: while training the gate is soft and every pair is computed, O(n^2);
+ * Korean page §2.1: the local window is attended at full resolution and the
+ * softmax is kept exact). The pages' "product of the local mask and the
+ * gate" is read as: pairs inside the causal window pass unchanged and pairs
+ * beyond it are scaled by the gate, inside one renormalised softmax:
+ *
+ *   gate_ij = 1 for 0 <= i - j <= window, sigmoid(lambda * a_ij) for i - j > window
+ *   out[b][h][i] = sum_{j <= i} gate_ij exp(scale q_i.k_j) v_j / sum_{j <= i} gate_ij exp(scale q_i.k_j)
+ *   lse[b][h][i] = log sum_{j <= i} gate_ij exp(scale q_i.k_j)
+ *
+ * G [B][n][K] fp32 soft assignments (e.g. the rows of focus_sinkhorn's
+ * output; any values are accepted), shared by all heads of a token. The
+ * affinity is computed from a bf16 hi/lo split of G (about 2^-16 relative).
+ * Other arguments and layouts as dense_causal_attn_fwd; lambda finite (any
+ * sign). Workspace: focus_soft_gate_attn_workspace_bytes() bytes (the split
+ * copy of G). Limits: 1 <= K <= 64, d_head in {32, 64, 128}.
+ * ---------------------------------------------------------------------- */
+size_t focus_soft_gate_attn_workspace_bytes(int B, int n, int K);
+focus_status focus_soft_gate_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      const float* G, int B, int Hq, int Hkv, int n, int d_head,
+                                      int K, int window, float scale, float lambda, void* out,
+                                      focus_dtype out_dtype, float* lse, void* workspace,
+                                      size_t workspace_bytes, focus_stream_t stream);
+
+/* ------------------------------------------------------------------------
  * Baseline: plain causal attention (every pair j <= i), the "full attention"
  * the Focus pages compare against. Same layouts and limits as above; needs no
  * workspace.

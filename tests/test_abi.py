@@ -40,7 +40,7 @@ def test_header_is_plain_c():
 def test_library_exports_every_declared_symbol():
     lib = focus.lib()
     names = declared_functions()
-    assert len(names) >= 18
+    assert len(names) >= 20
     out = subprocess.check_output(["nm", "-D", "--defined-only", focus.LIB_PATH], text=True)
     exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
     for name in names:
@@ -280,6 +280,44 @@ def test_sinkhorn_workspace_size():
     # 1M rows: 512-row workgroups, 2048 of them
     assert lib.focus_sinkhorn_workspace_bytes(1, 1 << 20, 64, 10) == 256 + 2048 * 64 * 4
     assert lib.focus_sinkhorn_workspace_bytes(1, 100, 0, 5) == 0
+
+
+def _sg(**kw):
+    args = dict(q=A, k=Bp, v=C_, G=D_, B=1, Hq=4, Hkv=2, n=256, d=64, K=8, w=16, scale=0.125,
+                lam=4.0, out=G_, dt=0, lse=None, ws=H_, wsb=1 << 20, stream=None)
+    args.update(kw)
+    return focus.lib().focus_soft_gate_attn_fwd(
+        args["q"], args["k"], args["v"], args["G"], args["B"], args["Hq"], args["Hkv"], args["n"],
+        args["d"], args["K"], args["w"], args["scale"], args["lam"], args["out"], args["dt"],
+        args["lse"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(G=None), INVALID, "G"),
+    (dict(G=D_ + 2), INVALID, "aligned"),
+    (dict(lam=float("nan")), INVALID, "lambda"),
+    (dict(lam=float("inf")), INVALID, "lambda"),
+    (dict(K=0), UNSUPPORTED, "K"),
+    (dict(K=65), UNSUPPORTED, "K"),
+    (dict(d=48), UNSUPPORTED, "d_head"),
+    (dict(q=None), INVALID, "q"),
+    (dict(scale=0.0), INVALID, "scale"),
+    (dict(out=D_), INVALID, "overlap"),
+    (dict(ws=None), WORKSPACE, "workspace"),
+    (dict(wsb=64), WORKSPACE, "too small"),
+])
+def test_soft_gate_rejects(kw, code, msg):
+    assert _sg(**kw) == code
+    assert msg in _err()
+
+
+def test_soft_gate_workspace_size():
+    lib = focus.lib()
+    # bf16 hi and lo rows of the assignments, K padded to 16 / 32 / 64
+    assert lib.focus_soft_gate_attn_workspace_bytes(1, 256, 8) == 256 * 4 * 16
+    assert lib.focus_soft_gate_attn_workspace_bytes(2, 1000, 20) == 2 * 1000 * 4 * 32
+    assert lib.focus_soft_gate_attn_workspace_bytes(1, 100, 33) == 25600
+    assert lib.focus_soft_gate_attn_workspace_bytes(1, 100, 65) == 0
 
 
 def test_assign_scores_rejects():
