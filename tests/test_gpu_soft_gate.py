@@ -46,6 +46,10 @@ CASES = [
     ("k64_d32", 1, 2, 1, 300, 32, 64, 7, 3.0),
     ("k33_d64_many_tiles", 2, 3, 3, 1100, 64, 33, 100, 9.0),
     ("wide_window", 1, 2, 2, 150, 128, 16, 149, 7.0),
+    # four and eight heads per workgroup: gates shared between waves
+    ("k16_g4_d64", 1, 8, 2, 400, 64, 16, 20, 6.0),
+    ("k8_g8_d32", 1, 8, 1, 300, 32, 8, 10, 4.0),
+    ("k64_g8_d128", 1, 8, 1, 450, 128, 64, 33, 15.0),
 ]
 
 
