@@ -93,6 +93,12 @@ def measured_traffic(workload, kernel):
     return value if sha == h.hexdigest() else None
 
 
+def device_info(torch):
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""),
+            "compute_units": p.multi_processor_count}
+
+
 def cpu_baseline(x, wl, target_s):
     """The oracle as it stands, on the host cores: full assignment and group
     sort, attention on a random row sample extrapolated per visited pair."""
@@ -446,6 +452,7 @@ def main():
              "long_range_merge": span(3, 4)}
     ev_step = span(0, 4)
     ms_step = max(wall_ms, ev_step)
+    per_step = sorted(evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps))
     log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
 
     gids = ids.cpu().numpy()
@@ -480,6 +487,9 @@ def main():
         "long_range_pairs_per_head": lr,
         "long_range_pairs_visited_per_head": lr_visited,
         "phase_ms": phase,
+        "step_ms_stats": {"median": float(np.median(per_step)), "min": per_step[0],
+                          "max": per_step[-1]},
+        "device": device_info(torch),
         "attn_ms": attn_ms,
         "attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
         "attn_frac_of_bf16_peak": flops / (attn_ms * 1e-3) / 1e12 / metrics.MI355X_BF16_DENSE_TFLOPS,

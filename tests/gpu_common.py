@@ -30,14 +30,21 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
-def sample_rows(rng, B, Hq, n, w, per_head=48, heads=None):
-    """Flattened (b*Hq+h)*n+i rows: the start, the window edge, the end and random rows."""
+def sample_rows(rng, B, Hq, n, w, per_head=48, heads=None, ids=None):
+    """Flattened (b*Hq+h)*n+i rows: the start, the window edge, the end and random rows;
+    with ids (B, n) or (B, n, m) also the first and last token of every group."""
     heads = range(Hq) if heads is None else heads
     fixed = {0, 1, min(n - 1, max(0, w - 1)), min(n - 1, w), min(n - 1, w + 1), n - 2, n - 1}
     rows = []
     for b in range(B):
+        edges = set()
+        if ids is not None:
+            ib = np.asarray(ids[b]).reshape(n, -1)
+            for g in np.unique(ib):
+                pos = np.nonzero((ib == g).any(axis=1))[0]
+                edges |= {int(pos[0]), int(pos[-1])}
         for h in heads:
-            picks = set(i for i in fixed if 0 <= i < n)
+            picks = set(i for i in fixed if 0 <= i < n) | edges
             picks |= set(rng.integers(0, n, size=min(per_head, n)).tolist())
             rows += [(b * Hq + h) * n + i for i in sorted(picks)]
     return np.array(rows, dtype=np.int64)

@@ -273,7 +273,9 @@ def test_whole_path_full_size_sampled(wl):
     rperm, roffs = oracle.group_sort(gids, K)
     assert np.array_equal(host(perm), rperm) and np.array_equal(host(offs), roffs)
 
-    rows = sample_rows(rng, B, Hq, n, w, per_head=max(16, 2048 // Hq))
+    # at least 8192 rows: every head, rows 0 .. w edges, the last rows, the
+    # first and last token of every group, and random rows
+    rows = sample_rows(rng, B, Hq, n, w, per_head=max(16, 8192 // Hq), ids=gids)
     ref, rlse, _ = oracle.attn(x["q"], x["k"], x["v"], gids, w, wl.softmax_scale, rows=rows)
     got16 = host(out.float()).reshape(-1, d)[rows]
     check_attn(got16, ref.reshape(-1, d), f"{wl.name} bf16 out", bf16_out=True)

@@ -276,7 +276,7 @@ def test_whole_path_top2_full_size_sampled(wl):
     rperm, roffs = oracle.group_sort_multi(gids, K)
     assert np.array_equal(host(perm), rperm) and np.array_equal(host(offs), roffs)
 
-    rows = sample_rows(rng, B, Hq, n, w, per_head=max(16, 1024 // Hq))
+    rows = sample_rows(rng, B, Hq, n, w, per_head=max(16, 4096 // Hq), ids=gids)
     ref, rlse, _ = oracle.attn_multi(x["q"], x["k"], x["v"], gids, w, wl.softmax_scale, rows=rows)
     check_attn(host(out.float()).reshape(-1, d)[rows], ref.reshape(-1, d),
                f"{wl.name} bf16 out", bf16_out=True)
