@@ -13,7 +13,9 @@
 //   pass p (p = 0 .. iters):  u[t] = 1 / sum_k A[t][k] v[k]     (v = 1 at p = 0)
 //     p < iters:  column partial sums sum_t A[t][k] u[t] per workgroup; a
 //                 small kernel then adds them (fixed order) and writes
-//                 v[k] = (n / K) / column sum for the next pass
+//                 v[k] = (n / K) / column sum for the next pass, or, when
+//                 there are few workgroups, each workgroup of the next pass
+//                 adds them itself in the same fixed order
 //     p = iters:  G[t][k] = A[t][k] u[t] v[k]
 //
 // A row's K scores sit in lpr lanes, four per lane when K is a multiple of
@@ -75,12 +77,46 @@ struct SinkArgs {
     const float* S;      // scores [B][n][K]
     float* G;            // output [B][n][K]
     const float* v;      // column scales [B][K] from the previous round
-    float* partial;      // column sums per workgroup [B][nblk][K]
+    float* partial;      // column sums per workgroup, two buffers [2][B][nblk][K]
+                         // (pass p writes buffer p % 2)
     int n, K, lpr, rpb, nblk, iters;
+    int fused;           // each workgroup adds the previous pass's sums itself
     float sl2;           // log2(e) / tau
+    float target;        // n / K
 };
 
+// Column totals of rows [0, J) of a [J][K] array in a fixed order: thread
+// (g, k) of ng = 256 / K groups adds rows g, g + ng, ... into eight running
+// sums (eight loads in flight), then the groups are added in order; returns
+// the total of column tid for tid < K. Every caller gets the same bits.
+__device__ float column_totals(const float* arr, int J, int K, float* gsum) {
+    const int tid = threadIdx.x;
+    const int ng = NT / K;
+    const int g = tid / K, k = tid % K;
+    float acc = 0.0f;
+    if (g < ng) {
+        float p8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int j = g;
+        for (; j + 7 * ng < J; j += 8 * ng) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) p8[q] += arr[(int64_t)(j + q * ng) * K + k];
+        }
+        float tail = 0.0f;
+        for (; j < J; j += ng) tail += arr[(int64_t)j * K + k];
+        acc = (((p8[0] + p8[1]) + (p8[2] + p8[3])) + ((p8[4] + p8[5]) + (p8[6] + p8[7]))) + tail;
+    }
+    gsum[tid] = acc;
+    __syncthreads();
+    float tot = 0.0f;
+    if (tid < K)
+        for (int j = 0; j < ng; ++j) tot += gsum[j * K + tid];
+    return tot;
+}
+
 constexpr int UNROLL = 8;   // row chunks in flight per wave
+// Per-workgroup column sums (workgroups x K) up to which each workgroup of
+// the next pass adds them itself instead of a separate reduce launch.
+constexpr int64_t kFuseMaxSums = 16384;
 
 // VPL scores per lane: 1, or 4 (one 16-byte load) when K is a multiple of
 // 4; a row then spans lpr = next power of two >= K / VPL lanes.
@@ -94,10 +130,22 @@ __global__ __launch_bounds__(NT) void sinkhorn_pass_kernel(SinkArgs a, int pass)
     const int c = lane & (lpr - 1);          // this lane's scores: columns VPL*c .. VPL*c + VPL-1
     const bool cvalid = VPL * c < a.K;
     const bool final_pass = pass == a.iters;
+    const size_t pstride = (size_t)gridDim.y * a.nblk * a.K;   // one partial buffer
+    const float* vsrc = a.v + (int64_t)b * a.K;
+    if (a.fused && pass > 0) {
+        // this workgroup adds the previous pass's per-workgroup sums itself
+        // (same order in every workgroup, so every copy of v is identical)
+        __shared__ float gsum[NT];
+        __shared__ float vsh[64];
+        const float* prev = a.partial + ((pass - 1) & 1) * pstride + (int64_t)b * a.nblk * a.K;
+        const float tot = column_totals(prev, a.nblk, a.K, gsum);
+        if (tid < a.K) vsh[tid] = tot > 0.0f ? a.target / tot : 0.0f;
+        __syncthreads();
+        vsrc = vsh;
+    }
     float vc[VPL];
 #pragma unroll
-    for (int j = 0; j < VPL; ++j)
-        vc[j] = (pass == 0 || !cvalid) ? 1.0f : a.v[(int64_t)b * a.K + VPL * c + j];
+    for (int j = 0; j < VPL; ++j) vc[j] = (pass == 0 || !cvalid) ? 1.0f : vsrc[VPL * c + j];
     const float* Sb = a.S + (int64_t)b * a.n * a.K;
     const int r0 = blk * a.rpb, r1 = min(a.n, r0 + a.rpb);
     float colacc[VPL];
@@ -157,7 +205,7 @@ __global__ __launch_bounds__(NT) void sinkhorn_pass_kernel(SinkArgs a, int pass)
     }
     __syncthreads();
     if (tid < a.K)
-        a.partial[((int64_t)b * a.nblk + blk) * a.K + tid] =
+        a.partial[(pass & 1) * pstride + ((int64_t)b * a.nblk + blk) * a.K + tid] =
             ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
 }
 
@@ -198,7 +246,7 @@ SinkhornLayout sinkhorn_layout(int B, int n, int K, int iters) {
     L.nblk = (n + L.rpb - 1) / L.rpb;
     size_t off = 0;
     L.v = off;       off += align_up((size_t)B * K * 4);
-    L.partial = off; off += align_up((size_t)B * L.nblk * K * 4);
+    L.partial = off; off += 2 * align_up((size_t)B * L.nblk * K * 4);
     L.total = off;
     return L;
 }
@@ -226,6 +274,11 @@ hipError_t launch_sinkhorn(const float* scores, int B, int n, int K, float tau, 
     a.iters = iters;
     a.sl2 = 1.44269504088896340736f / tau;
     const float target = (float)n / (float)K;
+    a.target = target;
+    // few enough per-workgroup sums: every workgroup of the next pass adds
+    // them itself, which saves the reduce launch of each round
+    a.fused = (int64_t)L.nblk * K <= kFuseMaxSums;
+    const size_t pstride = (size_t)B * L.nblk * K;
     const dim3 grid((unsigned)L.nblk, (unsigned)B);
     for (int p = 0; p <= iters; ++p) {
         if (vpl == 4)
@@ -234,9 +287,9 @@ hipError_t launch_sinkhorn(const float* scores, int B, int n, int K, float tau, 
             hipLaunchKernelGGL(sinkhorn_pass_kernel<1>, grid, dim3(NT), 0, stream, a, p);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        if (p == iters) break;
+        if (p == iters || a.fused) continue;
         hipLaunchKernelGGL(sinkhorn_reduce_kernel, dim3((unsigned)K, (unsigned)B), dim3(NT), 0,
-                           stream, a.partial, L.nblk, K, target, v);
+                           stream, a.partial + (p & 1) * pstride, L.nblk, K, target, v);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

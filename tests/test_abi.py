@@ -273,12 +273,12 @@ def test_sinkhorn_rejects(kw, code, msg):
 
 def test_sinkhorn_workspace_size():
     lib = focus.lib()
-    # column scales [B][K] + per-workgroup column sums [B][nblk][K] (128 rows per
-    # workgroup, at most 2048 workgroups), each region 256-byte aligned
-    assert lib.focus_sinkhorn_workspace_bytes(1, 100, 8, 5) == 2 * 256
-    assert lib.focus_sinkhorn_workspace_bytes(2, 32768, 32, 10) == 256 + 2 * 256 * 32 * 4
+    # column scales [B][K] + two buffers of per-workgroup column sums [B][nblk][K]
+    # (128 rows per workgroup, at most 2048 workgroups), each region 256-byte aligned
+    assert lib.focus_sinkhorn_workspace_bytes(1, 100, 8, 5) == 3 * 256
+    assert lib.focus_sinkhorn_workspace_bytes(2, 32768, 32, 10) == 256 + 2 * (2 * 256 * 32 * 4)
     # 1M rows: 512-row workgroups, 2048 of them
-    assert lib.focus_sinkhorn_workspace_bytes(1, 1 << 20, 64, 10) == 256 + 2048 * 64 * 4
+    assert lib.focus_sinkhorn_workspace_bytes(1, 1 << 20, 64, 10) == 256 + 2 * (2048 * 64 * 4)
     assert lib.focus_sinkhorn_workspace_bytes(1, 100, 0, 5) == 0
 
 

@@ -110,3 +110,20 @@ def test_soft_gate_full_size_sampled():
                                       8.0, rows=rows)
     check_attn(host(out).reshape(-1, wl.d)[rows], ref.reshape(-1, wl.d), f"{wl.name} soft gate")
     assert np.max(np.abs(host(lse).ravel()[rows] - rlse)) < 1e-3
+
+
+def test_soft_gate_deterministic_and_workspace_reusable():
+    say("[soft gate] determinism")
+    rng = np.random.default_rng(43)
+    B, Hq, Hkv, n, d, K = 1, 8, 2, 900, 128, 20
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    G = _soft(rng, B, n, K)
+    tq, tk, tv, tG = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(G)
+    ws = torch.empty(focus.focus_soft_gate_attn_workspace_bytes(B, n, K), dtype=torch.uint8,
+                     device="cuda")
+    a, la = focus.focus_soft_gate_attn_fwd(tq, tk, tv, tG, 40, 0.09, 6.0, workspace=ws,
+                                           out_dtype=torch.float32, want_lse=True)
+    b, lb = focus.focus_soft_gate_attn_fwd(tq, tk, tv, tG, 40, 0.09, 6.0, workspace=ws,
+                                           out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(la, lb)

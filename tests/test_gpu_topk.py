@@ -282,3 +282,23 @@ def test_whole_path_top2_full_size_sampled(wl):
                f"{wl.name} bf16 out", bf16_out=True)
     check_attn(host(out32).reshape(-1, d)[rows], ref.reshape(-1, d), f"{wl.name} fp32 out")
     assert np.max(np.abs(host(lse).ravel()[rows] - rlse.ravel())) < 1e-3
+
+
+def test_topk_deterministic_and_stream_independent():
+    say("[attn top-k] determinism / non-default stream")
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, n, d, K, m, w = 1, 8, 1, 1500, 128, 6, 2, 64
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = _member_ids(rng, B, n, K, m)
+    a = _run_topk(q, k, v, ids, K, m, w, 0.09)
+    b = _run_topk(q, k, v, ids, K, m, w, 0.09)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        tq, tk, tv, tid = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(ids)
+        perm, offs = focus.focus_group_sort(tid, K, stream=s)
+        out, lse = focus.focus_attn_topk_fwd(tq, tk, tv, tid, perm, offs, K, m, w, 0.09,
+                                             out_dtype=torch.float32, want_lse=True, stream=s)
+    s.synchronize()
+    c = (host(out), host(lse))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1], c[1])
