@@ -146,6 +146,12 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
         REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
         REQUIRE(ws_bytes >= need, FOCUS_ERR_WORKSPACE,
                 "workspace too small: %zu bytes given, %zu required", ws_bytes, need);
+        const size_t qbytes = (size_t)B * Hq * n * d * 2, kvbytes = (size_t)B * Hkv * n * d * 2;
+        const size_t obytes = (size_t)B * Hq * n * d * (out_dtype == FOCUS_F32 ? 4 : 2);
+        REQUIRE(!overlaps(workspace, need, q, qbytes) && !overlaps(workspace, need, k, kvbytes) &&
+                    !overlaps(workspace, need, v, kvbytes) &&
+                    !overlaps(workspace, need, out, obytes),
+                FOCUS_ERR_INVALID_ARGUMENT, "workspace must not overlap q, k, v or out");
     }
     focus::AttnProblem p{q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n, d, K, w, scale,
                          out, out_dtype == FOCUS_F32 ? 1 : 0, lse, need > 0 ? workspace : nullptr,

@@ -194,6 +194,7 @@ def _attn(fn="focus_attn_fwd", **kw):
     (dict(lse=G_ + 64), INVALID, "overlap"),
     (dict(ws=None), WORKSPACE, "workspace"),
     (dict(wsb=1024), WORKSPACE, "too small"),
+    (dict(ws=A + 4096), INVALID, "workspace must not overlap"),
 ])
 def test_attn_rejects(fn, kw, code, msg):
     assert _attn(fn, **kw) == code
