@@ -81,6 +81,7 @@ struct AttnArgs {
     const int32_t* perm;
     const int32_t* offsets;
     const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
+    const int32_t* order;   // long-range pass: sorted query tiles, most work first [B][ntiles]
     int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
     _Float16* og;           // window partial [B][Hq][n][D]: O * 2^-e in fp16 (|.| < 1)
     f32x2* lseg;            // per row (log2-sum-exp L or -inf: no key, e)
@@ -280,7 +281,16 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
     const int nseg = gl - gf + 1;
     int32_t* rec = plan + ((int64_t)b * ntiles + tile) * PLAN_INTS;
     if (nseg > SEGCAP) {
+        // too many groups for the record: the attention kernel derives the
+        // segments itself; only the tile's total work is kept (for the order)
+        int run = 0;
+        for (int t = 0; t < nseg; ++t) {
+            int ob, kend, kfull;
+            segment_range(perm_b, offb, ne, m, w, s0, s1, gf + t, ob, kend, kfull);
+            run += (kend - ob + bn_keys - 1) / bn_keys;
+        }
         rec[0] = -1;
+        rec[3] = run;
         return;
     }
     int run = 0;
@@ -298,6 +308,57 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
     rec[1] = gf;
     rec[2] = (s0 >= ob0 && s1 <= oe0) ? 1 : 0;
     rec[3] = run;
+}
+
+// Order in which the long-range pass takes the sorted query tiles of one
+// batch element: by decreasing work class (1 + floor(log2(key tiles)), 0 for
+// none), then by tile index; so the longest tiles start first and the
+// grid's tail is made of short ones. One workgroup per batch element: each
+// thread counts the classes of a contiguous chunk of tiles, the counts are
+// scanned per class, and every thread writes its chunk in order (stable,
+// deterministic).
+constexpr int ORDER_CLASSES = 17;
+__device__ __forceinline__ int work_class(int work) {
+    return work <= 0 ? 0 : min(ORDER_CLASSES - 1, 32 - __clz(work));
+}
+__global__ __launch_bounds__(256) void attn_order_kernel(const int32_t* __restrict__ plan,
+                                                         int ntiles,
+                                                         int32_t* __restrict__ order) {
+    __shared__ int cnt[ORDER_CLASSES][256];
+    __shared__ int base[ORDER_CLASSES];
+    const int b = blockIdx.x, tid = threadIdx.x;
+    const int chunk = (ntiles + 255) / 256;
+    const int t0 = min(ntiles, tid * chunk), t1 = min(ntiles, t0 + chunk);
+    const int32_t* pb = plan + (int64_t)b * ntiles * PLAN_INTS;
+    for (int c = 0; c < ORDER_CLASSES; ++c) cnt[c][tid] = 0;
+    for (int t = t0; t < t1; ++t) ++cnt[work_class(pb[(int64_t)t * PLAN_INTS + 3])][tid];
+    __syncthreads();
+    if (tid < ORDER_CLASSES) {
+        // exclusive prefix over threads, per class
+        int run = 0;
+        for (int j = 0; j < 256; ++j) {
+            const int x = cnt[tid][j];
+            cnt[tid][j] = run;
+            run += x;
+        }
+        base[tid] = run;   // class total for now
+    }
+    __syncthreads();
+    if (tid == 0) {
+        // classes from the highest down
+        int run = 0;
+        for (int c = ORDER_CLASSES - 1; c >= 0; --c) {
+            const int tot = base[c];
+            base[c] = run;
+            run += tot;
+        }
+    }
+    __syncthreads();
+    int32_t* ob = order + (int64_t)b * ntiles;
+    for (int t = t0; t < t1; ++t) {
+        const int c = work_class(pb[(int64_t)t * PLAN_INTS + 3]);
+        ob[base[c] + cnt[c][tid]++] = t;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -341,7 +402,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     rest /= a.nslices;
     int kvh = rest % a.Hkv;
     int b = rest / a.Hkv;
-    if (SORTED) tile = a.ntiles - 1 - tile;  // heavier sorted tiles first
+    if (SORTED) tile = clampi(a.order[(int64_t)b * a.ntiles + tile], 0, a.ntiles - 1);
     tile = __builtin_amdgcn_readfirstlane(tile);
     slice = __builtin_amdgcn_readfirstlane(slice);
     kvh = __builtin_amdgcn_readfirstlane(kvh);
@@ -1028,6 +1089,7 @@ AttnArgs make_args(const AttnProblem& p) {
         a.og = reinterpret_cast<_Float16*>(base + ws.og);
         a.lseg = reinterpret_cast<f32x2*>(base + ws.lseg);
         a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
+        a.order = reinterpret_cast<const int32_t*>(base + ws.order);
         a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
     }
     return a;
@@ -1078,6 +1140,10 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
                        p.ids, p.perm, p.offsets, a.ne, p.m, p.K, p.w, a.TT, a.ntiles,
                        attn_tile_keys(p.d, kLongRange),
                        const_cast<int32_t*>(a.plan));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_order_kernel, dim3(p.B), dim3(256), 0, stream, a.plan, a.ntiles,
+                       const_cast<int32_t*>(a.order));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.k = ks;
