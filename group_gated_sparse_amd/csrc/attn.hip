@@ -58,6 +58,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;      // threads per workgroup
 constexpr int ROWS = 128;    // query rows per workgroup (4 waves x 32)
@@ -417,7 +418,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // entry of the row (sorted passes: perm holds entries t*m + c; m = 1
     // makes the entry the position) and its sequence position
     int ent_i = rvalid ? s_row : 0;
-    if (SORTED && rvalid) ent_i = clampi(a.perm[bne + s_row], 0, ne - 1);
+    // Sorted passes: every row loads its entry (rows past the end take the
+    // last slot's, a valid position they never store to), so the load sits
+    // in no branch that would wait for it on its own.
+    if (SORTED) ent_i = clampi(a.perm[bne + min(s_row, ne - 1)], 0, ne - 1);
+    // Sorted passes: the tile's plan record, loaded beside the perm entry so
+    // that the two round trips overlap. Lane l < 8 of every wave holds ints
+    // 4l .. 4l+3: lane 0 the header, lane t + 1 segment t.
+    i32x4 prec = {0, 0, 0, 0};
+    if (SORTED)
+        prec = *reinterpret_cast<const i32x4*>(a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS +
+                                              4 * (lane & 7));
     const int pos_i = MULTI ? (ent_i >> 1) : ent_i;
     // multi pass: the row token's other group
     const int oth_i = (MULTI && rvalid) ? clampi(a.ids[bne + (ent_i ^ 1)], 0, a.K - 1) : 0;
@@ -441,24 +452,24 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     } else {
         const int s0 = tile * a.TT;
         const int s1 = min(ne, s0 + a.TT);
-        const int32_t* rec = a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS;
         if (hh == 0) rowpos[R] = ent_i;  // published by the barrier below
         if (MULTI && tid == 0) excl_any = 0;
-        // plan values are uniform: readfirstlane keeps them in scalar registers
-        int nseg = __builtin_amdgcn_readfirstlane(rec[0]);
+        // the header is uniform: readlane keeps it in scalar registers
+        int nseg = __builtin_amdgcn_readlane(prec[0], 0);
         if (nseg >= 0) {
             nseg = min(nseg, SEGCAP);
-            gfirst = clampi(__builtin_amdgcn_readfirstlane(rec[1]), 0, a.K - 1);
-            rows_one_group = __builtin_amdgcn_readfirstlane(rec[2]) != 0;
-            if (tid < nseg) {
-                const int ob = clampi(rec[4 + 4 * tid], 0, ne);
-                const int kend = clampi(rec[5 + 4 * tid], ob, ne);
-                seg_ob[tid] = ob;
-                seg_kend[tid] = kend;
-                seg_t0[tid] = rec[6 + 4 * tid];
-                seg_kfull[tid] = clampi(rec[7 + 4 * tid], ob, kend);
+            gfirst = clampi(__builtin_amdgcn_readlane(prec[1], 0), 0, a.K - 1);
+            rows_one_group = __builtin_amdgcn_readlane(prec[2], 0) != 0;
+            const int t = lane - 1;   // segment held by this lane
+            if (wave == 0 && t >= 0 && t < nseg) {
+                const int ob = clampi(prec[0], 0, ne);
+                const int kend = clampi(prec[1], ob, ne);
+                seg_ob[t] = ob;
+                seg_kend[t] = kend;
+                seg_t0[t] = prec[2];
+                seg_kfull[t] = clampi(prec[3], ob, kend);
             }
-            if (tid == 0) seg_t0[nseg] = rec[3];
+            if (tid == 0) seg_t0[nseg] = prec[3];
             __syncthreads();
         } else {
             // More groups in this tile than a plan record holds: derive the
@@ -507,23 +518,37 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         }
     }
 
+    // Sorted passes: a cursor over the segments, with the current segment's
+    // values held in scalar registers (first and end tile, first key slot,
+    // end of valid slots, end of the slots every row keeps); it is reloaded
+    // from LDS only when a tile crosses into the next segment.
+    struct SegCursor {
+        int seg, t0, t1, ob, kend, kfull;
+    };
+    auto seg_load = [&](SegCursor& c) {
+        // segment values are uniform (LDS, written by one thread each)
+        c.t0 = __builtin_amdgcn_readfirstlane(seg_t0[c.seg]);
+        c.t1 = __builtin_amdgcn_readfirstlane(seg_t0[c.seg + 1]);
+        c.ob = __builtin_amdgcn_readfirstlane(seg_ob[c.seg]);
+        c.kend = __builtin_amdgcn_readfirstlane(seg_kend[c.seg]);
+        c.kfull = __builtin_amdgcn_readfirstlane(seg_kfull[c.seg]);
+    };
     // Tile tau -> (segment, first key slot, end of valid slots, all pairs kept).
-    auto locate = [&](int tau, int& seg, int& kt0, int& kend, bool& full) {
+    auto locate = [&](int tau, SegCursor& c, int& kt0, int& kend, bool& full) {
         if (!SORTED) {
-            seg = 0;
             kt0 = kstart + tau * BN;
             kend = kend0;
             const int q0 = tile * a.TT;
             full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
                    (CAUSAL_ALL || kend - 1 - kt0 <= a.w);
         } else {
-            // segment values are uniform (LDS, written by one thread each)
-            while (__builtin_amdgcn_readfirstlane(seg_t0[seg + 1]) <= tau) ++seg;
-            kt0 = __builtin_amdgcn_readfirstlane(seg_ob[seg]) +
-                  (tau - __builtin_amdgcn_readfirstlane(seg_t0[seg])) * BN;
-            kend = __builtin_amdgcn_readfirstlane(seg_kend[seg]);
-            full = rows_one_group && !rows_excl &&
-                   (kt0 + BN <= __builtin_amdgcn_readfirstlane(seg_kfull[seg]));
+            while (c.t1 <= tau) {
+                ++c.seg;
+                seg_load(c);
+            }
+            kt0 = c.ob + (tau - c.t0) * BN;
+            kend = c.kend;
+            full = rows_one_group && !rows_excl && (kt0 + BN <= c.kfull);
         }
     };
 
@@ -540,7 +565,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         lane_off[i] = crow * G::ROWB + logical_chunk<D>(crow, (o % G::ROWB) / 16) * 16;
     }
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);   // wave index in a scalar register
-    int seg_issue = 0, seg_cur = 0;
+    SegCursor seg_issue = {0, 0, 0, 0, 0, 0};
+    if (SORTED && ntl > 0) seg_load(seg_issue);
+    SegCursor seg_cur = seg_issue;
     // soft-gated pass: this lane's share of the assignment-row copies (1 KB
     // copies wave, wave + 4, ...): key row within the tile and logical chunk
     constexpr int GCPW = (GNC + 3) / 4;
@@ -576,8 +603,13 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             }
         }
         // positions of the tile's key slots, for the mask of a partial tile
-        if (SORTED && !full && wave == 0)
-            copy16(a.spos + (int64_t)b * (ne + KPOS_PAD) + kt0 + 4 * lane, kposp);
+        // (a scalar base plus a 32-bit lane offset, like the tile copies: a
+        // per-lane 64-bit pointer here would be kept across the loop, spilled,
+        // and its reload would wait for the copies issued just before it)
+        if (SORTED && !full && wave == 0) {
+            const char* sp = reinterpret_cast<const char*>(a.spos + (int64_t)b * (ne + KPOS_PAD));
+            copy16(sp + (uint32_t)(4 * kt0 + 16 * lane), kposp);
+        }
         if constexpr (GATED) {
             // the key tile's assignment rows (hi and lo), row-clamped at the end
             unsigned char* gd = gk_lds + (bufp == buf0 ? 0 : BN * GROWB);
@@ -660,7 +692,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         // 8*(e>>2) + 4*hh + (e&3) of its row.
         // (branch-free: every condition is evaluated, combined with &)
         if (!full) {
-            const bool row_ok = !SORTED || g_i == gfirst + seg_cur;
+            const bool row_ok = !SORTED || g_i == gfirst + seg_cur.seg;
 #pragma unroll
             for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
@@ -816,29 +848,54 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // partial is stored as O~ = O * 2^-e (fp16, |O~| < 1) with the row's
     // log2-sum-exp L and e; (acc = O~, l = 2^-e, reference max = L + e) is
     // exactly the state that result stands for, so this pass's keys
-    // accumulate on top of it and the final normalisation merges both parts;
-    // the loads share the round trip of the Q rows and the first K/V tile.
-    // (The long-range pass merges the window partial; the window pass never
-    // merges, but keeping the path in its code gives both kernels a far
-    // better register allocation at three workgroups per CU.)
-    if (!CAUSAL_ALL && a.merge && rvalid) {
+    // accumulate on top of it and the final normalisation merges both parts.
+    // The sorted passes load the partial rows whatever (L, e) holds (the
+    // window pass writes every row), so their round trip overlaps that of
+    // (L, e), the Q rows and the first K/V tile, and take them into the
+    // state once the loads are back. (The window pass never merges, but
+    // keeping the plain form of this code in it gives it a far better
+    // register allocation at three workgroups per CU.)
+    const bool merging = !CAUSAL_ALL && a.merge && rvalid;
+    f32x2 le_in = {kNegInf, 0.0f};
+    f16x4 part_in[G::DB][4];
+    auto set_state = [&](int db, int i, f16x4 gv) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[db][4 * i + j] = (float)gv[j];
+    };
+    auto set_scale = [&]() {
+        m_ref = le_in[0] + le_in[1];
+        // halves are summed at the end
+        l_run = (hh == 0) ? __builtin_ldexpf(1.0f, -(int)le_in[1]) : 0.0f;
+    };
+    if (merging) {
         const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
-        const f32x2 le = a.lseg[row];
-        if (le[0] != kNegInf) {
-            const _Float16* grow_p = a.og + row * D;
+        le_in = a.lseg[row];
+        const _Float16* grow_p = a.og + row * D;
+        if (SORTED || le_in[0] != kNegInf) {
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const f16x4 gv = *reinterpret_cast<const f16x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[db][4 * i + j] = (float)gv[j];
+                    const f16x4 gv =
+                        *reinterpret_cast<const f16x4*>(grow_p + db * 32 + 8 * i + 4 * hh);
+                    if (SORTED) {
+                        part_in[db][i] = gv;
+                    } else {
+                        set_state(db, i, gv);
+                    }
                 }
-            m_ref = le[0] + le[1];
-            // halves are summed at the end
-            l_run = (hh == 0) ? __builtin_ldexpf(1.0f, -(int)le[1]) : 0.0f;
+            if (!SORTED) set_scale();
         }
     }
+    auto take_partial = [&]() {
+        if (SORTED && merging && le_in[0] != kNegInf) {
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) set_state(db, i, part_in[db][i]);
+            set_scale();
+        }
+    };
     // query row r -> (head, entry); the entry is the position except in
     // the multi pass (position = entry / 2)
     auto row_of = [&](int r, int& hr, int& pr) {
@@ -888,6 +945,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 gq[ks][part] =
                     *reinterpret_cast<const bf16x8*>(gr + part * KG + 16 * ks + 8 * hh);
     }
+
+    take_partial();
 
     // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
     // ---- compute of tile tau; one barrier per tile.
