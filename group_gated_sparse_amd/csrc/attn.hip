@@ -83,6 +83,7 @@ struct AttnArgs {
     const int32_t* offsets;
     const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
     const int32_t* order;   // long-range pass: sorted query tiles, most work first [B][ntiles]
+    const int32_t* rowend;  // long-range pass (one group per token): end of each sorted row's keys [B][n]
     int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
     _Float16* og;           // window partial [B][Hq][n][D]: O * 2^-e in fp16 (|.| < 1)
     f32x2* lseg;            // per row (log2-sum-exp L or -inf: no key, e)
@@ -258,6 +259,27 @@ __device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32
     }
 }
 
+// Per sorted slot s, with one group per token: the end of the key slots its
+// row keeps in the long-range pass, i.e. the first slot of its group's
+// segment whose position is >= (its position) - w. Positions increase inside
+// a segment, so this is a binary search over [segment start, s); with it a
+// partial key tile is masked by comparing slot indices, without the keys'
+// positions.
+__global__ __launch_bounds__(256) void attn_rowend_kernel(const int32_t* __restrict__ ids,
+                                                          const int32_t* __restrict__ perm,
+                                                          const int32_t* __restrict__ offsets,
+                                                          int n, int K, int w,
+                                                          int32_t* __restrict__ rowend) {
+    const int b = blockIdx.y;
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= n) return;
+    const int32_t* perm_b = perm + (int64_t)b * n;
+    const int pos = clampi(perm_b[s], 0, n - 1);
+    const int g = clampi(ids[(int64_t)b * n + pos], 0, K - 1);
+    const int ob = clampi(offsets[(int64_t)b * (K + 1) + g], 0, s);
+    rowend[(int64_t)b * n + s] = first_slot_at_or_above(perm_b, ob, s, pos - w);
+}
+
 // Tile plan of the long-range pass, once per (batch, sorted query tile) and
 // shared by every kv head: record = {nseg (-1: more than SEGCAP groups, the
 // attention kernel then derives its segments itself), first group, all query
@@ -379,12 +401,21 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     constexpr int GNC = BN * GROWB / 1024;
     // slots of the tiled order (n except in the multi pass)
     const int ne = MULTI ? a.ne : a.n;
-    // smem = [K/V buffer 0 | K/V buffer 1]; buffer 1 also stages the Q tile in
-    // the prologue, and the whole block stages the output rows in the epilogue.
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * G::TILEB];
-    unsigned char* const buf0 = smem;
-    unsigned char* const buf1 = smem + 2 * G::TILEB;
-    __shared__ __attribute__((aligned(1024))) int kpos0[KPOS_PAD], kpos1[KPOS_PAD];
+    // Two K/V buffers, [K tile | V tile] each. In the sorted passes they are
+    // two LDS variables: the compiler then sees that reads of one buffer
+    // never meet the copies into the other and does not wait for those
+    // copies before the reads (in the single-group pass, which copies no key
+    // positions, this takes the wait for the next tile's copy out of every
+    // tile; the other passes measured no gain from it and keep one variable).
+    // Buffer 1 also stages the Q tile in the prologue; the epilogue stages
+    // output rows in both (the first half of the rows in buffer 0).
+    constexpr bool SPLIT = SORTED;
+    __shared__ __attribute__((aligned(1024))) unsigned char buf0[(SPLIT ? 2 : 4) * G::TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char buf1_split[SPLIT ? 2 * G::TILEB : 16];
+    unsigned char* const buf1 = SPLIT ? buf1_split : buf0 + 2 * G::TILEB;
+    // multi pass: positions (and other groups) of the key slots of a partial tile
+    __shared__ __attribute__((aligned(1024))) int kpos0[MULTI ? KPOS_PAD : 4],
+        kpos1[MULTI ? KPOS_PAD : 4];
     // soft-gated pass: the key tile's assignment rows, one buffer per K/V buffer
     __shared__ __attribute__((aligned(1024))) unsigned char gk_lds[GATED ? 2 * BN * GROWB : 16];
     __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1], seg_kfull[MAXSEG];
@@ -422,6 +453,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // last slot's, a valid position they never store to), so the load sits
     // in no branch that would wait for it on its own.
     if (SORTED) ent_i = clampi(a.perm[bne + min(s_row, ne - 1)], 0, ne - 1);
+    // long-range pass: the end of the row's key slots (a partial tile is
+    // masked by slot index)
+    int kend_row = 0;
+    if (SORTED && !MULTI) kend_row = clampi(a.rowend[bne + min(s_row, ne - 1)], 0, ne);
     // Sorted passes: the tile's plan record, loaded beside the perm entry so
     // that the two round trips overlap. Lane l < 8 of every wave holds ints
     // 4l .. 4l+3: lane 0 the header, lane t + 1 segment t.
@@ -602,11 +637,12 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 copy16(vbase + go, dst + G::TILEB + i * 1024);
             }
         }
-        // positions of the tile's key slots, for the mask of a partial tile
-        // (a scalar base plus a 32-bit lane offset, like the tile copies: a
-        // per-lane 64-bit pointer here would be kept across the loop, spilled,
-        // and its reload would wait for the copies issued just before it)
-        if (SORTED && !full && wave == 0) {
+        // multi pass: positions and other groups of the tile's key slots, for
+        // the mask of a partial tile (a scalar base plus a 32-bit lane offset,
+        // like the tile copies: a per-lane 64-bit pointer here would be kept
+        // across the loop, spilled, and its reload would wait for the copies
+        // issued just before it). The single-group pass masks by slot index.
+        if (MULTI && !full && wave == 0) {
             const char* sp = reinterpret_cast<const char*>(a.spos + (int64_t)b * (ne + KPOS_PAD));
             copy16(sp + (uint32_t)(4 * kt0 + 16 * lane), kposp);
         }
@@ -658,10 +694,11 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     bf16x8 qf[G::KS];  // Q^T fragments, loaded once the first key tile is in flight
     bf16x8 gq[KG / 16][2];  // soft-gated pass: the row's assignment (hi, lo) fragments
 
-    auto compute = [&](int tau, const unsigned char* bufp, const int* kposp) {
-        int kt0, kend;
-        bool full;
-        locate(tau, seg_cur, kt0, kend, full);
+    // Tile tau, located before the next tile's copy is issued (between the
+    // copy and the tile's first LDS reads there is then no segment-cursor
+    // loop, across which the compiler would wait for the copy to land).
+    auto compute = [&](int tau, int kt0, int kend, bool full, const unsigned char* bufp,
+                       const int* kposp) {
         // S^T = K Q^T for the tile's 32-key blocks.
         f32x16 st[G::KB];
 #pragma unroll
@@ -699,7 +736,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int k0 = kb * 32 + 8 * e4 + 4 * hh;   // keys k0 .. k0+3
                     int4 kp = {0, 0, 0, 0};
-                    if (SORTED) kp = *reinterpret_cast<const int4*>(kposp + k0);
+                    if (MULTI) kp = *reinterpret_cast<const int4*>(kposp + k0);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int key = kt0 + k0 + j;
@@ -709,7 +746,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                             // keeps far keys and gates them instead)
                             ok = (key < kend) & (key <= pos_i) & (GATED || pos_i - key <= a.w);
                         } else if (!MULTI) {
-                            ok = row_ok & (key < kend) & (pos_i - kp[j] > a.w);
+                            // the row's keys are the slots of its group's segment below
+                            // kend_row (their positions are below pos_i - w)
+                            ok = row_ok & (key < kend_row);
                         } else {   // kp = position * 64 + the key token's other group
                             ok = row_ok & (key < kend) & (pos_i - (kp[j] >> 6) > a.w) &
                                  ((kp[j] & 63) != x_i);
@@ -951,15 +990,19 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // ---- main loop: two LDS buffers, the copy of tile tau+1 overlaps the
     // ---- compute of tile tau; one barrier per tile.
     for (int tau = 0; tau < ntl; tau += 2) {
+        int kt0, kend;
+        bool full;
         wait_vm();
         __syncthreads();
+        locate(tau, seg_cur, kt0, kend, full);
         if (tau + 1 < ntl) issue(tau + 1, buf1, kpos1);
-        compute(tau, buf0, kpos0);
+        compute(tau, kt0, kend, full, buf0, kpos0);
         if (tau + 1 >= ntl) break;
         wait_vm();
         __syncthreads();
+        locate(tau + 1, seg_cur, kt0, kend, full);
         if (tau + 2 < ntl) issue(tau + 2, buf0, kpos0);
-        compute(tau + 1, buf1, kpos1);
+        compute(tau + 1, kt0, kend, full, buf1, kpos1);
     }
 
     // Epilogue. Lane holds rows' O^T entries d = db*32 + 8*i + 4*hh + j at
@@ -995,6 +1038,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     const int nchk = RB / 16;          // 16-byte chunks per row
     const int cmask = (nchk < 16 ? nchk : 16) - 1;
     const int rpp = min(ROWS, (4 * G::TILEB) / RB);   // rows staged per pass
+    const int hrows = (2 * G::TILEB) / RB;            // rows staged per buffer
+    auto stage = [&](int rs) -> unsigned char* {
+        return rs < hrows ? buf0 + rs * RB : buf1 + (rs - hrows) * RB;
+    };
     char* dst = a.partial ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
     for (int r0 = 0; r0 < ROWS; r0 += rpp) {
         __syncthreads();               // K/V buffers (or the previous pass) are free
@@ -1008,10 +1055,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     const f32x4 o = {acc[db][4 * i] * scale_o, acc[db][4 * i + 1] * scale_o,
                                      acc[db][4 * i + 2] * scale_o, acc[db][4 * i + 3] * scale_o};
                     if (esize == 4) {
-                        *reinterpret_cast<f32x4*>(smem + rs * RB + ((qd ^ (rs & cmask)) << 4)) = o;
+                        *reinterpret_cast<f32x4*>(stage(rs) + ((qd ^ (rs & cmask)) << 4)) = o;
                     } else {
                         const int half = (qd & 1) ^ ((rs >> 4) & 1);
-                        unsigned char* sp = smem + rs * RB + (((qd >> 1) ^ (rs & cmask)) << 4) + half * 8;
+                        unsigned char* sp = stage(rs) + (((qd >> 1) ^ (rs & cmask)) << 4) + half * 8;
                         if (a.partial) {
                             const f16x4 oh = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2],
                                               (_Float16)o[3]};
@@ -1031,7 +1078,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             if (tile * a.TT + r % a.TT >= ne) continue;   // rows past the sequence end
             int hr, pr;
             row_of(r, hr, pr);
-            u32x4 val = *reinterpret_cast<const u32x4*>(smem + rs * RB + ((c ^ (rs & cmask)) << 4));
+            u32x4 val = *reinterpret_cast<const u32x4*>(stage(rs) + ((c ^ (rs & cmask)) << 4));
             if (esize == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
             *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * ne + pr) * RB) + c * 16) =
                 val;
@@ -1150,6 +1197,7 @@ AttnArgs make_args(const AttnProblem& p) {
         a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
         a.order = reinterpret_cast<const int32_t*>(base + ws.order);
         a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
+        a.rowend = reinterpret_cast<const int32_t*>(base + ws.rowend);
     }
     return a;
 }
@@ -1208,6 +1256,11 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     a.k = ks;
     a.v = vs;
     if (p.m == 1) {
+        hipLaunchKernelGGL(attn_rowend_kernel, dim3((p.n + 255) / 256, p.B), dim3(256), 0, stream,
+                           p.ids, p.perm, p.offsets, p.n, p.K, p.w,
+                           const_cast<int32_t*>(a.rowend));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
         a.merge = 1;     // start from the window partial, write the final output
         a.partial = 0;
         return launch<kLongRange>(a, p.d, stream);

@@ -75,11 +75,12 @@ inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_w
 // [B][Hkv][n*m][d]) and the sorted positions (int32 [B][n*m + pad]). With m
 // groups per token (m > 1) the sorted order lists n*m membership entries,
 // and the long-range pass writes one partial per entry (fp16
-// [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge. Last, the
+// [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge. Then the
 // order in which the long-range pass takes the sorted query tiles (int32
-// [B][tiles], most work first).
+// [B][tiles], most work first) and, with one group per token, the end of
+// the key slots each sorted row keeps (int32 [B][n]).
 struct AttnWorkspace {
-    size_t og, lseg, plan, ks, vs, spos, oge, lsege, order, total;
+    size_t og, lseg, plan, ks, vs, spos, oge, lsege, order, rowend, total;
 };
 inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m = 1) {
     AttnWorkspace w{};
@@ -96,6 +97,7 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d,
     w.oge = off;  off += m > 1 ? align_up((size_t)B * Hq * ne * d * 2) : 0;
     w.lsege = off; off += m > 1 ? align_up((size_t)B * Hq * ne * 8) : 0;
     w.order = off; off += align_up((size_t)B * ntiles * 4);
+    w.rowend = off; off += m == 1 ? align_up((size_t)B * n * 4) : 0;
     w.total = off;
     return w;
 }

@@ -118,9 +118,10 @@ def test_workspace_sizes():
     assert lib.focus_group_sort_workspace_bytes(1, 65536, 64) == 32 * 64 * 4
     # partial fp16 [B][Hq][n][d] + (lse, exponent) fp32 pairs [B][Hq][n] + 128 B plan per query
     # tile (here 64 tokens x 2 heads) + sorted bf16 K and V [B][Hkv][n][d] + int32 sorted
-    # positions [B][n + 256] + int32 tile order [B][tiles], each region 256-byte aligned
+    # positions [B][n + 256] + int32 tile order [B][tiles] + int32 end of each sorted row's keys
+    # [B][n], each region 256-byte aligned
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == (
-        256 * 2 * 32 * 2 + 4096 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4 + 256)
+        256 * 2 * 32 * 2 + 4096 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4 + 256 + 256 * 4)
     # no pair can be further apart than the window: no partial needed
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
@@ -128,7 +129,8 @@ def test_workspace_sizes():
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 1, 32) == \
         lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32)
     # m = 2: plan over 512 entries (8 tiles), sorted K, V and positions over 512 entries, then
-    # per-entry fp16 partials [B][Hq][512][d] and their pairs [B][Hq][512]
+    # per-entry fp16 partials [B][Hq][512][d] and their pairs [B][Hq][512] (no row ends: the
+    # two-group pass masks by key position)
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 2, 32) == (
         256 * 2 * 32 * 2 + 4096 + 8 * 128 + 2 * (512 * 32 * 2) + 768 * 4
         + 512 * 2 * 32 * 2 + 512 * 2 * 8 + 256)
