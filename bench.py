@@ -6,11 +6,12 @@
 One step = the whole hot path on one batch of seeded synthetic input already
 resident in HBM, all through the C ABI: focus_attn_window (the window pass,
 which needs no group data) on a second stream, while focus_assign ->
-focus_group_sort run on the main stream; then, once both are done,
-focus_attn_long_range_merge on the main stream (together the two passes are
-focus_attn_fwd). --no-overlap runs all four calls in order on one stream.
+focus_group_sort -> focus_attn_long_range_prepare (group-sorted K/V copies
+and the tile plan) run on the main stream; then, once both are done,
+focus_attn_long_range_apply on the main stream (together the calls are
+focus_attn_fwd). --no-overlap runs all five calls in order on one stream.
 Workloads with m = 2 groups per token use focus_assign_topk, the sort of the
-n*m membership entries and focus_attn_topk_long_range_merge instead.
+n*m membership entries and the focus_attn_topk_long_range_* calls instead.
 W untimed warm-up steps, then K timed steps between two device
 synchronisations. Per-call times come from HIP events recorded around each
 call, on the stream it runs on, inside the timed loop.
@@ -387,9 +388,9 @@ def main():
 
     side = torch.cuda.Stream()   # default priority
     overlap = not args.no_overlap
-    # events: 0 step start, 1 assign end, 2 sort end, 3 merge start, 4 step end (main
-    # stream); 5 window start, 6 window end (the stream the window pass runs on)
-    NEV = 7
+    # events: 0 step start, 1 assign end, 2 sort end, 7 prepare end, 3 apply start, 4 step
+    # end (main stream); 5 window start, 6 window end (the stream the window pass runs on)
+    NEV = 8
 
     def assign():
         if m == 1:
@@ -399,12 +400,20 @@ def main():
             focus.focus_assign_topk(hidden, P, C, m, bias, group_ids=ids, want_margin=False,
                                     workspace=ws_a)
 
+    def prepare():
+        if m == 1:
+            focus.focus_attn_long_range_prepare(q, k, v, ids, perm, offs, K, w, scale,
+                                                workspace=ws_t, out=out)
+        else:
+            focus.focus_attn_topk_long_range_prepare(q, k, v, ids, perm, offs, K, m, w, scale,
+                                                     workspace=ws_t, out=out)
+
     def long_range():
         if m == 1:
-            focus.focus_attn_long_range_merge(q, k, v, ids, perm, offs, K, w, scale,
+            focus.focus_attn_long_range_apply(q, k, v, ids, perm, offs, K, w, scale,
                                               workspace=ws_t, out=out)
         else:
-            focus.focus_attn_topk_long_range_merge(q, k, v, ids, perm, offs, K, m, w, scale,
+            focus.focus_attn_topk_long_range_apply(q, k, v, ids, perm, offs, K, m, w, scale,
                                                    workspace=ws_t, out=out)
 
     def step(evs=None):
@@ -414,12 +423,14 @@ def main():
         ws_stream = side if overlap else stream
         mark(0, stream)
         if overlap:
-            side.wait_stream(stream)   # the previous merge has consumed the workspace
+            side.wait_stream(stream)   # the previous apply has consumed the workspace
         else:
             assign()
             mark(1, stream)
             focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
             mark(2, stream)
+            prepare()
+            mark(7, stream)
         mark(5, ws_stream)
         focus.focus_attn_window(q, k, v, K, w, scale, workspace=ws_t, out=out, stream=ws_stream)
         mark(6, ws_stream)
@@ -428,6 +439,8 @@ def main():
             mark(1, stream)
             focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
             mark(2, stream)
+            prepare()
+            mark(7, stream)
             stream.wait_stream(side)
         mark(3, stream)
         long_range()
@@ -448,8 +461,8 @@ def main():
 
     def span(i, j):
         return float(np.mean([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)]))
-    phase = {"assign": span(0, 1), "sort": span(1, 2), "window": span(5, 6),
-             "long_range_merge": span(3, 4)}
+    phase = {"assign": span(0, 1), "sort": span(1, 2), "long_range_prepare": span(2, 7),
+             "window": span(5, 6), "long_range_apply": span(3, 4)}
     ev_step = span(0, 4)
     ms_step = max(wall_ms, ev_step)
     per_step = sorted(evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps))
@@ -463,7 +476,7 @@ def main():
         win, lr, lr_visited = metrics.pair_counts_multi(gids, w)
     pairs = win + lr
     flops = metrics.attn_flops(pairs, Hq, d)
-    attn_ms = phase["window"] + phase["long_range_merge"]
+    attn_ms = phase["window"] + phase["long_range_prepare"] + phase["long_range_apply"]
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -497,12 +510,12 @@ def main():
     }
 
     # The dominant kernel of the step and its roofline (bf16 MFMA bound).
-    kern = max(("long_range_merge", "window"), key=lambda nm: phase[nm])
-    kflops = metrics.attn_flops(lr if kern == "long_range_merge" else win, Hq, d)
+    kern = max(("long_range_apply", "window"), key=lambda nm: phase[nm])
+    kflops = metrics.attn_flops(lr if kern == "long_range_apply" else win, Hq, d)
     ach = kflops / (phase[kern] * 1e-3) / 1e12
-    kname = (f"attn_kernel<{d},{1 if m == 1 else 3}>" if kern == "long_range_merge"
+    kname = (f"attn_kernel<{d},{1 if m == 1 else 3}>" if kern == "long_range_apply"
              else f"attn_kernel<{d},0>")
-    res["roofline"] = {"kernel": kname + (" (long-range pass + merge)" if kern == "long_range_merge"
+    res["roofline"] = {"kernel": kname + (" (long-range pass + merge)" if kern == "long_range_apply"
                                           else " (window pass)"),
                        "bound": "mfma", "achieved": ach,
                        "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",

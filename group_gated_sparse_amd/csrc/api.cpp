@@ -121,7 +121,8 @@ focus_status check_attn_buffers(const uint16_t* q, const uint16_t* k, const uint
     return ok();
 }
 
-enum class AttnPart { kAll, kWindow, kLongRangeMerge };
+// kLongRangeMerge = kLongRangePrepare then kLongRangeApply
+enum class AttnPart { kAll, kWindow, kLongRangeMerge, kLongRangePrepare, kLongRangeApply };
 
 focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const int32_t* group_ids, const int32_t* perm,
@@ -157,12 +158,18 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
                          out, out_dtype == FOCUS_F32 ? 1 : 0, lse, need > 0 ? workspace : nullptr,
                          m};
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    if (part != AttnPart::kLongRangeMerge) {
+    if (part == AttnPart::kAll || part == AttnPart::kWindow) {
         hipError_t e = focus::launch_attn_window(p, hs);
         if (e != hipSuccess) return device_status(e, "window attention launch");
     }
-    if (part != AttnPart::kWindow) {
-        hipError_t e = focus::launch_attn_long_range(p, hs);
+    if (part == AttnPart::kAll || part == AttnPart::kLongRangeMerge ||
+        part == AttnPart::kLongRangePrepare) {
+        hipError_t e = focus::launch_attn_long_range_prepare(p, hs);
+        if (e != hipSuccess) return device_status(e, "long-range preparation launch");
+    }
+    if (part == AttnPart::kAll || part == AttnPart::kLongRangeMerge ||
+        part == AttnPart::kLongRangeApply) {
+        hipError_t e = focus::launch_attn_long_range_apply(p, hs);
         if (e != hipSuccess) return device_status(e, "long-range attention launch");
     }
     return ok();
@@ -364,6 +371,30 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
                       workspace_bytes, stream);
 }
 
+focus_status focus_attn_long_range_prepare(const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, const int32_t* group_ids,
+                                           const int32_t* perm, const int32_t* group_offsets,
+                                           int B, int Hq, int Hkv, int n, int d_head, int K,
+                                           int window, float scale, void* out,
+                                           focus_dtype out_dtype, float* lse, void* workspace,
+                                           size_t workspace_bytes, focus_stream_t stream) {
+    return attn_entry(AttnPart::kLongRangePrepare, q, k, v, group_ids, perm, group_offsets, B,
+                      Hq, Hkv, n, d_head, K, 1, window, scale, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+focus_status focus_attn_long_range_apply(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* group_ids, const int32_t* perm,
+                                         const int32_t* group_offsets, int B, int Hq, int Hkv,
+                                         int n, int d_head, int K, int window, float scale,
+                                         void* out, focus_dtype out_dtype, float* lse,
+                                         void* workspace, size_t workspace_bytes,
+                                         focus_stream_t stream) {
+    return attn_entry(AttnPart::kLongRangeApply, q, k, v, group_ids, perm, group_offsets, B, Hq,
+                      Hkv, n, d_head, K, 1, window, scale, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream);
+}
+
 size_t focus_soft_gate_attn_workspace_bytes(int B, int n, int K) {
     if (B < 1 || n < 1 || K < 1 || K > FOCUS_MAX_GROUPS) return 0;
     return focus::soft_gate_workspace(B, n, K);
@@ -428,6 +459,33 @@ focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t*
                                               void* workspace, size_t workspace_bytes,
                                               focus_stream_t stream) {
     return attn_entry(AttnPart::kLongRangeMerge, q, k, v, group_ids, perm, group_offsets, B, Hq,
+                      Hkv, n, d_head, K, m, window, scale, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+focus_status focus_attn_topk_long_range_prepare(const uint16_t* q, const uint16_t* k,
+                                                const uint16_t* v, const int32_t* group_ids,
+                                                const int32_t* perm,
+                                                const int32_t* group_offsets, int B, int Hq,
+                                                int Hkv, int n, int d_head, int K, int m,
+                                                int window, float scale, void* out,
+                                                focus_dtype out_dtype, float* lse,
+                                                void* workspace, size_t workspace_bytes,
+                                                focus_stream_t stream) {
+    return attn_entry(AttnPart::kLongRangePrepare, q, k, v, group_ids, perm, group_offsets, B,
+                      Hq, Hkv, n, d_head, K, m, window, scale, out, out_dtype, lse, workspace,
+                      workspace_bytes, stream);
+}
+
+focus_status focus_attn_topk_long_range_apply(const uint16_t* q, const uint16_t* k,
+                                              const uint16_t* v, const int32_t* group_ids,
+                                              const int32_t* perm, const int32_t* group_offsets,
+                                              int B, int Hq, int Hkv, int n, int d_head, int K,
+                                              int m, int window, float scale, void* out,
+                                              focus_dtype out_dtype, float* lse,
+                                              void* workspace, size_t workspace_bytes,
+                                              focus_stream_t stream) {
+    return attn_entry(AttnPart::kLongRangeApply, q, k, v, group_ids, perm, group_offsets, B, Hq,
                       Hkv, n, d_head, K, m, window, scale, out, out_dtype, lse, workspace,
                       workspace_bytes, stream);
 }

@@ -1214,6 +1214,20 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Long-range pass arguments: the sorted order lists n*m entries, and K and V
+// are read from their group-sorted copies.
+AttnArgs long_range_args(const AttnProblem& p) {
+    AttnArgs a = make_args(p);
+    a.ne = p.n * p.m;
+    a.ntiles = (a.ne + a.TT - 1) / a.TT;
+    a.total = p.B * p.Hkv * a.nslices * a.ntiles;
+    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
+    char* base = static_cast<char*>(p.workspace);
+    a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
+    a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
+    return a;
+}
+
 }  // namespace
 
 int attn_heads_per_wg(int hpk) {
@@ -1225,22 +1239,15 @@ int attn_heads_per_wg(int hpk) {
     return g;
 }
 
-hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
+hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
-    AttnArgs a = make_args(p);
-    // the sorted order lists n*m entries
-    a.ne = p.n * p.m;
-    a.ntiles = (a.ne + a.TT - 1) / a.TT;
-    a.total = p.B * p.Hkv * a.nslices * a.ntiles;
-    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
-    char* base = static_cast<char*>(p.workspace);
-    uint16_t* ks = reinterpret_cast<uint16_t*>(base + ws.ks);
-    uint16_t* vs = reinterpret_cast<uint16_t*>(base + ws.vs);
+    const AttnArgs a = long_range_args(p);
     const int64_t chunks = (int64_t)(a.ne + KPOS_PAD) * (p.d / 8);
     hipLaunchKernelGGL(attn_gather_kernel, dim3((unsigned)((chunks + 255) / 256), p.B * p.Hkv),
                        dim3(256), 0, stream, p.k, p.v, p.perm, p.ids, p.n, a.ne, p.m, p.K,
-                       p.Hkv, p.d, ks, vs, a.spos);
+                       p.Hkv, p.d, const_cast<uint16_t*>(a.k), const_cast<uint16_t*>(a.v),
+                       a.spos);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
@@ -1253,19 +1260,27 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
                        const_cast<int32_t*>(a.order));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.k = ks;
-    a.v = vs;
     if (p.m == 1) {
         hipLaunchKernelGGL(attn_rowend_kernel, dim3((p.n + 255) / 256, p.B), dim3(256), 0, stream,
                            p.ids, p.perm, p.offsets, p.n, p.K, p.w,
                            const_cast<int32_t*>(a.rowend));
         e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    }
+    return e;
+}
+
+hipError_t launch_attn_long_range_apply(const AttnProblem& p, hipStream_t stream) {
+    if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
+    if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
+    AttnArgs a = long_range_args(p);
+    if (p.m == 1) {
         a.merge = 1;     // start from the window partial, write the final output
         a.partial = 0;
         return launch<kLongRange>(a, p.d, stream);
     }
     // Two groups per token: one partial per entry, then the merge.
+    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
+    char* base = static_cast<char*>(p.workspace);
     _Float16* oge = reinterpret_cast<_Float16*>(base + ws.oge);
     f32x2* lsege = reinterpret_cast<f32x2*>(base + ws.lsege);
     const _Float16* og = a.og;
@@ -1274,7 +1289,7 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
     a.lseg = lsege;
     a.merge = 0;
     a.partial = 1;
-    e = launch<kLongMulti>(a, p.d, stream);
+    hipError_t e = launch<kLongMulti>(a, p.d, stream);
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)p.B * p.Hq * p.n;
     const int64_t threads = rows * (p.d / 8);
@@ -1295,6 +1310,12 @@ hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {
+    const hipError_t e = launch_attn_long_range_prepare(p, stream);
+    if (e != hipSuccess) return e;
+    return launch_attn_long_range_apply(p, stream);
 }
 
 hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream) {

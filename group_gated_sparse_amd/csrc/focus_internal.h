@@ -105,6 +105,11 @@ inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w, int m 
     if (!attn_has_long_range(n, w)) return 0;
     return attn_workspace_layout(B, Hq, Hkv, n, d, m).total;
 }
+// The long-range pass: prepare (sorted K/V copies, tile plan and order, row
+// ends; needs only k, v and the group data) then apply (the attention, merged
+// with the window partial); launch_attn_long_range runs both.
+hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stream);
+hipError_t launch_attn_long_range_apply(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_window(const AttnProblem& p, hipStream_t stream);
 hipError_t launch_attn_dense(const AttnProblem& p, hipStream_t stream);

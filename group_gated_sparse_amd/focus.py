@@ -42,12 +42,20 @@ _SIGNATURES = {
                                _p, _p, _sz, _p], _i),
     "focus_attn_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
                                  _i, _p, _p, _sz, _p], _i),
+    "focus_attn_long_range_prepare": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f,
+                                       _p, _i, _p, _p, _sz, _p], _i),
+    "focus_attn_long_range_apply": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
+                                     _i, _p, _p, _sz, _p], _i),
     "dense_causal_attn_fwd": ([_p, _p, _p, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p], _i),
     "focus_assign_topk": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
     "focus_attn_topk_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i, _i], _sz),
     "focus_attn_topk_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
                              _p, _p, _sz, _p], _i),
     "focus_attn_topk_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
+                                          _f, _p, _i, _p, _p, _sz, _p], _i),
+    "focus_attn_topk_long_range_prepare": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i,
+                                            _i, _f, _p, _i, _p, _p, _sz, _p], _i),
+    "focus_attn_topk_long_range_apply": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i,
                                           _f, _p, _i, _p, _p, _sz, _p], _i),
     "focus_assign_scores": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, _p], _i),
     "focus_sinkhorn_workspace_bytes": ([_i, _i, _i, _i], _sz),
@@ -311,6 +319,27 @@ def focus_attn_long_range_merge(q, k, v, group_ids, perm, group_offsets, K: int,
                       window, scale, out, out_dtype, lse, want_lse, workspace, stream)
 
 
+def focus_attn_long_range_prepare(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
+                                  scale: float, *, workspace, out, out_dtype=torch.bfloat16,
+                                  lse=None, stream=None):
+    """First half of focus_attn_long_range_merge: the group-sorted K/V
+    copies, tile plan and order and row ends, written into workspace. It
+    reads only k, v and the group data (pass the out and lse that the apply
+    call will get), so it may run beside focus_attn_window."""
+    _attn_call("focus_attn_long_range_prepare", q, k, v, group_ids, perm, group_offsets, K,
+               window, scale, out, out_dtype, lse, False, workspace, stream)
+
+
+def focus_attn_long_range_apply(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
+                                scale: float, *, workspace, out=None, out_dtype=torch.bfloat16,
+                                lse=None, want_lse: bool = False, stream=None):
+    """Second half of focus_attn_long_range_merge, after both
+    focus_attn_long_range_prepare and focus_attn_window on this workspace:
+    the intra-group attention merged with the window partial."""
+    return _attn_call("focus_attn_long_range_apply", q, k, v, group_ids, perm, group_offsets, K,
+                      window, scale, out, out_dtype, lse, want_lse, workspace, stream)
+
+
 def focus_attn_topk_fwd(q, k, v, group_ids, perm, group_offsets, K: int, m: int, window: int,
                         scale: float, *, out=None, out_dtype=torch.bfloat16, lse=None,
                         want_lse: bool = False, workspace=None, stream=None):
@@ -331,6 +360,24 @@ def focus_attn_topk_long_range_merge(q, k, v, group_ids, perm, group_offsets, K:
     same workspace): shared-group pairs beyond the window, one partial per
     membership entry, and the merge into out (and lse)."""
     return _attn_call("focus_attn_topk_long_range_merge", q, k, v, group_ids, perm,
+                      group_offsets, K, window, scale, out, out_dtype, lse, want_lse, workspace,
+                      stream, m=m)
+
+
+def focus_attn_topk_long_range_prepare(q, k, v, group_ids, perm, group_offsets, K: int, m: int,
+                                       window: int, scale: float, *, workspace, out,
+                                       out_dtype=torch.bfloat16, lse=None, stream=None):
+    """focus_attn_long_range_prepare for m groups per token."""
+    _attn_call("focus_attn_topk_long_range_prepare", q, k, v, group_ids, perm, group_offsets, K,
+               window, scale, out, out_dtype, lse, False, workspace, stream, m=m)
+
+
+def focus_attn_topk_long_range_apply(q, k, v, group_ids, perm, group_offsets, K: int, m: int,
+                                     window: int, scale: float, *, workspace, out=None,
+                                     out_dtype=torch.bfloat16, lse=None, want_lse: bool = False,
+                                     stream=None):
+    """focus_attn_long_range_apply for m groups per token."""
+    return _attn_call("focus_attn_topk_long_range_apply", q, k, v, group_ids, perm,
                       group_offsets, K, window, scale, out, out_dtype, lse, want_lse, workspace,
                       stream, m=m)
 

@@ -55,7 +55,7 @@ typedef enum {
 
 typedef enum { FOCUS_BF16 = 0, FOCUS_F32 = 1 } focus_dtype;
 
-#define FOCUS_ABI_VERSION 2
+#define FOCUS_ABI_VERSION 3
 #define FOCUS_MAX_GROUPS 64
 #define FOCUS_MAX_MEMBERSHIPS 2 /* groups per token (m) of the top-k variant */
 #define FOCUS_MAX_SINKHORN_ITERS 10000
@@ -217,6 +217,33 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
                                          focus_dtype out_dtype, float* lse, void* workspace,
                                          size_t workspace_bytes, focus_stream_t stream);
 
+/* focus_attn_long_range_merge in two calls, with its arguments and workspace:
+ * focus_attn_long_range_merge == focus_attn_long_range_prepare then
+ * focus_attn_long_range_apply on one stream.
+ *
+ * focus_attn_long_range_prepare reads only k, v and the group data (q, out
+ * and lse are checked, not read) and writes the group-sorted copies of K and
+ * V, the query-tile plan and order and each sorted row's key-slot end into
+ * the workspace. It writes no part of the workspace that focus_attn_window
+ * writes, so it may run on another stream while the window pass runs, once
+ * the sort is done. focus_attn_long_range_apply needs both (order them
+ * before it with stream events): it runs the intra-group attention, merges
+ * the window partial and writes out and lse. */
+focus_status focus_attn_long_range_prepare(const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, const int32_t* group_ids,
+                                           const int32_t* perm, const int32_t* group_offsets,
+                                           int B, int Hq, int Hkv, int n, int d_head, int K,
+                                           int window, float scale, void* out,
+                                           focus_dtype out_dtype, float* lse, void* workspace,
+                                           size_t workspace_bytes, focus_stream_t stream);
+focus_status focus_attn_long_range_apply(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                         const int32_t* group_ids, const int32_t* perm,
+                                         const int32_t* group_offsets,
+                                         int B, int Hq, int Hkv, int n, int d_head, int K,
+                                         int window, float scale, void* out,
+                                         focus_dtype out_dtype, float* lse, void* workspace,
+                                         size_t workspace_bytes, focus_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Step 3, top-k variant (Korean page §2.3 and §3.4; Japanese page §2.2 and
  * §3.3): each token belongs to m groups (m = 2 in the pages' runs), and a far
@@ -254,6 +281,26 @@ focus_status focus_attn_topk_fwd(const uint16_t* q, const uint16_t* k, const uin
                                  float* lse, void* workspace, size_t workspace_bytes,
                                  focus_stream_t stream);
 focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t* k,
+                                              const uint16_t* v, const int32_t* group_ids,
+                                              const int32_t* perm, const int32_t* group_offsets,
+                                              int B, int Hq, int Hkv, int n, int d_head, int K,
+                                              int m, int window, float scale, void* out,
+                                              focus_dtype out_dtype, float* lse,
+                                              void* workspace, size_t workspace_bytes,
+                                              focus_stream_t stream);
+/* focus_attn_topk_long_range_merge in two calls, as for m = 1 above:
+ * prepare (sorted K/V over the n*m entries, plan and order; may run beside
+ * the window pass) then apply (the per-entry partials and the final merge). */
+focus_status focus_attn_topk_long_range_prepare(const uint16_t* q, const uint16_t* k,
+                                                const uint16_t* v, const int32_t* group_ids,
+                                                const int32_t* perm,
+                                                const int32_t* group_offsets, int B, int Hq,
+                                                int Hkv, int n, int d_head, int K, int m,
+                                                int window, float scale, void* out,
+                                                focus_dtype out_dtype, float* lse,
+                                                void* workspace, size_t workspace_bytes,
+                                                focus_stream_t stream);
+focus_status focus_attn_topk_long_range_apply(const uint16_t* q, const uint16_t* k,
                                               const uint16_t* v, const int32_t* group_ids,
                                               const int32_t* perm, const int32_t* group_offsets,
                                               int B, int Hq, int Hkv, int n, int d_head, int K,

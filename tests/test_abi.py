@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert name in exported, f"{name} is declared but not exported"
         assert getattr(lib, name) is not None
-    assert lib.focus_abi_version() == 2
+    assert lib.focus_abi_version() == 3
 
 
 def _err():
@@ -174,7 +174,8 @@ def _attn(fn="focus_attn_fwd", **kw):
 
 
 @pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_window",
-                                "focus_attn_long_range_merge"])
+                                "focus_attn_long_range_merge", "focus_attn_long_range_prepare",
+                                "focus_attn_long_range_apply"])
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(q=None), INVALID, "q"),
     (dict(k=Bp + 8), INVALID, "aligned"),
@@ -203,7 +204,8 @@ def test_attn_rejects(fn, kw, code, msg):
     assert msg in _err()
 
 
-@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_long_range_merge"])
+@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_long_range_merge",
+                                "focus_attn_long_range_prepare", "focus_attn_long_range_apply"])
 @pytest.mark.parametrize("kw,msg", [(dict(ids=None), "group_ids"), (dict(perm=None), "perm"),
                                     (dict(offs=None), "group_offsets")])
 def test_attn_passes_needing_groups_reject_missing_group_data(fn, kw, msg):
@@ -222,7 +224,9 @@ def _attn_topk(fn="focus_attn_topk_fwd", m=2, **kw):
              args["stream"])
 
 
-@pytest.mark.parametrize("fn", ["focus_attn_topk_fwd", "focus_attn_topk_long_range_merge"])
+@pytest.mark.parametrize("fn", ["focus_attn_topk_fwd", "focus_attn_topk_long_range_merge",
+                                "focus_attn_topk_long_range_prepare",
+                                "focus_attn_topk_long_range_apply"])
 @pytest.mark.parametrize("m,kw,code,msg", [
     (0, {}, UNSUPPORTED, "m must be"),
     (3, dict(K=8), UNSUPPORTED, "m must be"),

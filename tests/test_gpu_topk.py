@@ -212,6 +212,37 @@ def test_topk_two_calls_equal_one():
     assert torch.equal(one, two) and torch.equal(lse1, lse2)
 
 
+def test_topk_three_calls_equal_one():
+    """focus_attn_window (second stream) beside the sort and
+    focus_attn_topk_long_range_prepare, then focus_attn_topk_long_range_apply
+    == focus_attn_topk_fwd, bit for bit."""
+    say("[attn top-k] prepare / apply calls")
+    rng = np.random.default_rng(33)
+    B, Hq, Hkv, n, d, K, m, w = 1, 8, 2, 700, 64, 6, 2, 50
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = _member_ids(rng, B, n, K, m)
+    tq, tk, tv, tid = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(ids)
+    perm, offs = focus.focus_group_sort(tid, K)
+    one, lse1 = focus.focus_attn_topk_fwd(tq, tk, tv, tid, perm, offs, K, m, w, 0.1,
+                                          out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    ws = torch.empty(focus.focus_attn_topk_workspace_bytes(B, Hq, Hkv, n, d, K, m, w),
+                     dtype=torch.uint8, device="cuda")
+    two = torch.empty_like(one)
+    lse2 = torch.empty_like(lse1)
+    side, main = torch.cuda.Stream(), torch.cuda.current_stream()
+    side.wait_stream(main)
+    focus.focus_attn_window(tq, tk, tv, K, w, 0.1, workspace=ws, out=two, lse=lse2, stream=side)
+    perm2, offs2 = focus.focus_group_sort(tid, K, stream=main)
+    focus.focus_attn_topk_long_range_prepare(tq, tk, tv, tid, perm2, offs2, K, m, w, 0.1,
+                                             workspace=ws, out=two, lse=lse2, stream=main)
+    main.wait_stream(side)
+    focus.focus_attn_topk_long_range_apply(tq, tk, tv, tid, perm2, offs2, K, m, w, 0.1,
+                                           workspace=ws, out=two, lse=lse2, stream=main)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two) and torch.equal(lse1, lse2)
+
+
 # ---------------------------------------------------------------- workloads
 def test_whole_path_small_top2():
     """assign (top-2) -> sort of entries -> attention, all rows, on the
