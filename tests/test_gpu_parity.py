@@ -52,6 +52,10 @@ ATTN_CASES = [
     ("gqa16", 1, 16, 1, 260, 64, 6, 30),
     ("wide_window", 1, 2, 2, 150, 32, 4, 149),
     ("many_tiles", 2, 3, 3, 1100, 64, 9, 100),
+    # query tiles spanning more than the 7 groups a plan record holds (the
+    # kernel derives the segments itself and masks every key tile)
+    ("many_groups_per_tile", 1, 2, 2, 1000, 64, 64, 8),
+    ("many_groups_d128", 1, 4, 4, 900, 128, 64, 10),
 ]
 
 
