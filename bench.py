@@ -338,7 +338,7 @@ def bench_soft_gate(args, wl):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library runs on one GPU "
               "(the design notes describe how the work would shard). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)

@@ -180,6 +180,20 @@ __device__ __forceinline__ void copy16(const void* src, void* lds_base) {
                                      0);
 }
 
+// 16-byte buffer -> LDS copy: lane l reads base + soff + voff (a 32-bit
+// per-lane offset) and lands at lds_base + 16*l. The buffer resource holds
+// the base and the byte size in scalar registers; reads past the size
+// return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ void copy16_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                           void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, soff, 0, 0);
+}
+
 // Workgroups are dealt round-robin to the 8 XCDs; renumber them so each XCD
 // works through one contiguous range of work items (neighbouring tiles of one
 // head share keys in that XCD's L2).
@@ -618,23 +632,28 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         bool full;
         locate(tau, seg_issue, kt0, kend, full);
         unsigned char* dst = bufp + wave_s * G::NI * 1024;
+        // The tile's K and V rows through buffer resources whose base is the
+        // tile's first row (scalar registers) and whose size stops at the
+        // sequence end; each lane adds its fixed 32-bit offset. In a tile that
+        // runs past the sequence end, rows from kend on re-read row kend - 1
+        // (they are masked).
+        const int64_t tb = (int64_t)kt0 * D;
+        const uint32_t nbytes = __builtin_amdgcn_readfirstlane(clampi(ne - kt0, 0, BN) * G::ROWB);
+        const __amdgpu_buffer_rsrc_t krs = make_rsrc(kbase + tb, nbytes);
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vbase + tb, nbytes);
         if (kt0 + BN <= ne) {
-            // the whole tile lies inside the sequence: a scalar tile base plus
-            // fixed per-lane offsets (rows past kend are read but masked)
-            const char* kt = reinterpret_cast<const char*>(kbase + (int64_t)kt0 * D);
-            const char* vt = reinterpret_cast<const char*>(vbase + (int64_t)kt0 * D);
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
-                copy16(kt + lane_off[i], dst + i * 1024);
-                copy16(vt + lane_off[i], dst + G::TILEB + i * 1024);
+                copy16_buf(krs, lane_off[i], 0, dst + i * 1024);
+                copy16_buf(vrs, lane_off[i], 0, dst + G::TILEB + i * 1024);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
-                const int slot = min(kt0 + (int)(lane_off[i] / G::ROWB), kend - 1);
-                const int64_t go = (int64_t)slot * D + (lane_off[i] % G::ROWB) / 2;
-                copy16(kbase + go, dst + i * 1024);
-                copy16(vbase + go, dst + G::TILEB + i * 1024);
+                const uint32_t r = min(lane_off[i] / G::ROWB, (uint32_t)max(kend - 1 - kt0, 0));
+                const uint32_t vo = r * G::ROWB + lane_off[i] % G::ROWB;
+                copy16_buf(krs, vo, 0, dst + i * 1024);
+                copy16_buf(vrs, vo, 0, dst + G::TILEB + i * 1024);
             }
         }
         // multi pass: positions and other groups of the tile's key slots, for
