@@ -1,7 +1,7 @@
 """Benchmark of the Focus forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--skip-cpu-baseline] [--skip-dense]
+                    [--skip-cpu-baseline] [--skip-dense] [--cold-mall]
 
 One step = the whole hot path on one batch of seeded synthetic input already
 resident in HBM, all through the C ABI: focus_attn_window (the window pass,
@@ -19,8 +19,10 @@ call, on the stream it runs on, inside the timed loop.
 Prints ONE JSON line. value = visited-pair TFLOP/s of the whole step
 (4*d flops per allowed (query head, i, j) pair / step time). Also reported:
 attention-only TFLOP/s, the dense causal baseline (dense_causal_attn_fwd) and
-the speedups over it, the roofline of the dominant kernel, and the CPU
-oracle timed on a bounded sample of the same workload.
+the speedups over it, the roofline of the dominant kernel, the pairs the
+kernels' tiles compute (masked ones included) with the tile utilization and
+computed-tile TFLOP/s of each pass, and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 import argparse
 import json
@@ -61,6 +63,10 @@ def parse():
     ap.add_argument("--lam", type=float, default=8.0, help="gate slope (--op soft_gate)")
     ap.add_argument("--iters", type=int, default=10, help="Sinkhorn rounds (--op sinkhorn)")
     ap.add_argument("--tau", type=float, default=1.0, help="Sinkhorn temperature (--op sinkhorn)")
+    ap.add_argument("--cold-mall", action="store_true",
+                    help="write a 512 MiB buffer before each timed step (outside its events), "
+                         "so the step starts with nothing of its inputs in the 256 MB "
+                         "Infinity Cache; the step time is then the HIP-event time")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch for calibrating HBM byte counters)")
@@ -454,17 +460,21 @@ def main():
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    flush = torch.empty(1 << 27, dtype=torch.float32, device=dv) if args.cold_mall else None
     for s in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(s))
         step(evs[s])
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del flush
 
     def span(i, j):
         return float(np.mean([evs[s][i].elapsed_time(evs[s][j]) for s in range(args.steps)]))
     phase = {"assign": span(0, 1), "sort": span(1, 2), "long_range_prepare": span(2, 7),
              "window": span(5, 6), "long_range_apply": span(3, 4)}
     ev_step = span(0, 4)
-    ms_step = max(wall_ms, ev_step)
+    ms_step = ev_step if args.cold_mall else max(wall_ms, ev_step)
     per_step = sorted(evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps))
     log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
 
@@ -477,6 +487,12 @@ def main():
     pairs = win + lr
     flops = metrics.attn_flops(pairs, Hq, d)
     attn_ms = phase["window"] + phase["long_range_prepare"] + phase["long_range_apply"]
+    # pairs the kernels' MFMAs form, masked ones included (their tiling)
+    tt = 128 // metrics.heads_per_workgroup(Hq, Hkv)
+    bn = metrics.tile_keys(d)
+    cwin = B * metrics.window_computed_pairs(n, w, tt, bn)
+    clr = metrics.long_range_computed_pairs(gids.reshape(B, n * m), perm.cpu().numpy(),
+                                            offs.cpu().numpy(), w, tt, bn, m)
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -493,6 +509,8 @@ def main():
         "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "n": n, "d_head": d,
                    "d_model": wl.d_model, "d_proj": wl.d_proj, "K": K, "window": w,
                    "groups_per_token": m, "out_dtype": "bf16",
+                   "mall": "cold (512 MiB written before each step)" if args.cold_mall
+                   else "warm",
                    "streams": "window pass overlapped with assign+sort" if overlap
                    else "one stream"},
         "visited_pairs_per_head": pairs,
@@ -507,6 +525,12 @@ def main():
         "attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
         "attn_frac_of_bf16_peak": flops / (attn_ms * 1e-3) / 1e12 / metrics.MI355X_BF16_DENSE_TFLOPS,
         "assign_GBps": (B * n * wl.d_model * 4) / (phase["assign"] * 1e-3) / 1e9,
+        "computed_pairs_per_head": {"window": cwin, "long_range": clr},
+        "tile_utilization": {"window": win / cwin, "long_range": lr_visited / max(clr, 1)},
+        "computed_tile_tflops": {
+            "window": metrics.attn_flops(cwin, Hq, d) / (phase["window"] * 1e-3) / 1e12,
+            "long_range": metrics.attn_flops(clr, Hq, d) / (phase["long_range_apply"] * 1e-3) / 1e12,
+            "attention": metrics.attn_flops(cwin + clr, Hq, d) / (attn_ms * 1e-3) / 1e12},
     }
 
     # The dominant kernel of the step and its roofline (bf16 MFMA bound).

@@ -78,3 +78,57 @@ def pair_counts_multi(ids: np.ndarray, w: int):
 
 def attn_flops(pairs: int, Hq: int, d: int) -> float:
     return 4.0 * d * pairs * Hq
+
+
+# ---- Computed pairs: the (query, key) products the attention kernels' MFMAs
+# ---- actually form, masked ones included, to separate masking waste from
+# ---- kernel speed. They follow the kernels' tiling: a workgroup takes TT
+# ---- tokens x G query heads (G = the largest of 8, 4, 2, 1 dividing Hq/Hkv,
+# ---- TT = 128 / G) and visits key tiles of BN keys (32 for d = 64 and 128,
+# ---- 64 for d = 32).
+
+def heads_per_workgroup(Hq: int, Hkv: int) -> int:
+    hpk = Hq // Hkv
+    for g in (8, 4, 2, 1):
+        if hpk % g == 0:
+            return g
+    return 1
+
+
+def tile_keys(d: int) -> int:
+    return 64 if d == 32 else 32
+
+
+def window_computed_pairs(n: int, w: int, TT: int, BN: int) -> int:
+    """Per query head: key tiles of [max(0, q0 - w), last query] for every
+    tile of TT tokens, times TT rows."""
+    q0 = np.arange(0, n, TT, dtype=np.int64)
+    kend = np.minimum(n, q0 + TT)
+    kstart = np.maximum(0, q0 - w)
+    ntl = (kend - kstart + BN - 1) // BN
+    return int(ntl.sum()) * BN * TT
+
+
+def long_range_computed_pairs(ids: np.ndarray, perm: np.ndarray, offsets: np.ndarray, w: int,
+                              TT: int, BN: int, m: int = 1) -> int:
+    """Per query head, summed over the batch: for each tile of TT sorted
+    slots and each group g among them, the key tiles of g's segment below
+    the first slot whose position is >= (largest query position of g in the
+    tile) - w, times TT rows. ids is [B][n*m] flat, perm [B][n*m] entries
+    (position = entry // m), offsets [B][K+1]."""
+    B, ne = perm.shape
+    total = 0
+    for b in range(B):
+        pb, ob_, ib = perm[b].astype(np.int64), offsets[b].astype(np.int64), ids[b]
+        for s0 in range(0, ne, TT):
+            s1 = min(ne, s0 + TT)
+            gf, gl = int(ib[pb[s0]]), int(ib[pb[s1 - 1]])
+            for g in range(gf, gl + 1):
+                ob, oe = int(ob_[g]), int(ob_[g + 1])
+                qlo, qhi = max(s0, ob), min(s1, oe)
+                if qlo >= qhi:
+                    continue
+                maxpos = int(pb[qhi - 1]) // m
+                kend = ob + int(np.searchsorted(pb[ob:qhi], m * (maxpos - w), side="left"))
+                total += (kend - ob + BN - 1) // BN
+    return total * BN * TT
