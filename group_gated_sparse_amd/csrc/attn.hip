@@ -718,6 +718,22 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // loop, across which the compiler would wait for the copy to land).
     auto compute = [&](int tau, int kt0, int kend, bool full, const unsigned char* bufp,
                        const int* kposp) {
+        // A wave none of whose rows keeps a key of this tile skips it (all
+        // its products would be masked). With one query head per kv head
+        // the four waves hold different tokens, so near either end of the
+        // workgroup's key range, or in a segment of another group, some
+        // waves have nothing to do; their SIMD serves the other workgroups.
+        {
+            bool needs;
+            if (!SORTED) {
+                needs = rvalid && kt0 <= pos_i && (CAUSAL_ALL || kt0 + BN - 1 >= pos_i - a.w);
+            } else if (!MULTI) {
+                needs = rvalid && g_i == gfirst + seg_cur.seg && kt0 < kend_row;
+            } else {
+                needs = rvalid && g_i == gfirst + seg_cur.seg;
+            }
+            if (!__any(needs)) return;
+        }
         // S^T = K Q^T for the tile's 32-key blocks.
         f32x16 st[G::KB];
 #pragma unroll
