@@ -14,8 +14,10 @@
 //     groups are being assigned and sorted. It writes the normalised partial
 //     output as 16 bits per element (fp16 with a per-row power-of-two scale)
 //     and its log2-sum-exp per row.
-//   long-range pass (group-sorted order): K and V are first copied into
-//     group-sorted order (row s = row perm[s]); a plan kernel lists, per
+//   long-range pass (group-sorted order): key slot s is key row perm[s],
+//     read in place (one group per token: each tile copy takes its rows'
+//     positions from perm, loaded a tile ahead) or from group-sorted copies
+//     of K and V (two groups per token); a plan kernel lists, per
 //     sorted query tile, the key-slot range of each group present (keys of
 //     the group with position below (largest query position) - w). The
 //     attention kernel, for each tile of 128/G sorted tokens x G query heads
@@ -103,6 +105,8 @@ struct AttnArgs {
     float nl2;            // soft-gated pass: -lambda * log2(e)
     int out_f32;
     int merge;     // start from the partial in og/lseg (row of the original position)
+    int direct;    // long-range pass, one group per token: k and v are the sequence-order
+                   // tensors and key rows are read at their positions (perm), not copied
     int partial;   // write the normalised partial to og/lseg instead of out/lse
 };
 
@@ -617,6 +621,29 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     SegCursor seg_issue = {0, 0, 0, 0, 0, 0};
     if (SORTED && ntl > 0) seg_load(seg_issue);
     SegCursor seg_cur = seg_issue;
+    // Long-range pass reading K and V rows in place (direct): the position
+    // of each of this lane's NI rows of the next tile to copy, loaded from
+    // perm one tile ahead (so the copy never waits for it), and a buffer
+    // resource over the head's n rows.
+    const bool direct = SORTED && !MULTI && a.direct;
+    SegCursor seg_pref = seg_issue;
+    int pnext[G::NI];
+    const __amdgpu_buffer_rsrc_t krs_head =
+        make_rsrc(kbase, direct ? (uint32_t)a.n * G::ROWB : 0u);
+    const __amdgpu_buffer_rsrc_t vrs_head =
+        make_rsrc(vbase, direct ? (uint32_t)a.n * G::ROWB : 0u);
+    auto prefetch = [&](int tau) {
+        int kt0, kend;
+        bool full;
+        locate(tau, seg_pref, kt0, kend, full);
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) {
+            // rows past the segment's valid slots take its last valid slot (masked)
+            const int slot = min(kt0 + (int)(lane_off[i] / G::ROWB), kend - 1);
+            pnext[i] = a.perm[bne + clampi(slot, 0, ne - 1)];
+        }
+    };
+    if (direct && ntl > 0) prefetch(0);
     // soft-gated pass: this lane's share of the assignment-row copies (1 KB
     // copies wave, wave + 4, ...): key row within the tile and logical chunk
     constexpr int GCPW = (GNC + 3) / 4;
@@ -632,6 +659,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         bool full;
         locate(tau, seg_issue, kt0, kend, full);
         unsigned char* dst = bufp + wave_s * G::NI * 1024;
+        if (direct) {
+#pragma unroll
+            for (int i = 0; i < G::NI; ++i) {
+                const uint32_t vo = (uint32_t)clampi(pnext[i], 0, a.n - 1) * G::ROWB +
+                                    lane_off[i] % G::ROWB;
+                copy16_buf(krs_head, vo, 0, dst + i * 1024);
+                copy16_buf(vrs_head, vo, 0, dst + G::TILEB + i * 1024);
+            }
+            if (tau + 1 < ntl) prefetch(tau + 1);
+            return;
+        }
         // The tile's K and V rows through buffer resources whose base is the
         // tile's first row (scalar registers) and whose size stops at the
         // sequence end; each lane adds its fixed 32-bit offset. In a tile that
@@ -1249,17 +1287,26 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Long-range pass arguments: the sorted order lists n*m entries, and K and V
-// are read from their group-sorted copies.
+// Long-range pass arguments: the sorted order lists n*m entries. With one
+// group per token K and V rows are read in place at the positions perm
+// gives (a head's rows must span fewer than 2^31 bytes, the reach of a
+// buffer resource); otherwise from group-sorted copies made by the prepare
+// call.
+bool long_range_direct(const AttnProblem& p) {
+    return p.m == 1 && (int64_t)p.n * p.d * 2 < ((int64_t)1 << 31);
+}
 AttnArgs long_range_args(const AttnProblem& p) {
     AttnArgs a = make_args(p);
     a.ne = p.n * p.m;
     a.ntiles = (a.ne + a.TT - 1) / a.TT;
     a.total = p.B * p.Hkv * a.nslices * a.ntiles;
-    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
-    char* base = static_cast<char*>(p.workspace);
-    a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
-    a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
+    a.direct = long_range_direct(p) ? 1 : 0;
+    if (!a.direct) {
+        const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
+        char* base = static_cast<char*>(p.workspace);
+        a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
+        a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
+    }
     return a;
 }
 
@@ -1278,13 +1325,16 @@ hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stre
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
     const AttnArgs a = long_range_args(p);
-    const int64_t chunks = (int64_t)(a.ne + KPOS_PAD) * (p.d / 8);
-    hipLaunchKernelGGL(attn_gather_kernel, dim3((unsigned)((chunks + 255) / 256), p.B * p.Hkv),
-                       dim3(256), 0, stream, p.k, p.v, p.perm, p.ids, p.n, a.ne, p.m, p.K,
-                       p.Hkv, p.d, const_cast<uint16_t*>(a.k), const_cast<uint16_t*>(a.v),
-                       a.spos);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (!a.direct) {
+        const int64_t chunks = (int64_t)(a.ne + KPOS_PAD) * (p.d / 8);
+        hipLaunchKernelGGL(attn_gather_kernel,
+                           dim3((unsigned)((chunks + 255) / 256), p.B * p.Hkv), dim3(256), 0,
+                           stream, p.k, p.v, p.perm, p.ids, p.n, a.ne, p.m, p.K, p.Hkv, p.d,
+                           const_cast<uint16_t*>(a.k), const_cast<uint16_t*>(a.v), a.spos);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
                        p.ids, p.perm, p.offsets, a.ne, p.m, p.K, p.w, a.TT, a.ntiles,
                        attn_tile_keys(p.d, kLongRange),

@@ -72,7 +72,8 @@ inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_w
 // Attention workspace, byte offsets: the window partial output (fp16
 // [B][Hq][n][d], scaled per row), its log2-sum-exp and scale exponent (fp32
 // pairs [B][Hq][n]), the tile plan, group-sorted copies of K and V (bf16
-// [B][Hkv][n*m][d]) and the sorted positions (int32 [B][n*m + pad]). With m
+// [B][Hkv][n*m][d]; used with m > 1, or when one head's K rows span 2^31
+// bytes or more) and the sorted positions (int32 [B][n*m + pad]). With m
 // groups per token (m > 1) the sorted order lists n*m membership entries,
 // and the long-range pass writes one partial per entry (fp16
 // [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge. Then the

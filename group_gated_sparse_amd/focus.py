@@ -322,8 +322,10 @@ def focus_attn_long_range_merge(q, k, v, group_ids, perm, group_offsets, K: int,
 def focus_attn_long_range_prepare(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
                                   scale: float, *, workspace, out, out_dtype=torch.bfloat16,
                                   lse=None, stream=None):
-    """First half of focus_attn_long_range_merge: the group-sorted K/V
-    copies, tile plan and order and row ends, written into workspace. It
+    """First half of focus_attn_long_range_merge: the tile plan and order,
+    the row ends and (with two groups per token, or key rows of one head
+    spanning 2^31 bytes or more) group-sorted K/V copies, written into
+    workspace. It
     reads only k, v and the group data (pass the out and lse that the apply
     call will get), so it may run beside focus_attn_window."""
     _attn_call("focus_attn_long_range_prepare", q, k, v, group_ids, perm, group_offsets, K,

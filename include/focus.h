@@ -222,9 +222,11 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
  * focus_attn_long_range_apply on one stream.
  *
  * focus_attn_long_range_prepare reads only k, v and the group data (q, out
- * and lse are checked, not read) and writes the group-sorted copies of K and
- * V, the query-tile plan and order and each sorted row's key-slot end into
- * the workspace. It writes no part of the workspace that focus_attn_window
+ * and lse are checked, not read) and writes the query-tile plan and order
+ * and each sorted row's key-slot end into the workspace; with two groups per
+ * token, or when one kv head's rows of K span 2^31 bytes or more, also
+ * group-sorted copies of K and V (otherwise the long-range pass reads key
+ * rows in place, at the positions perm gives). It writes no part of the workspace that focus_attn_window
  * writes, so it may run on another stream while the window pass runs, once
  * the sort is done. focus_attn_long_range_apply needs both (order them
  * before it with stream events): it runs the intra-group attention, merges
