@@ -1,7 +1,7 @@
 """Benchmark of the Focus forward pass on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--skip-cpu-baseline] [--skip-dense] [--cold-mall]
+                    [--skip-cpu-baseline] [--skip-dense] [--cold-mall] [--graph]
 
 One step = the whole hot path on one batch of seeded synthetic input already
 resident in HBM, all through the C ABI: focus_attn_window (the window pass,
@@ -67,6 +67,10 @@ def parse():
                     help="write a 512 MiB buffer before each timed step (outside its events), "
                          "so the step starts with nothing of its inputs in the 256 MB "
                          "Infinity Cache; the step time is then the HIP-event time")
+    ap.add_argument("--graph", action="store_true",
+                    help="also capture one whole step (both streams) into a HIP graph and time "
+                         "its replays; value and ms_per_step are then the replayed step's, the "
+                         "per-call times and the roofline come from the eager pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device-to-device copy (a reference "
                          "dispatch for calibrating HBM byte counters)")
@@ -423,6 +427,7 @@ def main():
                                                    workspace=ws_t, out=out)
 
     def step(evs=None):
+        stream = torch.cuda.current_stream()   # the capture stream under --graph
         def mark(i, st):
             if evs is not None:
                 evs[i].record(st)
@@ -476,6 +481,32 @@ def main():
     ev_step = span(0, 4)
     ms_step = ev_step if args.cold_mall else max(wall_ms, ev_step)
     per_step = sorted(evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps))
+    eager_ms = ms_step
+    if args.graph:
+        # The whole step captured once (window on the second stream, the rest on
+        # the capture stream) and replayed; the replay must equal the eager result.
+        if args.cold_mall:
+            raise SystemExit("--graph and --cold-mall are exclusive")
+        ref_out = out.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(max(args.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref_out):
+            raise RuntimeError("the replayed step differs from the eager step")
+        ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ge0.record(stream)
+        for _ in range(args.steps):
+            g.replay()
+        ge1.record(stream)
+        torch.cuda.synchronize()
+        g_wall = (time.perf_counter() - t0) * 1e3 / args.steps
+        ms_step = max(g_wall, ge0.elapsed_time(ge1) / args.steps)
+        log(f"graph replay: {ms_step:.4f} ms per step (eager {eager_ms:.4f})")
+        del g, ref_out
     log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
 
     gids = ids.cpu().numpy()
@@ -511,6 +542,7 @@ def main():
                    "groups_per_token": m, "out_dtype": "bf16",
                    "mall": "cold (512 MiB written before each step)" if args.cold_mall
                    else "warm",
+                   "launch": "HIP graph of the whole step, replayed" if args.graph else "eager",
                    "streams": "window pass overlapped with assign+sort" if overlap
                    else "one stream"},
         "visited_pairs_per_head": pairs,
@@ -518,6 +550,7 @@ def main():
         "long_range_pairs_per_head": lr,
         "long_range_pairs_visited_per_head": lr_visited,
         "phase_ms": phase,
+        "eager_ms_per_step": eager_ms,
         "step_ms_stats": {"median": float(np.median(per_step)), "min": per_step[0],
                           "max": per_step[-1]},
         "device": device_info(torch),
