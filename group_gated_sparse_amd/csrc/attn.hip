@@ -30,14 +30,15 @@
 // The two key sets {i-j <= w} and {i-j > w, same group} are disjoint, so
 // every allowed pair is counted exactly once.
 //
-// Per workgroup: 4 waves x 32 query rows. Per 64-key tile:
+// Per workgroup: 4 waves x 32 query rows. Per key tile (32 or 64 keys):
 //   S^T (keys x rows) = K Q^T   : A = K from LDS, B = Q^T held in registers
 //   online softmax per row in registers (one row per lane pair, exp2 domain)
 //   O^T (d x rows)  += V^T P^T  : A = V^T via LDS transposing reads
 //                                 (ds_read_b64_tr_b16), B = P^T in registers
 // with v_mfma_f32_32x32x16_bf16 and fp32 accumulation. K and V tiles are
-// copied HBM -> LDS by global_load_lds_dwordx4 into two LDS buffers: the copy
-// of tile t+1 runs while tile t is computed, one barrier per tile. The
+// copied HBM -> LDS by buffer_load_dwordx4 ... lds into two LDS buffers: the
+// copy of tile t+1 runs while tile t is computed, one barrier per tile. A
+// wave skips a tile none of its rows keeps. The
 // probabilities are taken against a reference max that is only moved (and
 // the accumulator rescaled) when a lane's probability sum for a tile exceeds
 // 2^8, so no per-tile max is computed on the common path, probabilities stay
