@@ -45,6 +45,7 @@
 // <= 256, and the final normalisation is exact either way.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <cstdlib>
 
 #include "focus_internal.h"
 
@@ -1293,7 +1294,11 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
 // gives (a head's rows must span fewer than 2^31 bytes, the reach of a
 // buffer resource); otherwise from group-sorted copies made by the prepare
 // call.
+// Setting FOCUS_LONG_RANGE_COPIES in the environment forces the copies for
+// one group per token too (read at every call, by prepare and apply alike,
+// so that tests can compare both paths).
 bool long_range_direct(const AttnProblem& p) {
+    if (std::getenv("FOCUS_LONG_RANGE_COPIES") != nullptr) return false;
     return p.m == 1 && (int64_t)p.n * p.d * 2 < ((int64_t)1 << 31);
 }
 AttnArgs long_range_args(const AttnProblem& p) {

@@ -358,3 +358,29 @@ def test_focus_attn_extreme_score_ranges(qscale):
         f"(bound {2.0 ** -8 * vmax + 1e-3:.3e})")
     assert err.max() <= 2.0 ** -8 * vmax + 1e-3 and err.mean() <= 1e-3
     assert np.max(np.abs(lse - rlse)) < 1e-3
+
+
+@pytest.mark.parametrize("case", [("copies_gqa8", 1, 16, 2, 700, 128, 7, 64),
+                                  ("copies_ragged_d64", 2, 3, 3, 333, 64, 5, 20)],
+                         ids=lambda c: c[0])
+def test_long_range_copy_path_equals_in_place(case, monkeypatch):
+    """With one group per token the long-range pass reads key rows in place;
+    the group-sorted copies it uses otherwise (two groups per token, or one
+    head's K rows spanning 2^31 bytes or more) are forced here through
+    FOCUS_LONG_RANGE_COPIES. Both load the same rows into each key tile, so
+    the outputs agree bit for bit, and both match the oracle."""
+    name, B, Hq, Hkv, n, d, K, w = case
+    say(f"[attn] {name}: B={B} Hq={Hq} Hkv={Hkv} n={n} d={d} K={K} w={w}")
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    scale = 1.0 / math.sqrt(d)
+    monkeypatch.delenv("FOCUS_LONG_RANGE_COPIES", raising=False)
+    out_a, lse_a, _, _ = _run_attn(q, k, v, ids, K, w, scale)
+    monkeypatch.setenv("FOCUS_LONG_RANGE_COPIES", "1")
+    out_b, lse_b, _, _ = _run_attn(q, k, v, ids, K, w, scale)
+    monkeypatch.delenv("FOCUS_LONG_RANGE_COPIES")
+    assert np.array_equal(out_a, out_b) and np.array_equal(lse_a, lse_b)
+    ref, rlse, _ = oracle.attn(q, k, v, ids, w, scale)
+    check_attn(out_b.reshape(-1, d), ref.reshape(-1, d), name)
+    assert np.max(np.abs(lse_b - rlse)) < 1e-3
