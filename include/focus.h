@@ -226,7 +226,8 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
  * and each sorted row's key-slot end into the workspace; with two groups per
  * token, or when one kv head's rows of K span 2^31 bytes or more, also
  * group-sorted copies of K and V (otherwise the long-range pass reads key
- * rows in place, at the positions perm gives). It writes no part of the workspace that focus_attn_window
+ * rows in place, at the positions perm gives; setting FOCUS_LONG_RANGE_COPIES
+ * in the environment makes both calls use the copies, for testing). It writes no part of the workspace that focus_attn_window
  * writes, so it may run on another stream while the window pass runs, once
  * the sort is done. focus_attn_long_range_apply needs both (order them
  * before it with stream events): it runs the intra-group attention, merges
