@@ -128,7 +128,8 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
                         const int32_t* group_ids, const int32_t* perm,
                         const int32_t* group_offsets, int B, int Hq, int Hkv, int n, int d, int K,
                         int m, int w, float scale, void* out, focus_dtype out_dtype, float* lse,
-                        void* workspace, size_t ws_bytes, focus_stream_t stream) {
+                        void* workspace, size_t ws_bytes, focus_stream_t stream,
+                        bool force_copies = false) {
     const AttnShape s{B, Hq, Hkv, n, d, K, w, m};
     focus_status st = check_attn_shape(s, true);
     if (st != FOCUS_OK) return st;
@@ -141,7 +142,9 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     }
     // the window pass only uses the leading part of the workspace, which
     // is laid out the same for every m
-    const size_t need = focus::attn_workspace(B, Hq, Hkv, n, d, w, part == AttnPart::kWindow ? 1 : m);
+    const size_t need = part == AttnPart::kWindow
+                            ? focus::attn_workspace(B, Hq, Hkv, n, d, w)
+                            : focus::attn_workspace(B, Hq, Hkv, n, d, w, m, force_copies);
     if (need > 0) {
         REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -156,7 +159,7 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     }
     focus::AttnProblem p{q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n, d, K, w, scale,
                          out, out_dtype == FOCUS_F32 ? 1 : 0, lse, need > 0 ? workspace : nullptr,
-                         m};
+                         m, force_copies ? 1 : 0};
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (part == AttnPart::kAll || part == AttnPart::kWindow) {
         hipError_t e = focus::launch_attn_window(p, hs);
@@ -346,6 +349,25 @@ focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
     return attn_entry(AttnPart::kAll, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n,
                       d_head, K, 1, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
                       stream);
+}
+
+size_t focus_attn_sorted_kv_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K,
+                                            int window) {
+    (void)K;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;
+    if (d_head != 32 && d_head != 64 && d_head != 128) return 0;
+    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, 1, true);
+}
+
+focus_status focus_attn_fwd_sorted_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      const int32_t* group_ids, const int32_t* perm,
+                                      const int32_t* group_offsets, int B, int Hq, int Hkv, int n,
+                                      int d_head, int K, int window, float scale, void* out,
+                                      focus_dtype out_dtype, float* lse, void* workspace,
+                                      size_t workspace_bytes, focus_stream_t stream) {
+    return attn_entry(AttnPart::kAll, q, k, v, group_ids, perm, group_offsets, B, Hq, Hkv, n,
+                      d_head, K, 1, window, scale, out, out_dtype, lse, workspace, workspace_bytes,
+                      stream, true);
 }
 
 focus_status focus_attn_window(const uint16_t* q, const uint16_t* k, const uint16_t* v,

@@ -42,10 +42,12 @@
 // probabilities are taken against a reference max that is only moved (and
 // the accumulator rescaled) when a lane's probability sum for a tile exceeds
 // 2^8, so no per-tile max is computed on the common path, probabilities stay
-// <= 256, and the final normalisation is exact either way.
+// <= 256, and the final normalisation is exact either way. Each row keeps two
+// sums: that of the probabilities as the PV product takes them (rounded to
+// bf16), which normalises the output, so the weights applied to V sum to one
+// exactly; and that of the fp32 probabilities, which gives the log-sum-exp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-#include <cstdlib>
 
 #include "focus_internal.h"
 
@@ -62,6 +64,7 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int NT = 256;      // threads per workgroup
@@ -496,6 +499,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     int ntl = 0;
     int kstart = 0, kend0 = 0;               // sequence-order passes
     int gfirst = 0, g_i = -1;                // long-range pass
+    int nseg_tile = 1;                       // long-range pass: group segments of this tile
     int x_i = -1;                            // multi pass: excluded key group, or -1
     bool rows_one_group = false, rows_excl = false;
     if (!SORTED) {
@@ -554,7 +558,13 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             }
             __syncthreads();
         }
-        ntl = __builtin_amdgcn_readfirstlane(seg_t0[nseg]);
+        // Key tiles in total, bounded by what nseg segments of at most ne
+        // slots each can hold, and the segment count kept for the cursor:
+        // a plan that does not match the data gives wrong numbers, but the
+        // loops below still end.
+        nseg_tile = __builtin_amdgcn_readfirstlane(nseg);
+        ntl = __builtin_amdgcn_readfirstlane(
+            clampi(seg_t0[nseg], 0, nseg * ((ne + BN - 1) / BN)));
         // the row's group: segments are consecutive in sorted order
         if (rvalid) {
             int t = 0;
@@ -597,7 +607,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             full = (kt0 + BN - 1 <= q0) && (kt0 + BN <= kend) &&
                    (CAUSAL_ALL || kend - 1 - kt0 <= a.w);
         } else {
-            while (c.t1 <= tau) {
+            while (c.t1 <= tau && c.seg + 1 < nseg_tile) {
                 ++c.seg;
                 seg_load(c);
             }
@@ -749,7 +759,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
-    float m_ref = kNegInf, l_run = 0.0f;
+    // l_run: sum of the fp32 probabilities (log-sum-exp); l_pv: sum of the
+    // bf16-rounded probabilities the PV MFMAs multiply (output normaliser)
+    float m_ref = kNegInf, l_run = 0.0f, l_pv = 0.0f;
     bf16x8 qf[G::KS];  // Q^T fragments, loaded once the first key tile is in flight
     bf16x8 gq[KG / 16][2];  // soft-gated pass: the row's assignment (hi, lo) fragments
 
@@ -879,8 +891,11 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         // them exceeds 2^8 (some score grew more than 8 in log2 units past
         // m_ref), or a row has no reference yet, is the reference moved to
         // the tile max, the accumulator rescaled and the tile recomputed.
-        // Either way every probability is <= 2^8; the row sum adds them in
-        // fp32 and the PV product takes them rounded to bf16.
+        // Either way every probability is <= 2^8. The PV product takes them
+        // rounded to bf16; the output normaliser adds exactly those rounded
+        // values (two per v_dot2c_f32_bf16 against (1, 1)), so the weights
+        // applied to V sum to one and a row whose weight sits on few keys
+        // carries no normalisation bias; the log-sum-exp adds the fp32 values.
         bf16x8 pf[G::KB][2];
         float psum;
         auto probs = [&](float m_use) {
@@ -914,6 +929,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             const float m_new = fmaxf(m_ref, tmax);
             const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
             l_run *= alpha;
+            l_pv *= alpha;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
@@ -922,6 +938,18 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             probs(m_ref == kNegInf ? 0.0f : m_ref);
         }
         l_run += psum;
+        {
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const bf16x2 pair = {pf[kb][sp][2 * j], pf[kb][sp][2 * j + 1]};
+                        l_pv = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_pv, false);
+                    }
+        }
 
         // O^T += V^T P^T. For k-step (kb, sp) the B slots 0..3 / 4..7 of lane
         // half hh hold keys kb*32+16*sp+4*hh+{0..3} / +8+{0..3}; the A operand
@@ -978,8 +1006,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     };
     auto set_scale = [&]() {
         m_ref = le_in[0] + le_in[1];
-        // halves are summed at the end
+        // halves are summed at the end; the partial's weight enters both sums
         l_run = (hh == 0) ? __builtin_ldexpf(1.0f, -(int)le_in[1]) : 0.0f;
+        l_pv = l_run;
     };
     if (merging) {
         const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;
@@ -1081,12 +1110,14 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     }
 
     // Epilogue. Lane holds rows' O^T entries d = db*32 + 8*i + 4*hh + j at
-    // acc[db][4*i + j]; l_run covers this lane half's keys. The rows are
-    // written to LDS (chunk slots XOR-swizzled by row) and stored as whole
-    // contiguous rows.
+    // acc[db][4*i + j]; l_run and l_pv cover this lane half's keys. The rows
+    // are written to LDS (chunk slots XOR-swizzled by row) and stored as
+    // whole contiguous rows. O is normalised by l_pv (the weights it was
+    // accumulated with), the log-sum-exp comes from l_run.
     const float l_tot = l_run + other_half(l_run);
+    const float l_pv_tot = l_pv + other_half(l_pv);
     const int64_t row = ((int64_t)b * a.Hq + h) * ne + ent_i;   // output row
-    float scale_o = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float scale_o = l_pv_tot > 0.0f ? 1.0f / l_pv_tot : 0.0f;
     int esize;
     if (a.partial) {
         // 16-bit partial with a per-row power-of-two scale: O~ = O * 2^-e
@@ -1265,7 +1296,7 @@ AttnArgs make_args(const AttnProblem& p) {
     a.sl2 = p.scale * 1.44269504088896340736f;
     a.out_f32 = p.out_f32;
     if (p.workspace) {
-        const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
+        const AttnWorkspace ws = attn_workspace_layout(p);
         char* base = static_cast<char*>(p.workspace);
         a.og = reinterpret_cast<_Float16*>(base + ws.og);
         a.lseg = reinterpret_cast<f32x2*>(base + ws.lseg);
@@ -1289,26 +1320,19 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Long-range pass arguments: the sorted order lists n*m entries. With one
-// group per token K and V rows are read in place at the positions perm
-// gives (a head's rows must span fewer than 2^31 bytes, the reach of a
-// buffer resource); otherwise from group-sorted copies made by the prepare
-// call.
-// Setting FOCUS_LONG_RANGE_COPIES in the environment forces the copies for
-// one group per token too (read at every call, by prepare and apply alike,
-// so that tests can compare both paths).
-bool long_range_direct(const AttnProblem& p) {
-    if (std::getenv("FOCUS_LONG_RANGE_COPIES") != nullptr) return false;
-    return p.m == 1 && (int64_t)p.n * p.d * 2 < ((int64_t)1 << 31);
-}
+// Long-range pass arguments: the sorted order lists n*m entries. K and V
+// rows are read in place at the positions perm gives, or from group-sorted
+// copies made by the prepare call (attn_sorted_copies: two groups per token,
+// a head's rows beyond a buffer resource's 2^31-byte reach, or asked for).
+// The choice depends only on the problem, so prepare and apply agree.
 AttnArgs long_range_args(const AttnProblem& p) {
     AttnArgs a = make_args(p);
     a.ne = p.n * p.m;
     a.ntiles = (a.ne + a.TT - 1) / a.TT;
     a.total = p.B * p.Hkv * a.nslices * a.ntiles;
-    a.direct = long_range_direct(p) ? 1 : 0;
+    a.direct = attn_sorted_copies(p.n, p.d, p.m, p.force_copies != 0) ? 0 : 1;
     if (!a.direct) {
-        const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
+        const AttnWorkspace ws = attn_workspace_layout(p);
         char* base = static_cast<char*>(p.workspace);
         a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
         a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
@@ -1370,7 +1394,7 @@ hipError_t launch_attn_long_range_apply(const AttnProblem& p, hipStream_t stream
         return launch<kLongRange>(a, p.d, stream);
     }
     // Two groups per token: one partial per entry, then the merge.
-    const AttnWorkspace ws = attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m);
+    const AttnWorkspace ws = attn_workspace_layout(p);
     char* base = static_cast<char*>(p.workspace);
     _Float16* oge = reinterpret_cast<_Float16*>(base + ws.oge);
     f32x2* lsege = reinterpret_cast<f32x2*>(base + ws.lsege);

@@ -57,6 +57,7 @@ struct AttnProblem {
     float* lse;
     void* workspace;
     int m = 1;     // groups per token: ids [B][n][m]; perm holds entries t*m + c
+    int force_copies = 0;   // long-range pass from group-sorted K/V copies at any size
 };
 
 // True when some pair further apart than the window can exist (n - 1 > w).
@@ -69,21 +70,31 @@ constexpr int PLAN_INTS = 32;   // ints per plan record (4 + 4 * SEGCAP)
 int attn_heads_per_wg(int hpk);
 inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_wg(Hq / Hkv); }
 
+// Whether the long-range pass reads group-sorted copies of K and V (made by
+// its prepare step) rather than key rows in place: always with two groups
+// per token; with one, when a kv head's K rows span 2^31 bytes or more (the
+// reach of a buffer resource), or when the caller asks for the copies.
+inline bool attn_sorted_copies(int n, int d, int m, bool force) {
+    return force || m > 1 || (int64_t)n * d * 2 >= ((int64_t)1 << 31);
+}
+
 // Attention workspace, byte offsets: the window partial output (fp16
 // [B][Hq][n][d], scaled per row), its log2-sum-exp and scale exponent (fp32
-// pairs [B][Hq][n]), the tile plan, group-sorted copies of K and V (bf16
-// [B][Hkv][n*m][d]; used with m > 1, or when one head's K rows span 2^31
-// bytes or more) and the sorted positions (int32 [B][n*m + pad]). With m
-// groups per token (m > 1) the sorted order lists n*m membership entries,
-// and the long-range pass writes one partial per entry (fp16
-// [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge. Then the
-// order in which the long-range pass takes the sorted query tiles (int32
-// [B][tiles], most work first) and, with one group per token, the end of
-// the key slots each sorted row keeps (int32 [B][n]).
+// pairs [B][Hq][n]), the tile plan, the order in which the long-range pass
+// takes the sorted query tiles (int32 [B][tiles], most work first) and, with
+// one group per token, the end of the key slots each sorted row keeps (int32
+// [B][n]). With sorted copies (attn_sorted_copies) also the group-sorted K
+// and V (bf16 [B][Hkv][n*m][d]) and the sorted slots' positions (int32
+// [B][n*m + pad]). With m groups per token (m > 1) the sorted order lists
+// n*m membership entries, and the long-range pass writes one partial per
+// entry (fp16 [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge.
+// The first two regions lead every layout, so the window pass, which uses
+// only them, takes the same offsets for every m.
 struct AttnWorkspace {
-    size_t og, lseg, plan, ks, vs, spos, oge, lsege, order, rowend, total;
+    size_t og, lseg, plan, order, rowend, ks, vs, spos, oge, lsege, total;
 };
-inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m = 1) {
+inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m,
+                                           bool copies) {
     AttnWorkspace w{};
     const int TT = attn_tokens_per_tile(Hq, Hkv);
     const size_t ne = (size_t)n * m;
@@ -92,20 +103,27 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d,
     w.og = off;   off += align_up((size_t)B * Hq * n * d * 2);
     w.lseg = off; off += align_up((size_t)B * Hq * n * 8);
     w.plan = off; off += align_up((size_t)B * ntiles * PLAN_INTS * 4);
-    w.ks = off;   off += align_up((size_t)B * Hkv * ne * d * 2);
-    w.vs = off;   off += align_up((size_t)B * Hkv * ne * d * 2);
-    w.spos = off; off += align_up((size_t)B * (ne + KPOS_PAD) * 4);
-    w.oge = off;  off += m > 1 ? align_up((size_t)B * Hq * ne * d * 2) : 0;
-    w.lsege = off; off += m > 1 ? align_up((size_t)B * Hq * ne * 8) : 0;
     w.order = off; off += align_up((size_t)B * ntiles * 4);
     w.rowend = off; off += m == 1 ? align_up((size_t)B * n * 4) : 0;
+    w.ks = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
+    w.vs = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
+    w.spos = off; off += copies ? align_up((size_t)B * (ne + KPOS_PAD) * 4) : 0;
+    w.oge = off;  off += m > 1 ? align_up((size_t)B * Hq * ne * d * 2) : 0;
+    w.lsege = off; off += m > 1 ? align_up((size_t)B * Hq * ne * 8) : 0;
     w.total = off;
     return w;
 }
-inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w, int m = 1) {
-    if (!attn_has_long_range(n, w)) return 0;
-    return attn_workspace_layout(B, Hq, Hkv, n, d, m).total;
+inline AttnWorkspace attn_workspace_layout(const AttnProblem& p) {
+    return attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m,
+                                 attn_sorted_copies(p.n, p.d, p.m, p.force_copies != 0));
 }
+inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w, int m = 1,
+                             bool force_copies = false) {
+    if (!attn_has_long_range(n, w)) return 0;
+    return attn_workspace_layout(B, Hq, Hkv, n, d, m, attn_sorted_copies(n, d, m, force_copies))
+        .total;
+}
+
 // The long-range pass: prepare (sorted K/V copies, tile plan and order, row
 // ends; needs only k, v and the group data) then apply (the attention, merged
 // with the window partial); launch_attn_long_range runs both.

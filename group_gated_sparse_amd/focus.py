@@ -38,6 +38,9 @@ _SIGNATURES = {
     "focus_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "focus_attn_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p,
                         _sz, _p], _i),
+    "focus_attn_sorted_kv_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
+    "focus_attn_fwd_sorted_kv": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
+                                  _p, _p, _sz, _p], _i),
     "focus_attn_window": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i,
                                _p, _p, _sz, _p], _i),
     "focus_attn_long_range_merge": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p,
@@ -115,13 +118,26 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _workspace(nbytes: int, device, given: Optional[torch.Tensor]):
+def _new(shape, dtype, device, stream) -> torch.Tensor:
+    """A tensor the binding allocates for a call enqueued on `stream`.
+
+    torch's caching allocator ties a block to the stream current at
+    allocation; when the kernels run on another stream, record_stream keeps
+    the block from being handed out again (e.g. a workspace dropped on
+    return) until the work queued on that stream has passed it."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(t.device):
+        t.record_stream(stream)
+    return t
+
+
+def _workspace(nbytes: int, device, given: Optional[torch.Tensor], stream=None):
     if nbytes == 0:
         return given
     if given is not None:
         _need(given, "workspace", torch.uint8)
         return given
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _new(nbytes, torch.uint8, device, stream)
 
 
 # ---------------------------------------------------------------------------
@@ -158,14 +174,14 @@ def _assign(hidden, P, C, bias, m, group_ids, margin, want_margin, workspace, st
     dev = hidden.device
     ids_shape = (B, n) if m == 1 else (B, n, m)
     if group_ids is None:
-        group_ids = torch.empty(ids_shape, dtype=torch.int32, device=dev)
+        group_ids = _new(ids_shape, torch.int32, dev, stream)
     _need(group_ids, "group_ids", torch.int32, ids_shape)
     if margin is None and want_margin:
-        margin = torch.empty((B, n), dtype=torch.float32, device=dev)
+        margin = _new((B, n), torch.float32, dev, stream)
     if margin is not None:
         _need(margin, "margin", torch.float32, (B, n))
     nbytes = focus_assign_workspace_bytes(d_model, K)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     _check_status(lib().focus_assign_topk(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n,
                                           d_model, d_proj, K, int(m), _ptr(group_ids),
                                           _ptr(margin), _ptr(ws),
@@ -186,9 +202,9 @@ def focus_assign_scores(hidden: torch.Tensor, P: torch.Tensor, C: torch.Tensor,
     if bias is not None:
         _need(bias, "bias", torch.float32, (K,))
     if scores is None:
-        scores = torch.empty((B, n, K), dtype=torch.float32, device=hidden.device)
+        scores = _new((B, n, K), torch.float32, hidden.device, stream)
     _need(scores, "scores", torch.float32, (B, n, K))
-    ws = _workspace(focus_assign_workspace_bytes(d_model, K), hidden.device, workspace)
+    ws = _workspace(focus_assign_workspace_bytes(d_model, K), hidden.device, workspace, stream)
     _check_status(lib().focus_assign_scores(_ptr(hidden), _ptr(P), _ptr(C), _ptr(bias), B, n,
                                             d_model, d_proj, K, _ptr(scores), _ptr(ws),
                                             0 if ws is None else ws.numel(), _stream(stream)))
@@ -206,9 +222,10 @@ def focus_sinkhorn(scores: torch.Tensor, tau: float, iters: int, *, G=None, work
     _need(scores, "scores", torch.float32)
     B, n, K = scores.shape
     if G is None:
-        G = torch.empty_like(scores)
+        G = _new(scores.shape, torch.float32, scores.device, stream)
     _need(G, "G", torch.float32, (B, n, K))
-    ws = _workspace(focus_sinkhorn_workspace_bytes(B, n, K, iters), scores.device, workspace)
+    ws = _workspace(focus_sinkhorn_workspace_bytes(B, n, K, iters), scores.device, workspace,
+                    stream)
     _check_status(lib().focus_sinkhorn(_ptr(scores), B, n, K, float(tau), int(iters), _ptr(G),
                                        _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(stream)))
@@ -230,13 +247,13 @@ def focus_group_sort(group_ids: torch.Tensor, K: int, *, perm=None, group_offset
     B, n = group_ids.shape
     dev = group_ids.device
     if perm is None:
-        perm = torch.empty((B, n), dtype=torch.int32, device=dev)
+        perm = _new((B, n), torch.int32, dev, stream)
     if group_offsets is None:
-        group_offsets = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+        group_offsets = _new((B, K + 1), torch.int32, dev, stream)
     _need(perm, "perm", torch.int32, (B, n))
     _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
     nbytes = focus_group_sort_workspace_bytes(B, n, K)
-    ws = _workspace(nbytes, dev, workspace)
+    ws = _workspace(nbytes, dev, workspace, stream)
     _check_status(lib().focus_group_sort(_ptr(group_ids), B, n, K, _ptr(perm),
                                          _ptr(group_offsets), _ptr(ws),
                                          0 if ws is None else ws.numel(), _stream(stream)))
@@ -246,6 +263,11 @@ def focus_group_sort(group_ids: torch.Tensor, K: int, *, perm=None, group_offset
 def focus_attn_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K: int,
                                window: int) -> int:
     return int(lib().focus_attn_workspace_bytes(B, Hq, Hkv, n, d_head, K, window))
+
+
+def focus_attn_sorted_kv_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K: int,
+                                         window: int) -> int:
+    return int(lib().focus_attn_sorted_kv_workspace_bytes(B, Hq, Hkv, n, d_head, K, window))
 
 
 def focus_attn_topk_workspace_bytes(B: int, Hq: int, Hkv: int, n: int, d_head: int, K: int,
@@ -268,19 +290,21 @@ def _attn_call(fn_name, q, k, v, group_ids, perm, group_offsets, K, window, scal
     if needs_groups or group_offsets is not None:
         _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
     if out is None:
-        out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
+        out = _new((B, Hq, n, d), out_dtype, q.device, stream)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     _need(out, "out", out.dtype, (B, Hq, n, d))
     if lse is None and want_lse:
-        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+        lse = _new((B, Hq, n), torch.float32, q.device, stream)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, n))
-    if m is None:
+    if fn_name == "focus_attn_fwd_sorted_kv":
+        nbytes = focus_attn_sorted_kv_workspace_bytes(B, Hq, Hkv, n, d, K, window)
+    elif m is None:
         nbytes = focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, window)
     else:
         nbytes = focus_attn_topk_workspace_bytes(B, Hq, Hkv, n, d, K, m, window)
-    ws = _workspace(nbytes, q.device, workspace)
+    ws = _workspace(nbytes, q.device, workspace, stream)
     dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
     fn = getattr(lib(), fn_name)
     shape_args = (B, Hq, Hkv, n, d, K) if m is None else (B, Hq, Hkv, n, d, K, int(m))
@@ -297,6 +321,18 @@ def focus_attn_fwd(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
     Returns (out, lse or None)."""
     out, lse, _ = _attn_call("focus_attn_fwd", q, k, v, group_ids, perm, group_offsets, K,
                              window, scale, out, out_dtype, lse, want_lse, workspace, stream)
+    return out, lse
+
+
+def focus_attn_fwd_sorted_kv(q, k, v, group_ids, perm, group_offsets, K: int, window: int,
+                             scale: float, *, out=None, out_dtype=torch.bfloat16, lse=None,
+                             want_lse: bool = False, workspace=None, stream=None):
+    """focus_attn_fwd with the long-range pass reading group-sorted copies of
+    K and V (gathered by its preparation) instead of key rows in place; the
+    library takes this path by itself only for very long rows. Same result,
+    bit for bit. Returns (out, lse or None)."""
+    out, lse, _ = _attn_call("focus_attn_fwd_sorted_kv", q, k, v, group_ids, perm, group_offsets,
+                             K, window, scale, out, out_dtype, lse, want_lse, workspace, stream)
     return out, lse
 
 
@@ -393,10 +429,10 @@ def dense_causal_attn_fwd(q, k, v, scale: float, *, out=None, out_dtype=torch.bf
     _need(k, "k", torch.bfloat16, (B, Hkv, n, d))
     _need(v, "v", torch.bfloat16, (B, Hkv, n, d))
     if out is None:
-        out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
+        out = _new((B, Hq, n, d), out_dtype, q.device, stream)
     _need(out, "out", out.dtype, (B, Hq, n, d))
     if lse is None and want_lse:
-        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+        lse = _new((B, Hq, n), torch.float32, q.device, stream)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, n))
     dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
@@ -426,15 +462,16 @@ def focus_soft_gate_attn_fwd(q, k, v, G, window: int, scale: float, lam: float, 
         raise ValueError(f"G must have shape (B, n, K) = ({B}, {n}, K)")
     K = G.shape[2]
     if out is None:
-        out = torch.empty((B, Hq, n, d), dtype=out_dtype, device=q.device)
+        out = _new((B, Hq, n, d), out_dtype, q.device, stream)
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bfloat16 or float32")
     _need(out, "out", out.dtype, (B, Hq, n, d))
     if lse is None and want_lse:
-        lse = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+        lse = _new((B, Hq, n), torch.float32, q.device, stream)
     if lse is not None:
         _need(lse, "lse", torch.float32, (B, Hq, n))
-    ws = _workspace(focus_soft_gate_attn_workspace_bytes(B, n, K), q.device, workspace)
+    ws = _workspace(focus_soft_gate_attn_workspace_bytes(B, n, K), q.device, workspace,
+                    stream)
     dt = FOCUS_F32 if out.dtype == torch.float32 else FOCUS_BF16
     _check_status(lib().focus_soft_gate_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(G), B, Hq, Hkv,
                                                  n, d, K, window, float(scale), float(lam),

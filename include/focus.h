@@ -55,7 +55,7 @@ typedef enum {
 
 typedef enum { FOCUS_BF16 = 0, FOCUS_F32 = 1 } focus_dtype;
 
-#define FOCUS_ABI_VERSION 3
+#define FOCUS_ABI_VERSION 4
 #define FOCUS_MAX_GROUPS 64
 #define FOCUS_MAX_MEMBERSHIPS 2 /* groups per token (m) of the top-k variant */
 #define FOCUS_MAX_SINKHORN_ITERS 10000
@@ -138,6 +138,15 @@ focus_status focus_sinkhorn(const float* scores, int B, int n, int K, float tau,
 /* ------------------------------------------------------------------------
  * Step 2: stable grouping of tokens (counting sort per batch element).
  *
+ * The grouping the method rests on (Japanese page §2, opening: tokens are
+ * gathered into groups by learnable centroids and far attention is limited
+ * to pairs inside one group; §2.2: at inference, far pairs of different
+ * groups are skipped, not zeroed; Korean page §2.3: the sparse pattern splits
+ * into a local-window call and an intra-group long-range call). The
+ * intra-group call attends each group's tokens among themselves, so the
+ * tokens are laid out group by group, in sequence order inside each group;
+ * this is that layout.
+ *
  * group_offsets[b][k] = number of tokens of batch b whose id is < k (K+1
  *                       entries; empty groups repeat an offset)
  * perm[b][group_offsets[b][g] + r] = t, the r-th token (in increasing t)
@@ -191,6 +200,26 @@ focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
                             float scale, void* out, focus_dtype out_dtype, float* lse,
                             void* workspace, size_t workspace_bytes, focus_stream_t stream);
 
+/* focus_attn_fwd with the long-range pass reading group-sorted copies of K
+ * and V, which its preparation gathers into the workspace, instead of key
+ * rows in place at the positions perm gives. focus_attn_fwd takes this path
+ * by itself when one kv head's rows of K span 2^31 bytes or more (beyond a
+ * buffer resource's reach), and the top-k calls always take it; this entry
+ * point takes it at any size, so the path can be checked against the in-place
+ * one (both load the same rows into every key tile, so the results agree bit
+ * for bit). Same arguments and semantics as focus_attn_fwd; the workspace is
+ * focus_attn_sorted_kv_workspace_bytes() bytes (the sorted K and V add
+ * 2 * B * Hkv * n * d_head * 2 bytes to focus_attn_workspace_bytes()). */
+size_t focus_attn_sorted_kv_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K,
+                                            int window);
+focus_status focus_attn_fwd_sorted_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      const int32_t* group_ids, const int32_t* perm,
+                                      const int32_t* group_offsets,
+                                      int B, int Hq, int Hkv, int n, int d_head, int K,
+                                      int window, float scale, void* out, focus_dtype out_dtype,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      focus_stream_t stream);
+
 /* The two passes of focus_attn_fwd as separate calls, with the same
  * arguments and the same workspace, which carries the window partial result
  * from the first call to the second: focus_attn_fwd == focus_attn_window
@@ -226,10 +255,10 @@ focus_status focus_attn_long_range_merge(const uint16_t* q, const uint16_t* k, c
  * and each sorted row's key-slot end into the workspace; with two groups per
  * token, or when one kv head's rows of K span 2^31 bytes or more, also
  * group-sorted copies of K and V (otherwise the long-range pass reads key
- * rows in place, at the positions perm gives; setting FOCUS_LONG_RANGE_COPIES
- * in the environment makes both calls use the copies, for testing). It writes no part of the workspace that focus_attn_window
- * writes, so it may run on another stream while the window pass runs, once
- * the sort is done. focus_attn_long_range_apply needs both (order them
+ * rows in place, at the positions perm gives). Which of the two the calls
+ * take depends only on the shape, so prepare and apply always agree. It
+ * writes no part of the workspace that focus_attn_window writes, so it may
+ * run on another stream while the window pass runs, once the sort is done. focus_attn_long_range_apply needs both (order them
  * before it with stream events): it runs the intra-group attention, merges
  * the window partial and writes out and lse. */
 focus_status focus_attn_long_range_prepare(const uint16_t* q, const uint16_t* k,
@@ -340,9 +369,16 @@ focus_status focus_soft_gate_attn_fwd(const uint16_t* q, const uint16_t* k, cons
                                       size_t workspace_bytes, focus_stream_t stream);
 
 /* ------------------------------------------------------------------------
- * Baseline: plain causal attention (every pair j <= i), the "full attention"
- * the Focus pages compare against. Same layouts and limits as above; needs no
- * workspace.
+ * Baseline: plain causal attention (every pair j <= i), the full attention
+ * the Focus pages measure their speed-ups against (Korean page §2.3: 2x to
+ * 8.6x over it with two FlashAttention calls; §3.4 and Japanese page §3.3:
+ * 8.6x wall-clock at one million tokens, 2x with top-2 membership at K = 4).
+ * It runs on the same kernel core as the Focus passes, so the speed-up of
+ * focus_attn_fwd over it isolates the pairs skipped. Same layouts and limits
+ * as above; needs no workspace.
+ *
+ *   out[b][h][i] = sum_{j <= i} softmax_j(scale * q_i . k_j) v_j
+ *   lse[b][h][i] = log sum_{j <= i} exp(scale * q_i . k_j)   (natural log)
  * ---------------------------------------------------------------------- */
 focus_status dense_causal_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    int B, int Hq, int Hkv, int n, int d_head, float scale,

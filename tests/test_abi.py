@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert name in exported, f"{name} is declared but not exported"
         assert getattr(lib, name) is not None
-    assert lib.focus_abi_version() == 3
+    assert lib.focus_abi_version() == 4
 
 
 def _err():
@@ -117,11 +117,21 @@ def test_workspace_sizes():
     assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 256
     assert lib.focus_group_sort_workspace_bytes(1, 65536, 64) == 32 * 64 * 4
     # partial fp16 [B][Hq][n][d] + (lse, exponent) fp32 pairs [B][Hq][n] + 128 B plan per query
-    # tile (here 64 tokens x 2 heads) + sorted bf16 K and V [B][Hkv][n][d] + int32 sorted
-    # positions [B][n + 256] + int32 tile order [B][tiles] + int32 end of each sorted row's keys
-    # [B][n], each region 256-byte aligned
-    assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == (
-        256 * 2 * 32 * 2 + 4096 + 4 * 128 + 2 * (256 * 32 * 2) + 512 * 4 + 256 + 256 * 4)
+    # tile (here 64 tokens x 2 heads) + int32 tile order [B][tiles] + int32 end of each sorted
+    # row's keys [B][n], each region 256-byte aligned; key rows are read in place, so no
+    # sorted copies of K and V are reserved
+    in_place = 256 * 2 * 32 * 2 + 4096 + 4 * 128 + 256 + 256 * 4
+    assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == in_place
+    # the sorted-copy path adds sorted bf16 K and V [B][Hkv][n][d] and int32 sorted positions
+    # [B][n + 256]
+    assert lib.focus_attn_sorted_kv_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == (
+        in_place + 2 * (256 * 32 * 2) + 512 * 4)
+    assert lib.focus_attn_sorted_kv_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
+    assert lib.focus_attn_sorted_kv_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
+    # the bench workload (70B GQA, n = 32768): no 134 MB of sorted K and V on the in-place path
+    big = lib.focus_attn_workspace_bytes(1, 64, 8, 32768, 128, 32, 1024)
+    assert lib.focus_attn_sorted_kv_workspace_bytes(1, 64, 8, 32768, 128, 32, 1024) - big == (
+        2 * 8 * 32768 * 128 * 2 + (32768 + 256) * 4)
     # no pair can be further apart than the window: no partial needed
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 255) == 0
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 48, 4, 32) == 0
@@ -173,7 +183,7 @@ def _attn(fn="focus_attn_fwd", **kw):
              args["out"], args["dt"], args["lse"], args["ws"], args["wsb"], args["stream"])
 
 
-@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_window",
+@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_fwd_sorted_kv", "focus_attn_window",
                                 "focus_attn_long_range_merge", "focus_attn_long_range_prepare",
                                 "focus_attn_long_range_apply"])
 @pytest.mark.parametrize("kw,code,msg", [
@@ -204,8 +214,9 @@ def test_attn_rejects(fn, kw, code, msg):
     assert msg in _err()
 
 
-@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_long_range_merge",
-                                "focus_attn_long_range_prepare", "focus_attn_long_range_apply"])
+@pytest.mark.parametrize("fn", ["focus_attn_fwd", "focus_attn_fwd_sorted_kv",
+                                "focus_attn_long_range_merge", "focus_attn_long_range_prepare",
+                                "focus_attn_long_range_apply"])
 @pytest.mark.parametrize("kw,msg", [(dict(ids=None), "group_ids"), (dict(perm=None), "perm"),
                                     (dict(offs=None), "group_offsets")])
 def test_attn_passes_needing_groups_reject_missing_group_data(fn, kw, msg):
@@ -334,6 +345,18 @@ def test_assign_scores_rejects():
     assert f(A, Bp, C_, None, 1, 8, 64, 16, 4, A + 64, E_, 1 << 20, None) == INVALID
     assert "overlap" in _err()
     assert f(A, Bp, C_, None, 1, 8, 64, 16, 0, D_, E_, 1 << 20, None) == UNSUPPORTED
+
+
+def test_sorted_kv_call_needs_the_larger_workspace():
+    """focus_attn_fwd_sorted_kv validates against its own, larger workspace
+    size: the in-place size is rejected before anything is enqueued."""
+    lib = focus.lib()
+    small = lib.focus_attn_workspace_bytes(1, 4, 2, 256, 64, 4, 16)
+    big = lib.focus_attn_sorted_kv_workspace_bytes(1, 4, 2, 256, 64, 4, 16)
+    assert small < big
+    assert _attn("focus_attn_fwd_sorted_kv", wsb=small) == WORKSPACE
+    assert "too small" in _err()
+    assert _attn("focus_attn_fwd_sorted_kv", wsb=big - 1) == WORKSPACE
 
 
 def test_window_pass_takes_no_group_data():
