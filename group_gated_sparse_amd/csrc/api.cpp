@@ -333,6 +333,38 @@ focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K, int
                          "group sort launch");
 }
 
+static_assert(focus::kSortScratchBytes == FOCUS_SORT_NOALLOC_SCRATCH_BYTES,
+              "the header states the size of the sort's static scratch");
+
+focus_status focus_group_sort_noalloc(const int32_t* group_ids, int B, int n, int K,
+                                      int32_t* perm, int32_t* group_offsets,
+                                      focus_stream_t stream) {
+    REQUIRE(B >= 1 && n >= 1, FOCUS_ERR_INVALID_ARGUMENT, "B and n must be >= 1 (got B=%d n=%d)",
+            B, n);
+    REQUIRE(K >= 1 && K <= FOCUS_MAX_GROUPS, FOCUS_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)",
+            FOCUS_MAX_GROUPS, K);
+    REQUIRE(B <= 65535, FOCUS_ERR_UNSUPPORTED, "B must be <= 65535 (got %d)", B);
+    REQUIRE_PTR(group_ids, 4);
+    REQUIRE_PTR(perm, 4);
+    REQUIRE_PTR(group_offsets, 4);
+    const size_t nb = (size_t)B * n * 4;
+    REQUIRE(!overlaps(perm, nb, group_ids, nb) &&
+                !overlaps(group_offsets, (size_t)B * (K + 1) * 4, group_ids, nb) &&
+                !overlaps(group_offsets, (size_t)B * (K + 1) * 4, perm, nb),
+            FOCUS_ERR_INVALID_ARGUMENT, "group_ids, perm and group_offsets must not overlap");
+    const size_t need = focus::group_sort_workspace(B, n, K);
+    REQUIRE(need <= focus::kSortScratchBytes, FOCUS_ERR_UNSUPPORTED,
+            "the sort needs %zu bytes of scratch and the library's static scratch holds %zu "
+            "(B * ceil(n / 2048) * K * 4 bytes); call focus_group_sort with a workspace",
+            need, focus::kSortScratchBytes);
+    int32_t* scratch = nullptr;
+    const hipError_t e = focus::group_sort_scratch(&scratch);
+    if (e != hipSuccess) return device_status(e, "sort scratch address");
+    return device_status(focus::launch_group_sort(group_ids, B, n, K, perm, group_offsets,
+                                                  scratch, static_cast<hipStream_t>(stream)),
+                         "group sort launch");
+}
+
 size_t focus_attn_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int window) {
     (void)K;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;

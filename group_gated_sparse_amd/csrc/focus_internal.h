@@ -41,6 +41,11 @@ constexpr int SORT_BLOCK_TOKENS = 2048;  // tokens per workgroup of the two sort
 size_t group_sort_workspace(int B, int n, int K);
 hipError_t launch_group_sort(const int32_t* ids, int B, int n, int K, int32_t* perm,
                              int32_t* offsets, void* workspace, hipStream_t stream);
+// The library's own scratch for the sort (focus_group_sort_noalloc): a
+// static device array of kSortScratchBytes; group_sort_scratch gives its
+// address on the current device (looked up once per device).
+constexpr size_t kSortScratchBytes = (size_t)1 << 20;
+hipError_t group_sort_scratch(int32_t** ptr);
 
 // ---- attention --------------------------------------------------------------
 struct AttnProblem {

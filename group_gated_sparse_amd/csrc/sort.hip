@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "focus_internal.h"
 
 namespace focus {
@@ -117,6 +119,37 @@ __global__ __launch_bounds__(SORT_T) void sort_scatter_kernel(const int32_t* __r
 }
 
 }  // namespace
+
+// The per-block group counts of focus_group_sort_noalloc live here instead of
+// in a caller's workspace: a device array of the library, one copy on every
+// GPU it runs on, held until the process ends. Every call on one GPU uses the
+// same copy; the histogram pass writes every count the scatter pass reads, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) int32_t scratch[kSortScratchBytes / 4];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t group_sort_scratch(int32_t** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        // The name `scratch` is only a host-side stand-in for the array; its
+        // address on this device comes from the runtime, once per device.
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t group_sort_workspace(int B, int n, int K) {
     const int nblk = (n + SORT_BLOCK_TOKENS - 1) / SORT_BLOCK_TOKENS;

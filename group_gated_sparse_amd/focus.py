@@ -35,6 +35,7 @@ _SIGNATURES = {
     "focus_assign": ([_p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
     "focus_group_sort_workspace_bytes": ([_i, _i, _i], _sz),
     "focus_group_sort": ([_p, _i, _i, _i, _p, _p, _p, _sz, _p], _i),
+    "focus_group_sort_noalloc": ([_p, _i, _i, _i, _p, _p, _p], _i),
     "focus_attn_workspace_bytes": ([_i, _i, _i, _i, _i, _i, _i], _sz),
     "focus_attn_fwd": ([_p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _f, _p, _i, _p, _p,
                         _sz, _p], _i),
@@ -257,6 +258,22 @@ def focus_group_sort(group_ids: torch.Tensor, K: int, *, perm=None, group_offset
     _check_status(lib().focus_group_sort(_ptr(group_ids), B, n, K, _ptr(perm),
                                          _ptr(group_offsets), _ptr(ws),
                                          0 if ws is None else ws.numel(), _stream(stream)))
+    return perm, group_offsets
+
+
+def focus_group_sort_noalloc(group_ids: torch.Tensor, K: int, *, perm, group_offsets,
+                             stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """focus_group_sort with the library's static scratch instead of a
+    workspace: the call allocates nothing, so perm and group_offsets must be
+    given. Calls overlapping on one GPU share that scratch and race."""
+    _need(group_ids, "group_ids", torch.int32)
+    if group_ids.dim() == 3:
+        group_ids = group_ids.view(group_ids.shape[0], -1)
+    B, n = group_ids.shape
+    _need(perm, "perm", torch.int32, (B, n))
+    _need(group_offsets, "group_offsets", torch.int32, (B, K + 1))
+    _check_status(lib().focus_group_sort_noalloc(_ptr(group_ids), B, n, K, _ptr(perm),
+                                                 _ptr(group_offsets), _stream(stream)))
     return perm, group_offsets
 
 

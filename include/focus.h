@@ -166,6 +166,26 @@ focus_status focus_group_sort(const int32_t* group_ids, int B, int n, int K,
                               int32_t* perm, int32_t* group_offsets,
                               void* workspace, size_t workspace_bytes, focus_stream_t stream);
 
+/* focus_group_sort without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Same arguments, results and limits, minus the
+ * workspace: the per-block group counts go to a static device array of the
+ * library, FOCUS_SORT_NOALLOC_SCRATCH_BYTES (1 MiB) on every GPU it runs on,
+ * held until the process ends. The call allocates nothing; on its first use
+ * on a device it looks up that device's copy of the array (the device current
+ * at the call, which must be the stream's device).
+ * Limit: focus_group_sort_workspace_bytes(B, n, K) <= 1 MiB, i.e.
+ *   B * ceil(n / 2048) * K <= 262144 (e.g. B = 8 at n = 2^20, K = 64); larger
+ *   requests return FOCUS_ERR_UNSUPPORTED and enqueue nothing.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (different streams or threads with no ordering between them) race and
+ * give wrong results. Calls ordered on one stream are safe; no state carries
+ * from one call to the next. */
+#define FOCUS_SORT_NOALLOC_SCRATCH_BYTES (1u << 20)
+focus_status focus_group_sort_noalloc(const int32_t* group_ids, int B, int n, int K,
+                                      int32_t* perm, int32_t* group_offsets,
+                                      focus_stream_t stream);
+
 /* ------------------------------------------------------------------------
  * Step 3: exact-softmax attention over the Focus pattern (Korean page §2.1
  * and §2.3; Japanese page §2.1-§2.2). For query row (b, h, i), with kv head
