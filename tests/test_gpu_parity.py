@@ -132,6 +132,44 @@ def test_deterministic_and_stream_independent():
         assert np.array_equal(x, y) and np.array_equal(x, z)
 
 
+def test_side_stream_call_keeps_the_buffers_it_allocates():
+    """A call enqueued on a side stream while the default stream stays
+    current: the binding allocates the sort's and the attention's workspaces
+    and outputs and drops the workspaces on return, while the kernels still
+    run on the side stream. Large tensors allocated and filled on the default
+    stream right after each call must not land on those blocks (the binding
+    records the side stream on them), so the results equal an eager run on
+    the default stream bit for bit."""
+    say("[attn] side-stream call, default stream allocating meanwhile")
+    rng = np.random.default_rng(4242)
+    B, Hq, Hkv, n, d, K, w = 1, 16, 2, 8192, 128, 8, 256
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = rng.integers(0, K, size=(B, n), dtype=np.int32)
+    tq, tk, tv, tid = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(ids)
+    perm, offs = focus.focus_group_sort(tid, K)
+    ref, ref_lse = focus.focus_attn_fwd(tq, tk, tv, tid, perm, offs, K, w, 0.1,
+                                        out_dtype=torch.float32, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse, ref_perm = host(ref), host(ref_lse), host(perm)
+    del perm, offs
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    nbytes = focus.focus_attn_workspace_bytes(B, Hq, Hkv, n, d, K, w)
+    junk = []
+    perm_s, offs_s = focus.focus_group_sort(tid, K, stream=side)
+    junk.append(torch.full((1 << 20,), -1, dtype=torch.int32, device=tq.device))
+    out_s, lse_s = focus.focus_attn_fwd(tq, tk, tv, tid, perm_s, offs_s, K, w, 0.1,
+                                        out_dtype=torch.float32, want_lse=True, stream=side)
+    for _ in range(3):
+        junk.append(torch.full((nbytes // 4,), float("nan"), dtype=torch.float32,
+                               device=tq.device))
+    main.wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(perm_s), ref_perm)
+    assert np.array_equal(host(out_s), ref) and np.array_equal(host(lse_s), ref_lse)
+
+
 def test_two_calls_equal_one():
     """focus_attn_window (on a second stream, no group data, started before
     the groups are sorted) then focus_attn_long_range_merge ==
