@@ -49,6 +49,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "focus_internal.h"
 
 namespace focus {
@@ -90,7 +92,8 @@ struct AttnArgs {
     const int32_t* offsets;
     const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
     const int32_t* order;   // long-range pass: sorted query tiles, most work first [B][ntiles]
-    const int32_t* rowend;  // long-range pass (one group per token): end of each sorted row's keys [B][n]
+    const int32_t* pack;    // long-range pass (one group per token): a record per ordered tile
+    int pack_ints;          // ints per packed record
     int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
     _Float16* og;           // window partial [B][Hq][n][D]: O * 2^-e in fp16 (|.| < 1)
     f32x2* lseg;            // per row (log2-sum-exp L or -inf: no key, e)
@@ -100,7 +103,8 @@ struct AttnArgs {
     int ne;        // slots of the tiled order: n, or n*m entries in the multi pass
     int hpk;       // Hq / Hkv
     int G;         // query heads packed per workgroup
-    int TT;        // tokens per workgroup tile (ROWS / G)
+    int TT;        // tokens per workgroup tile (ROWS / G, a power of two)
+    int tt_log;    // log2(TT)
     int nslices;   // hpk / G
     int ntiles;    // ceil(n / TT)
     int total;     // workgroups
@@ -282,25 +286,62 @@ __device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32
     }
 }
 
-// Per sorted slot s, with one group per token: the end of the key slots its
-// row keeps in the long-range pass, i.e. the first slot of its group's
-// segment whose position is >= (its position) - w. Positions increase inside
-// a segment, so this is a binary search over [segment start, s); with it a
-// partial key tile is masked by comparing slot indices, without the keys'
-// positions.
-__global__ __launch_bounds__(256) void attn_rowend_kernel(const int32_t* __restrict__ ids,
-                                                          const int32_t* __restrict__ perm,
-                                                          const int32_t* __restrict__ offsets,
-                                                          int n, int K, int w,
-                                                          int32_t* __restrict__ rowend) {
-    const int b = blockIdx.y;
-    const int s = blockIdx.x * 256 + threadIdx.x;
-    if (s >= n) return;
+// Long-range pass with one group per token: one record per ordered query
+// tile j (the tile order[j]), so that the attention kernel finds at a fixed
+// address everything its prologue needs before the first key tile, in one
+// round trip rather than a chain of dependent loads (order, then perm, plan
+// and row ends, then the first key tile's positions):
+//   [0, 32)             the tile's plan record
+//   [32]                the tile's index
+//   [64, 64+TT)         its rows' entries (sorted slot -> position)
+//   [64+TT, 64+2TT)     each row's key-slot end: the first slot of its
+//                       group's segment whose position is >= its position -
+//                       w (positions increase inside a segment, so this is a
+//                       binary search over [segment start, slot)); a partial
+//                       key tile is then masked by comparing slot indices
+//   [64+2TT, 64+2TT+BN) the positions of the rows of the first key tile the
+//                       tile visits (the first non-empty segment's first BN
+//                       slots, clamped to its valid slots)
+// Rows past the sequence end take the last slot's values.
+__global__ __launch_bounds__(256) void attn_pack_kernel(
+    const int32_t* __restrict__ plan, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, int n, int K, int w, int TT, int BN, int ntiles, int pi,
+    int32_t* __restrict__ pack) {
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int tile = clampi(order[(int64_t)b * ntiles + j], 0, ntiles - 1);
+    const int32_t* src = plan + ((int64_t)b * ntiles + tile) * PLAN_INTS;
+    int32_t* dst = pack + ((int64_t)b * ntiles + j) * pi;
     const int32_t* perm_b = perm + (int64_t)b * n;
-    const int pos = clampi(perm_b[s], 0, n - 1);
-    const int g = clampi(ids[(int64_t)b * n + pos], 0, K - 1);
-    const int ob = clampi(offsets[(int64_t)b * (K + 1) + g], 0, s);
-    rowend[(int64_t)b * n + s] = first_slot_at_or_above(perm_b, ob, s, pos - w);
+    int ob0 = 0, kend0 = 0;   // the first segment with key tiles (none: ob0 = kend0)
+    const int nseg = min(src[0], SEGCAP);
+    for (int t = 0; t < nseg; ++t) {
+        const int ob = src[4 + 4 * t], ke = src[5 + 4 * t];
+        if (ke > ob) {
+            ob0 = ob;
+            kend0 = ke;
+            break;
+        }
+    }
+    for (int i = threadIdx.x; i < pi; i += 256) {
+        int val = 0;
+        if (i < PLAN_INTS) {
+            val = src[i];
+        } else if (i == PLAN_INTS) {
+            val = tile;
+        } else if (i >= 64 && i < 64 + TT) {
+            val = perm_b[min(tile * TT + (i - 64), n - 1)];
+        } else if (i >= 64 + TT && i < 64 + 2 * TT) {
+            const int slot = min(tile * TT + (i - 64 - TT), n - 1);
+            const int pos = clampi(perm_b[slot], 0, n - 1);
+            const int g = clampi(ids[(int64_t)b * n + pos], 0, K - 1);
+            const int ob = clampi(offsets[(int64_t)b * (K + 1) + g], 0, slot);
+            val = first_slot_at_or_above(perm_b, ob, slot, pos - w);
+        } else if (i >= 64 + 2 * TT && i < 64 + 2 * TT + BN && kend0 > ob0) {
+            val = perm_b[clampi(min(ob0 + (i - 64 - 2 * TT), kend0 - 1), 0, n - 1)];
+        }
+        dst[i] = val;
+    }
 }
 
 // Tile plan of the long-range pass, once per (batch, sorted query tile) and
@@ -414,6 +455,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     constexpr int BN = G::BN;
     constexpr bool SORTED = PHASE == kLongRange || PHASE == kLongMulti;
     constexpr bool MULTI = PHASE == kLongMulti;   // entries of two groups per token
+    // single-group long-range pass: work item = ordered slot of a packed record
+    constexpr bool PACKED = PHASE == kLongRange;
+    static_assert(!PACKED || BN == attn_long_range_tile_keys(D), "packed record tile size");
     constexpr bool GATED = attn_gated(PHASE);
     constexpr bool CAUSAL_ALL = PHASE == kDense || GATED;   // key range [0, last row]
     // soft-gated pass: assignment columns (padded), bytes per key row of the
@@ -457,14 +501,34 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     rest /= a.nslices;
     int kvh = rest % a.Hkv;
     int b = rest / a.Hkv;
-    if (SORTED) tile = clampi(a.order[(int64_t)b * a.ntiles + tile], 0, a.ntiles - 1);
-    tile = __builtin_amdgcn_readfirstlane(tile);
     slice = __builtin_amdgcn_readfirstlane(slice);
     kvh = __builtin_amdgcn_readfirstlane(kvh);
     b = __builtin_amdgcn_readfirstlane(b);
-
     const int R = wave * 32 + rl;
-    const int hslot = R / a.TT, tok = R % a.TT;
+    const int hslot = R >> a.tt_log, tok = R & (a.TT - 1);
+    // Packed pass: every load the prologue needs before the first key tile
+    // is at a fixed address in the item's record, so they form one round
+    // trip: lanes 0-15 of every wave hold record ints 4l .. 4l+3 (lane 0 the
+    // header, lane t + 1 segment t, lane 8 the tile index), every lane its
+    // row's entry and key-slot end and its rows of the first key tile.
+    const int32_t* rec = nullptr;
+    i32x4 prec = {0, 0, 0, 0};
+    int ent_pk = 0, kend_pk = 0;
+    int pos0_pk[G::NI];
+    if (PACKED) {
+        rec = a.pack + ((int64_t)b * a.ntiles + tile) * a.pack_ints;
+        prec = *reinterpret_cast<const i32x4*>(rec + 4 * (lane & 15));
+        ent_pk = rec[64 + tok];
+        kend_pk = rec[64 + a.TT + tok];
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i)
+            pos0_pk[i] = rec[64 + 2 * a.TT + ((wave * G::NI + i) * 1024 + 16 * lane) / G::ROWB];
+        tile = clampi(__builtin_amdgcn_readlane(prec[0], 8), 0, a.ntiles - 1);
+    } else if (SORTED) {
+        tile = clampi(a.order[(int64_t)b * a.ntiles + tile], 0, a.ntiles - 1);
+    }
+    tile = __builtin_amdgcn_readfirstlane(tile);
+
     const int h = kvh * a.hpk + slice * a.G + hslot;
     const int64_t bne = (int64_t)b * ne;
     const int s_row = tile * a.TT + tok;
@@ -472,19 +536,18 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // entry of the row (sorted passes: perm holds entries t*m + c; m = 1
     // makes the entry the position) and its sequence position
     int ent_i = rvalid ? s_row : 0;
-    // Sorted passes: every row loads its entry (rows past the end take the
-    // last slot's, a valid position they never store to), so the load sits
-    // in no branch that would wait for it on its own.
-    if (SORTED) ent_i = clampi(a.perm[bne + min(s_row, ne - 1)], 0, ne - 1);
+    // Sorted passes: every row has an entry (rows past the end take the last
+    // slot's, a valid position they never store to).
+    if (PACKED) ent_i = clampi(ent_pk, 0, ne - 1);
+    else if (SORTED) ent_i = clampi(a.perm[bne + min(s_row, ne - 1)], 0, ne - 1);
     // long-range pass: the end of the row's key slots (a partial tile is
     // masked by slot index)
     int kend_row = 0;
-    if (SORTED && !MULTI) kend_row = clampi(a.rowend[bne + min(s_row, ne - 1)], 0, ne);
-    // Sorted passes: the tile's plan record, loaded beside the perm entry so
+    if (PACKED) kend_row = clampi(kend_pk, 0, ne);
+    // Multi pass: the tile's plan record, loaded beside the perm entry so
     // that the two round trips overlap. Lane l < 8 of every wave holds ints
     // 4l .. 4l+3: lane 0 the header, lane t + 1 segment t.
-    i32x4 prec = {0, 0, 0, 0};
-    if (SORTED)
+    if (MULTI)
         prec = *reinterpret_cast<const i32x4*>(a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS +
                                               4 * (lane & 7));
     const int pos_i = MULTI ? (ent_i >> 1) : ent_i;
@@ -655,7 +718,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             pnext[i] = a.perm[bne + clampi(slot, 0, ne - 1)];
         }
     };
-    if (direct && ntl > 0) prefetch(0);
+    // the first key tile's positions: from the packed record when the plan
+    // record holds the segments (otherwise the kernel derived them itself)
+    if (direct && ntl > 0) {
+        if (PACKED && __builtin_amdgcn_readlane(prec[0], 0) >= 0) {
+#pragma unroll
+            for (int i = 0; i < G::NI; ++i) pnext[i] = pos0_pk[i];
+        } else {
+            prefetch(0);
+        }
+    }
     // soft-gated pass: this lane's share of the assignment-row copies (1 KB
     // copies wave, wave + 4, ...): key row within the tile and logical chunk
     constexpr int GCPW = (GNC + 3) / 4;
@@ -1042,11 +1114,11 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // query row r -> (head, entry); the entry is the position except in
     // the multi pass (position = entry / 2)
     auto row_of = [&](int r, int& hr, int& pr) {
-        hr = kvh * a.hpk + slice * a.G + r / a.TT;
+        hr = kvh * a.hpk + slice * a.G + (r >> a.tt_log);
         if (SORTED) {
             pr = rowpos[r];
         } else {
-            pr = min(tile * a.TT + r % a.TT, a.n - 1);
+            pr = min(tile * a.TT + (r & (a.TT - 1)), a.n - 1);
         }
     };
     if (G::QSTAGE) {
@@ -1110,85 +1182,104 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     }
 
     // Epilogue. Lane holds rows' O^T entries d = db*32 + 8*i + 4*hh + j at
-    // acc[db][4*i + j]; l_run and l_pv cover this lane half's keys. The rows
-    // are written to LDS (chunk slots XOR-swizzled by row) and stored as
-    // whole contiguous rows. O is normalised by l_pv (the weights it was
-    // accumulated with), the log-sum-exp comes from l_run.
+    // acc[db][4*i + j]; l_run and l_pv cover this lane half's keys. O is
+    // normalised by l_pv (the weights it was accumulated with), the
+    // log-sum-exp comes from l_run. The rows are written to LDS (chunk slots
+    // XOR-swizzled by row) and stored as whole contiguous rows; each output
+    // kind has its own straight-line path (sizes known at compile time).
     const float l_tot = l_run + other_half(l_run);
     const float l_pv_tot = l_pv + other_half(l_pv);
     const int64_t row = ((int64_t)b * a.Hq + h) * ne + ent_i;   // output row
-    float scale_o = l_pv_tot > 0.0f ? 1.0f / l_pv_tot : 0.0f;
-    int esize;
-    if (a.partial) {
-        // 16-bit partial with a per-row power-of-two scale: O~ = O * 2^-e
-        // with e the exponent of max |O| (so |O~| < 1), kept in fp16, whose
-        // 11-bit significand keeps the merge as precise as the final output
-        esize = 2;
-        float mx = 0.0f;
-#pragma unroll
-        for (int db = 0; db < G::DB; ++db)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, __builtin_fabsf(acc[db][e]));
-        mx = fmaxf(mx, other_half(mx)) * scale_o;
-        const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
-        scale_o = __builtin_ldexpf(scale_o, -ex);
-        if (rvalid && hh == 0) {
-            const f32x2 le = {l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf, (float)ex};
-            a.lseg[row] = le;
-        }
-    } else {
-        esize = a.out_f32 ? 4 : 2;
-        if (rvalid && hh == 0 && a.lse) a.lse[row] = (m_ref + __log2f(l_tot)) * kLn2;
-    }
-    const int RB = D * esize;          // bytes per output row
-    const int nchk = RB / 16;          // 16-byte chunks per row
-    const int cmask = (nchk < 16 ? nchk : 16) - 1;
-    const int rpp = min(ROWS, (4 * G::TILEB) / RB);   // rows staged per pass
-    const int hrows = (2 * G::TILEB) / RB;            // rows staged per buffer
-    auto stage = [&](int rs) -> unsigned char* {
-        return rs < hrows ? buf0 + rs * RB : buf1 + (rs - hrows) * RB;
-    };
-    char* dst = a.partial ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
-    for (int r0 = 0; r0 < ROWS; r0 += rpp) {
-        __syncthreads();               // K/V buffers (or the previous pass) are free
-        if (R >= r0 && R < r0 + rpp) {
-            const int rs = R - r0;
+    const float inv_l = l_pv_tot > 0.0f ? __builtin_amdgcn_rcpf(l_pv_tot) : 0.0f;
+    // kind 0: fp16 partial O * 2^-e; 1: bf16 output; 2: fp32 output
+    auto epilogue = [&](auto kind_tag) {
+        constexpr int KIND = decltype(kind_tag)::value;
+        constexpr int ESZ = KIND == 2 ? 4 : 2;
+        constexpr int RB = D * ESZ;                          // bytes per output row
+        constexpr int NCHK = RB / 16;                        // 16-byte chunks per row
+        constexpr int CMASK = (NCHK < 16 ? NCHK : 16) - 1;
+        constexpr int RPP = ROWS < 4 * G::TILEB / RB ? ROWS : 4 * G::TILEB / RB;   // rows per pass
+        constexpr int HROWS = 2 * G::TILEB / RB;             // rows staged per buffer
+        float scale_o = inv_l;
+        if constexpr (KIND == 0) {
+            // 16-bit partial with a per-row power-of-two scale: O~ = O * 2^-e
+            // with e the exponent of max |O| (so |O~| < 1), kept in fp16, whose
+            // 11-bit significand keeps the merge as precise as the final output
+            float mx = 0.0f;
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int qd = db * 8 + 2 * i + hh;   // quad index: d = 4*qd .. +3
-                    const f32x4 o = {acc[db][4 * i] * scale_o, acc[db][4 * i + 1] * scale_o,
-                                     acc[db][4 * i + 2] * scale_o, acc[db][4 * i + 3] * scale_o};
-                    if (esize == 4) {
-                        *reinterpret_cast<f32x4*>(stage(rs) + ((qd ^ (rs & cmask)) << 4)) = o;
-                    } else {
-                        const int half = (qd & 1) ^ ((rs >> 4) & 1);
-                        unsigned char* sp = stage(rs) + (((qd >> 1) ^ (rs & cmask)) << 4) + half * 8;
-                        if (a.partial) {
-                            const f16x4 oh = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2],
-                                              (_Float16)o[3]};
-                            *reinterpret_cast<f16x4*>(sp) = oh;
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, __builtin_fabsf(acc[db][e]));
+            mx = fmaxf(mx, other_half(mx)) * scale_o;
+            const int ex = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+            scale_o = __builtin_ldexpf(scale_o, -ex);
+            if (rvalid && hh == 0) {
+                const f32x2 le = {l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf, (float)ex};
+                a.lseg[row] = le;
+            }
+        } else {
+            if (rvalid && hh == 0 && a.lse) a.lse[row] = (m_ref + __log2f(l_tot)) * kLn2;
+        }
+        auto stage = [&](int rs) -> unsigned char* {
+            return rs < HROWS ? buf0 + rs * RB : buf1 + (rs - HROWS) * RB;
+        };
+        char* dst = KIND == 0 ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
+#pragma unroll
+        for (int r0 = 0; r0 < ROWS; r0 += RPP) {
+            // K/V buffers (or the previous pass) are free
+            __syncthreads();
+            if (R >= r0 && R < r0 + RPP) {
+                const int rs = R - r0;
+#pragma unroll
+                for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int qd = db * 8 + 2 * i + hh;   // quad index: d = 4*qd .. +3
+                        const f32x4 o = {acc[db][4 * i] * scale_o, acc[db][4 * i + 1] * scale_o,
+                                         acc[db][4 * i + 2] * scale_o, acc[db][4 * i + 3] * scale_o};
+                        if constexpr (KIND == 2) {
+                            *reinterpret_cast<f32x4*>(stage(rs) + ((qd ^ (rs & CMASK)) << 4)) = o;
                         } else {
-                            const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2],
-                                               (__bf16)o[3]};
-                            *reinterpret_cast<bf16x4*>(sp) = ob;
+                            const int half = (qd & 1) ^ ((rs >> 4) & 1);
+                            unsigned char* sp =
+                                stage(rs) + (((qd >> 1) ^ (rs & CMASK)) << 4) + half * 8;
+                            if constexpr (KIND == 0) {
+                                const f16x4 oh = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2],
+                                                  (_Float16)o[3]};
+                                *reinterpret_cast<f16x4*>(sp) = oh;
+                            } else {
+                                const bf16x4 ob = {(__bf16)o[0], (__bf16)o[1], (__bf16)o[2],
+                                                   (__bf16)o[3]};
+                                *reinterpret_cast<bf16x4*>(sp) = ob;
+                            }
                         }
                     }
-                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int idx0 = 0; idx0 < RPP * NCHK; idx0 += NT) {
+                const int idx = idx0 + tid;
+                if (RPP * NCHK % NT != 0 && idx >= RPP * NCHK) break;
+                const int rs = idx / NCHK, c = idx % NCHK;
+                const int r = r0 + rs;
+                const int tk = r & (a.TT - 1);
+                if (tile * a.TT + tk >= ne) continue;   // rows past the sequence end
+                int hr, pr;
+                row_of(r, hr, pr);
+                u32x4 val = *reinterpret_cast<const u32x4*>(stage(rs) + ((c ^ (rs & CMASK)) << 4));
+                if (ESZ == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
+                *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * ne + pr) * RB) +
+                                          c * 16) = val;
+            }
         }
-        __syncthreads();
-        for (int idx = tid; idx < rpp * nchk; idx += NT) {
-            const int rs = idx / nchk, c = idx % nchk;
-            const int r = r0 + rs;
-            if (tile * a.TT + r % a.TT >= ne) continue;   // rows past the sequence end
-            int hr, pr;
-            row_of(r, hr, pr);
-            u32x4 val = *reinterpret_cast<const u32x4*>(stage(rs) + ((c ^ (rs & cmask)) << 4));
-            if (esize == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
-            *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * ne + pr) * RB) + c * 16) =
-                val;
-        }
+    };
+    // partials: the window pass ahead of a long-range pass, the multi pass
+    if (MULTI || (PHASE == kWindow && a.partial)) {
+        epilogue(std::integral_constant<int, 0>{});
+    } else if (a.out_f32) {
+        epilogue(std::integral_constant<int, 2>{});
+    } else {
+        epilogue(std::integral_constant<int, 1>{});
     }
 }
 
@@ -1289,6 +1380,7 @@ AttnArgs make_args(const AttnProblem& p) {
     a.hpk = p.Hq / p.Hkv;
     a.G = attn_heads_per_wg(a.hpk);
     a.TT = ROWS / a.G;
+    a.tt_log = 31 - __builtin_clz((unsigned)a.TT);
     a.nslices = a.hpk / a.G;
     a.ne = p.n;
     a.ntiles = (p.n + a.TT - 1) / a.TT;
@@ -1303,7 +1395,8 @@ AttnArgs make_args(const AttnProblem& p) {
         a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
         a.order = reinterpret_cast<const int32_t*>(base + ws.order);
         a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
-        a.rowend = reinterpret_cast<const int32_t*>(base + ws.rowend);
+        a.pack = reinterpret_cast<const int32_t*>(base + ws.pack);
+        a.pack_ints = attn_pack_ints(a.TT, attn_long_range_tile_keys(p.d));
     }
     return a;
 }
@@ -1376,9 +1469,10 @@ hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stre
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.m == 1) {
-        hipLaunchKernelGGL(attn_rowend_kernel, dim3((p.n + 255) / 256, p.B), dim3(256), 0, stream,
-                           p.ids, p.perm, p.offsets, p.n, p.K, p.w,
-                           const_cast<int32_t*>(a.rowend));
+        hipLaunchKernelGGL(attn_pack_kernel, dim3(a.ntiles, p.B), dim3(256), 0, stream, a.plan,
+                           a.order, p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT,
+                           attn_long_range_tile_keys(p.d), a.ntiles, a.pack_ints,
+                           const_cast<int32_t*>(a.pack));
         e = hipGetLastError();
     }
     return e;

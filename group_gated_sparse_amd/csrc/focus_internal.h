@@ -74,6 +74,13 @@ constexpr int PLAN_INTS = 32;   // ints per plan record (4 + 4 * SEGCAP)
 
 int attn_heads_per_wg(int hpk);
 inline int attn_tokens_per_tile(int Hq, int Hkv) { return 128 / attn_heads_per_wg(Hq / Hkv); }
+// Keys per tile of the long-range pass (32, or 64 at d = 32).
+constexpr int attn_long_range_tile_keys(int d) { return d == 32 ? 64 : 32; }
+// Ints per packed record of the single-group long-range pass: the plan
+// record and tile index (64), then per row its entry and key-slot end (TT
+// each), then the positions of the first key tile's rows (BN), rounded up to
+// 256 bytes.
+inline int attn_pack_ints(int TT, int BN) { return (64 + 2 * TT + BN + 63) / 64 * 64; }
 
 // Whether the long-range pass reads group-sorted copies of K and V (made by
 // its prepare step) rather than key rows in place: always with two groups
@@ -87,8 +94,9 @@ inline bool attn_sorted_copies(int n, int d, int m, bool force) {
 // [B][Hq][n][d], scaled per row), its log2-sum-exp and scale exponent (fp32
 // pairs [B][Hq][n]), the tile plan, the order in which the long-range pass
 // takes the sorted query tiles (int32 [B][tiles], most work first) and, with
-// one group per token, the end of the key slots each sorted row keeps (int32
-// [B][n]). With sorted copies (attn_sorted_copies) also the group-sorted K
+// one group per token, one packed record per ordered tile (int32
+// [B][tiles][attn_pack_ints]: plan record, tile index, each row's entry and
+// key-slot end, the first key tile's positions). With sorted copies (attn_sorted_copies) also the group-sorted K
 // and V (bf16 [B][Hkv][n*m][d]) and the sorted slots' positions (int32
 // [B][n*m + pad]). With m groups per token (m > 1) the sorted order lists
 // n*m membership entries, and the long-range pass writes one partial per
@@ -96,7 +104,7 @@ inline bool attn_sorted_copies(int n, int d, int m, bool force) {
 // The first two regions lead every layout, so the window pass, which uses
 // only them, takes the same offsets for every m.
 struct AttnWorkspace {
-    size_t og, lseg, plan, order, rowend, ks, vs, spos, oge, lsege, total;
+    size_t og, lseg, plan, order, pack, ks, vs, spos, oge, lsege, total;
 };
 inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m,
                                            bool copies) {
@@ -109,7 +117,9 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d,
     w.lseg = off; off += align_up((size_t)B * Hq * n * 8);
     w.plan = off; off += align_up((size_t)B * ntiles * PLAN_INTS * 4);
     w.order = off; off += align_up((size_t)B * ntiles * 4);
-    w.rowend = off; off += m == 1 ? align_up((size_t)B * n * 4) : 0;
+    w.pack = off;
+    off += m == 1 ? align_up((size_t)B * ntiles * attn_pack_ints(TT, attn_long_range_tile_keys(d)) * 4)
+                  : 0;
     w.ks = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
     w.vs = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
     w.spos = off; off += copies ? align_up((size_t)B * (ne + KPOS_PAD) * 4) : 0;

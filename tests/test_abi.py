@@ -117,10 +117,11 @@ def test_workspace_sizes():
     assert lib.focus_group_sort_workspace_bytes(2, 100, 8) == 256
     assert lib.focus_group_sort_workspace_bytes(1, 65536, 64) == 32 * 64 * 4
     # partial fp16 [B][Hq][n][d] + (lse, exponent) fp32 pairs [B][Hq][n] + 128 B plan per query
-    # tile (here 64 tokens x 2 heads) + int32 tile order [B][tiles] + int32 end of each sorted
-    # row's keys [B][n], each region 256-byte aligned; key rows are read in place, so no
-    # sorted copies of K and V are reserved
-    in_place = 256 * 2 * 32 * 2 + 4096 + 4 * 128 + 256 + 256 * 4
+    # tile (here 64 tokens x 2 heads, 4 tiles) + int32 tile order [B][tiles] + one packed record
+    # per tile (64 ints of plan record and tile index, 64 row entries, 64 row key ends, 64
+    # positions of a 64-key tile: 256 ints), each region 256-byte aligned; key rows are read in
+    # place, so no sorted copies of K and V are reserved
+    in_place = 256 * 2 * 32 * 2 + 4096 + 4 * 128 + 256 + 4 * 256 * 4
     assert lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32) == in_place
     # the sorted-copy path adds sorted bf16 K and V [B][Hkv][n][d] and int32 sorted positions
     # [B][n + 256]
