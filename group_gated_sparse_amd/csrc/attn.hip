@@ -885,10 +885,18 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         }
 
         // Mask (partial tiles only). Lane holds keys kidx = kb*32 +
-        // 8*(e>>2) + 4*hh + (e&3) of its row.
+        // 8*(e>>2) + 4*hh + (e&3) of its row, i.e. key kt0 + 4*hh + c with a
+        // compile-time c; each test is one subtraction or compare against c.
         // (branch-free: every condition is evaluated, combined with &)
         if (!full) {
             const bool row_ok = !SORTED || g_i == gfirst + seg_cur.seg;
+            // sequence-order passes: kept keys are those with 0 <= pos_i - key
+            // <= w (keys past the last row then fail too: pos_i < kend for
+            // every stored row; the dense pass runs with w = n, the gated
+            // pass keeps far keys and gates them instead)
+            const int dpos = pos_i - kt0 - 4 * hh;   // pos_i - key = dpos - c
+            // single-group pass: kept keys are the slots below kend_row
+            const int dend = row_ok ? kend_row - kt0 - 4 * hh : -1;   // key < kend_row: c < dend
 #pragma unroll
             for (int kb = 0; kb < G::KB; ++kb)
 #pragma unroll
@@ -898,17 +906,14 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     if (MULTI) kp = *reinterpret_cast<const int4*>(kposp + k0);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const int key = kt0 + k0 + j;
+                        const int c = kb * 32 + 8 * e4 + j;
                         bool ok;
                         if (!SORTED) {
-                            // (the dense pass runs with w = n; the gated pass
-                            // keeps far keys and gates them instead)
-                            ok = (key < kend) & (key <= pos_i) & (GATED || pos_i - key <= a.w);
+                            ok = GATED ? c <= dpos : (uint32_t)(dpos - c) <= (uint32_t)a.w;
                         } else if (!MULTI) {
-                            // the row's keys are the slots of its group's segment below
-                            // kend_row (their positions are below pos_i - w)
-                            ok = row_ok & (key < kend_row);
+                            ok = c < dend;
                         } else {   // kp = position * 64 + the key token's other group
+                            const int key = kt0 + k0 + j;
                             ok = row_ok & (key < kend) & (pos_i - (kp[j] >> 6) > a.w) &
                                  ((kp[j] & 63) != x_i);
                         }
@@ -1002,10 +1007,14 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             const float alpha = (m_new == m_ref) ? 1.0f : __builtin_amdgcn_exp2f(m_ref - m_new);
             l_run *= alpha;
             l_pv *= alpha;
+            // rows with no reference yet hold nothing to rescale (the first
+            // key tile of every sequence-order item)
+            if (__any(m_ref != kNegInf)) {
 #pragma unroll
-            for (int db = 0; db < G::DB; ++db)
+                for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+                    for (int e = 0; e < 16; ++e) acc[db][e] *= alpha;
+            }
             m_ref = m_new;
             probs(m_ref == kNegInf ? 0.0f : m_ref);
         }
