@@ -110,6 +110,21 @@ def device_info(torch):
             "compute_units": p.multi_processor_count}
 
 
+def host_cpu():
+    """The host CPU's model name and logical core count (the oracle's
+    OpenMP thread count is reported separately as cores)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cores": os.cpu_count()}
+
+
 def cpu_baseline(x, wl, target_s):
     """The oracle as it stands, on the host cores: full assignment and group
     sort, attention on a random row sample extrapolated per visited pair."""
@@ -157,6 +172,7 @@ def cpu_baseline(x, wl, target_s):
         "value": flops / step_s / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
+        "host_cpu": host_cpu(),
         "kind": "oracle",
         "sample": (f"full fp32 assignment ({wl.B * wl.n} tokens, {t_assign:.2f} s) and group sort "
                    f"({t_sort:.3f} s); fp64 attention on {rows_done} random query rows "
@@ -517,7 +533,10 @@ def main():
         win, lr, lr_visited = metrics.pair_counts_multi(gids, w)
     pairs = win + lr
     flops = metrics.attn_flops(pairs, Hq, d)
-    attn_ms = phase["window"] + phase["long_range_prepare"] + phase["long_range_apply"]
+    # the two attention passes; the tile plan (prepare) runs beside the window
+    # pass in the step and is reported apart as plan_ms
+    attn_ms = phase["window"] + phase["long_range_apply"]
+    plan_ms = phase["long_range_prepare"]
     # pairs the kernels' MFMAs form, masked ones included (their tiling)
     tt = 128 // metrics.heads_per_workgroup(Hq, Hkv)
     bn = metrics.tile_keys(d)
@@ -555,6 +574,7 @@ def main():
                           "max": per_step[-1]},
         "device": device_info(torch),
         "attn_ms": attn_ms,
+        "plan_ms": plan_ms,
         "attn_tflops": flops / (attn_ms * 1e-3) / 1e12,
         "attn_frac_of_bf16_peak": flops / (attn_ms * 1e-3) / 1e12 / metrics.MI355X_BF16_DENSE_TFLOPS,
         "assign_GBps": (B * n * wl.d_model * 4) / (phase["assign"] * 1e-3) / 1e9,

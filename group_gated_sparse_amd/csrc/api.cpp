@@ -143,8 +143,8 @@ focus_status attn_entry(AttnPart part, const uint16_t* q, const uint16_t* k, con
     // the window pass only uses the leading part of the workspace, which
     // is laid out the same for every m
     const size_t need = part == AttnPart::kWindow
-                            ? focus::attn_workspace(B, Hq, Hkv, n, d, w)
-                            : focus::attn_workspace(B, Hq, Hkv, n, d, w, m, force_copies);
+                            ? focus::attn_window_workspace(B, Hq, Hkv, n, d, w)
+                            : focus::attn_workspace(B, Hq, Hkv, n, d, w, K, m, force_copies);
     if (need > 0) {
         REQUIRE(workspace != nullptr, FOCUS_ERR_WORKSPACE, "workspace of %zu bytes required", need);
         REQUIRE(aligned(workspace, 16), FOCUS_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -366,10 +366,9 @@ focus_status focus_group_sort_noalloc(const int32_t* group_ids, int B, int n, in
 }
 
 size_t focus_attn_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int window) {
-    (void)K;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;
     if (d_head != 32 && d_head != 64 && d_head != 128) return 0;
-    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window);
+    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, K);
 }
 
 focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -385,10 +384,9 @@ focus_status focus_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t
 
 size_t focus_attn_sorted_kv_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K,
                                             int window) {
-    (void)K;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;
     if (d_head != 32 && d_head != 64 && d_head != 128) return 0;
-    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, 1, true);
+    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, K, 1, true);
 }
 
 focus_status focus_attn_fwd_sorted_kv(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -486,11 +484,11 @@ focus_status focus_soft_gate_attn_fwd(const uint16_t* q, const uint16_t* k, cons
 
 size_t focus_attn_topk_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int m,
                                        int window) {
-    (void)K;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv || n < 1 || window < 0) return 0;
     if (d_head != 32 && d_head != 64 && d_head != 128) return 0;
+    if (K < 1 || K > FOCUS_MAX_GROUPS) return 0;
     if (m < 1 || m > FOCUS_MAX_MEMBERSHIPS || (int64_t)n * m > ((int64_t)1 << 24)) return 0;
-    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, m);
+    return focus::attn_workspace(B, Hq, Hkv, n, d_head, window, K, m);
 }
 
 focus_status focus_attn_topk_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,

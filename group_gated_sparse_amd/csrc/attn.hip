@@ -78,10 +78,12 @@ constexpr float kProbSumCap = 256.0f;  // a lane's probability sum that triggers
 constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 
 // kLongMulti: the long-range pass over membership entries, two groups per token.
+// kLongSets: the long-range pass with two groups per token and few groups
+// (K <= 4), over tokens sorted by their membership set.
 // kSoftGate + s (s = 0, 1, 2): the training-time soft-gated pass over every
 // causal pair, with soft assignments of KG = 16 << s columns (zero-padded).
-enum { kWindow = 0, kLongRange = 1, kDense = 2, kLongMulti = 3, kSoftGate = 4 };
-constexpr bool attn_gated(int PHASE) { return PHASE >= kSoftGate; }
+enum { kWindow = 0, kLongRange = 1, kDense = 2, kLongMulti = 3, kSoftGate = 4, kLongSets = 7 };
+constexpr bool attn_gated(int PHASE) { return PHASE >= kSoftGate && PHASE < kLongSets; }
 
 struct AttnArgs {
     const uint16_t* q;
@@ -95,6 +97,7 @@ struct AttnArgs {
     const int32_t* pack;    // long-range pass (one group per token): a record per ordered tile
     int pack_ints;          // ints per packed record
     int32_t* spos;          // positions of sorted slots, [B][n + KPOS_PAD], padded kNoPos
+    int set_lut;            // set pass: group mask of membership set s in bits 4s .. 4s+3
     _Float16* og;           // window partial [B][Hq][n][D]: O * 2^-e in fp16 (|.| < 1)
     f32x2* lseg;            // per row (log2-sum-exp L or -inf: no key, e)
     void* out;
@@ -344,6 +347,95 @@ __global__ __launch_bounds__(256) void attn_pack_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Two groups per token with few groups (K <= 4, at most 6 membership sets):
+// tokens are sorted by their membership set {a, b}, and a query tile of set
+// S visits the key segments of every set that shares a group with S. Each
+// kept pair then meets exactly once, in the query's tile, and the pass can
+// merge the window partial and write the result itself.
+//
+// Set id of the unordered pair a < b of K groups: the pairs in lexicographic
+// order, (0,1) = 0, (0,2) = 1, ...
+__device__ __forceinline__ int pair_set_id(int a, int b, int K) {
+    return a * K - a * (a + 1) / 2 + (b - a - 1);
+}
+__device__ __forceinline__ int token_group_mask(const int32_t* ids_t, int K) {
+    return (1 << clampi(ids_t[0], 0, K - 1)) | (1 << clampi(ids_t[1], 0, K - 1));
+}
+// sid[t] = set id of token t's two groups (ids [B*n][2]), clamped to [0, S).
+__global__ __launch_bounds__(256) void attn_set_id_kernel(const int32_t* __restrict__ ids,
+                                                          int64_t ntok, int K, int S,
+                                                          int32_t* __restrict__ sid) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= ntok) return;
+    const int g0 = clampi(ids[2 * t], 0, K - 1), g1 = clampi(ids[2 * t + 1], 0, K - 1);
+    sid[t] = clampi(pair_set_id(min(g0, g1), max(g0, g1), K), 0, S - 1);
+}
+// Per set-sorted slot s: (position << 6) | the token's group mask, then
+// KPOS_PAD padding slots (kNoPos): the keys' data for masking partial tiles.
+__global__ __launch_bounds__(256) void attn_set_spos_kernel(const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ ids,
+                                                            int n, int K,
+                                                            int32_t* __restrict__ spos) {
+    const int b = blockIdx.y;
+    const int s = blockIdx.x * 256 + threadIdx.x;
+    if (s >= n + KPOS_PAD) return;
+    int val = kNoPos;
+    if (s < n) {
+        const int pos = clampi(perm[(int64_t)b * n + s], 0, n - 1);
+        val = (pos << 6) | token_group_mask(ids + ((int64_t)b * n + pos) * 2, K);
+    }
+    spos[(int64_t)b * (n + KPOS_PAD) + s] = val;
+}
+// Plan record of a set-sorted query tile (same layout as attn_plan_kernel's):
+// one segment per membership set t (so nseg = S and segment t is set t), with
+// the key slots [ob, kend) of set t whose positions lie below (largest query
+// position of the tile) - w when set t shares a group with some row of the
+// tile, and none otherwise; kfull: slots below it pair with every row (all
+// rows of one set, positions below (smallest query position) - w).
+__global__ __launch_bounds__(256) void attn_set_plan_kernel(
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ ids, int n, int K, int S, int w, int TT, int ntiles,
+    int bn_keys, int set_lut, int32_t* __restrict__ plan) {
+    const int b = blockIdx.y;
+    const int tile = blockIdx.x * 256 + threadIdx.x;
+    if (tile >= ntiles) return;
+    const int32_t* perm_b = perm + (int64_t)b * n;
+    const int32_t* offb = offsets + (int64_t)b * (S + 1);
+    const int s0 = tile * TT, s1 = min(n, s0 + TT);
+    int umask = 0, mask0 = -1, minpos = n, maxpos = 0;
+    bool one_set = true;
+    for (int sl = s0; sl < s1; ++sl) {
+        const int pos = clampi(perm_b[sl], 0, n - 1);
+        const int mk = token_group_mask(ids + ((int64_t)b * n + pos) * 2, K);
+        if (mask0 < 0) mask0 = mk;
+        one_set = one_set && mk == mask0;
+        umask |= mk;
+        minpos = min(minpos, pos);
+        maxpos = max(maxpos, pos);
+    }
+    int32_t* rec = plan + ((int64_t)b * ntiles + tile) * PLAN_INTS;
+    int run = 0;
+    for (int t = 0; t < S; ++t) {
+        const int ob = clampi(offb[t], 0, n);
+        const int oe = clampi(offb[t + 1], ob, n);
+        int kend = ob, kfull = ob;
+        if (((set_lut >> (4 * t)) & 15) & umask) {
+            kend = first_slot_at_or_above(perm_b, ob, oe, maxpos - w);
+            kfull = first_slot_at_or_above(perm_b, ob, kend, minpos - w);
+        }
+        rec[4 + 4 * t] = ob;
+        rec[5 + 4 * t] = kend;
+        rec[6 + 4 * t] = run;
+        rec[7 + 4 * t] = kfull;
+        run += (kend - ob + bn_keys - 1) / bn_keys;
+    }
+    rec[0] = S;
+    rec[1] = 0;
+    rec[2] = one_set ? 1 : 0;
+    rec[3] = run;
+}
+
 // Tile plan of the long-range pass, once per (batch, sorted query tile) and
 // shared by every kv head: record = {nseg (-1: more than SEGCAP groups, the
 // attention kernel then derives its segments itself), first group, all query
@@ -453,8 +545,10 @@ template <int D, int PHASE>
 __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(AttnArgs a) {
     using G = Geom<D, attn_tile_keys(D, PHASE)>;
     constexpr int BN = G::BN;
-    constexpr bool SORTED = PHASE == kLongRange || PHASE == kLongMulti;
+    constexpr bool SORTED = PHASE == kLongRange || PHASE == kLongMulti || PHASE == kLongSets;
     constexpr bool MULTI = PHASE == kLongMulti;   // entries of two groups per token
+    constexpr bool SETS = PHASE == kLongSets;     // tokens sorted by membership set
+    constexpr bool KPOS = MULTI || SETS;          // partial tiles masked by staged key data
     // single-group long-range pass: work item = ordered slot of a packed record
     constexpr bool PACKED = PHASE == kLongRange;
     static_assert(!PACKED || BN == attn_long_range_tile_keys(D), "packed record tile size");
@@ -481,8 +575,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     __shared__ __attribute__((aligned(1024))) unsigned char buf1_split[SPLIT ? 2 * G::TILEB : 16];
     unsigned char* const buf1 = SPLIT ? buf1_split : buf0 + 2 * G::TILEB;
     // multi pass: positions (and other groups) of the key slots of a partial tile
-    __shared__ __attribute__((aligned(1024))) int kpos0[MULTI ? KPOS_PAD : 4],
-        kpos1[MULTI ? KPOS_PAD : 4];
+    __shared__ __attribute__((aligned(1024))) int kpos0[KPOS ? KPOS_PAD : 4],
+        kpos1[KPOS ? KPOS_PAD : 4];
     // soft-gated pass: the key tile's assignment rows, one buffer per K/V buffer
     __shared__ __attribute__((aligned(1024))) unsigned char gk_lds[GATED ? 2 * BN * GROWB : 16];
     __shared__ int seg_ob[MAXSEG], seg_kend[MAXSEG], seg_t0[MAXSEG + 1], seg_kfull[MAXSEG];
@@ -544,15 +638,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // masked by slot index)
     int kend_row = 0;
     if (PACKED) kend_row = clampi(kend_pk, 0, ne);
-    // Multi pass: the tile's plan record, loaded beside the perm entry so
-    // that the two round trips overlap. Lane l < 8 of every wave holds ints
-    // 4l .. 4l+3: lane 0 the header, lane t + 1 segment t.
-    if (MULTI)
+    // Multi and set passes: the tile's plan record, loaded beside the perm
+    // entry so that the two round trips overlap. Lane l < 8 of every wave
+    // holds ints 4l .. 4l+3: lane 0 the header, lane t + 1 segment t.
+    if (MULTI || SETS)
         prec = *reinterpret_cast<const i32x4*>(a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS +
                                               4 * (lane & 7));
     const int pos_i = MULTI ? (ent_i >> 1) : ent_i;
     // multi pass: the row token's other group
     const int oth_i = (MULTI && rvalid) ? clampi(a.ids[bne + (ent_i ^ 1)], 0, a.K - 1) : 0;
+    // set pass: the row token's group mask (a key is kept when it shares one)
+    const int gmask_i = SETS ? token_group_mask(a.ids + ((int64_t)b * a.n + pos_i) * 2, a.K) : 0;
 
     const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + kvh) * ne * D;
     const uint16_t* vbase = a.v + ((int64_t)b * a.Hkv + kvh) * ne * D;
@@ -743,6 +839,15 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         bool full;
         locate(tau, seg_issue, kt0, kend, full);
         unsigned char* dst = bufp + wave_s * G::NI * 1024;
+        // multi and set passes: the key slots' positions and group data, for
+        // the mask of a partial tile (a scalar base plus a 32-bit lane offset,
+        // like the tile copies: a per-lane 64-bit pointer here would be kept
+        // across the loop, spilled, and its reload would wait for the copies
+        // issued just before it). The single-group pass masks by slot index.
+        if (KPOS && !full && wave == 0) {
+            const char* sp = reinterpret_cast<const char*>(a.spos + (int64_t)b * (ne + KPOS_PAD));
+            copy16(sp + (uint32_t)(4 * kt0 + 16 * lane), kposp);
+        }
         if (direct) {
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
@@ -777,15 +882,6 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 copy16_buf(krs, vo, 0, dst + i * 1024);
                 copy16_buf(vrs, vo, 0, dst + G::TILEB + i * 1024);
             }
-        }
-        // multi pass: positions and other groups of the tile's key slots, for
-        // the mask of a partial tile (a scalar base plus a 32-bit lane offset,
-        // like the tile copies: a per-lane 64-bit pointer here would be kept
-        // across the loop, spilled, and its reload would wait for the copies
-        // issued just before it). The single-group pass masks by slot index.
-        if (MULTI && !full && wave == 0) {
-            const char* sp = reinterpret_cast<const char*>(a.spos + (int64_t)b * (ne + KPOS_PAD));
-            copy16(sp + (uint32_t)(4 * kt0 + 16 * lane), kposp);
         }
         if constexpr (GATED) {
             // the key tile's assignment rows (hi and lo), row-clamped at the end
@@ -851,6 +947,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             bool needs;
             if (!SORTED) {
                 needs = rvalid && kt0 <= pos_i && (CAUSAL_ALL || kt0 + BN - 1 >= pos_i - a.w);
+            } else if (SETS) {
+                // the segment's set shares a group with the row's
+                needs = rvalid && (gmask_i & (a.set_lut >> (4 * seg_cur.seg))) != 0;
             } else if (!MULTI) {
                 needs = rvalid && g_i == gfirst + seg_cur.seg && kt0 < kend_row;
             } else {
@@ -889,7 +988,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         // compile-time c; each test is one subtraction or compare against c.
         // (branch-free: every condition is evaluated, combined with &)
         if (!full) {
-            const bool row_ok = !SORTED || g_i == gfirst + seg_cur.seg;
+            const bool row_ok = !SORTED || SETS || g_i == gfirst + seg_cur.seg;
             // sequence-order passes: kept keys are those with 0 <= pos_i - key
             // <= w (keys past the last row then fail too: pos_i < kend for
             // every stored row; the dense pass runs with w = n, the gated
@@ -903,13 +1002,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 for (int e4 = 0; e4 < 4; ++e4) {
                     const int k0 = kb * 32 + 8 * e4 + 4 * hh;   // keys k0 .. k0+3
                     int4 kp = {0, 0, 0, 0};
-                    if (MULTI) kp = *reinterpret_cast<const int4*>(kposp + k0);
+                    if (KPOS) kp = *reinterpret_cast<const int4*>(kposp + k0);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int c = kb * 32 + 8 * e4 + j;
                         bool ok;
                         if (!SORTED) {
                             ok = GATED ? c <= dpos : (uint32_t)(dpos - c) <= (uint32_t)a.w;
+                        } else if (SETS) {   // kp = position * 64 + the key token's group mask
+                            const int key = kt0 + k0 + j;
+                            ok = (key < kend) & (pos_i - (kp[j] >> 6) > a.w) &
+                                 ((kp[j] & gmask_i) != 0);
                         } else if (!MULTI) {
                             ok = c < dend;
                         } else {   // kp = position * 64 + the key token's other group
@@ -1432,7 +1535,7 @@ AttnArgs long_range_args(const AttnProblem& p) {
     a.ne = p.n * p.m;
     a.ntiles = (a.ne + a.TT - 1) / a.TT;
     a.total = p.B * p.Hkv * a.nslices * a.ntiles;
-    a.direct = attn_sorted_copies(p.n, p.d, p.m, p.force_copies != 0) ? 0 : 1;
+    a.direct = attn_sorted_copies(p.n, p.d, p.m, p.K, p.force_copies != 0) ? 0 : 1;
     if (!a.direct) {
         const AttnWorkspace ws = attn_workspace_layout(p);
         char* base = static_cast<char*>(p.workspace);
@@ -1453,9 +1556,70 @@ int attn_heads_per_wg(int hpk) {
     return g;
 }
 
+// Set pass (two groups per token, K <= 4): the group masks of the membership
+// sets, 4 bits each (set s in bits 4s .. 4s+3).
+int set_mask_table(int K) {
+    int lut = 0, s = 0;
+    for (int x = 0; x < K; ++x)
+        for (int y = x + 1; y < K; ++y) lut |= ((1 << x) | (1 << y)) << (4 * s++);
+    return lut;
+}
+
+// Set pass arguments: the sorted order lists the n tokens by membership set;
+// key rows come from set-sorted copies of K and V (contiguous key tiles).
+AttnArgs set_pass_args(const AttnProblem& p) {
+    AttnArgs a = make_args(p);
+    const AttnWorkspace ws = attn_workspace_layout(p);
+    char* base = static_cast<char*>(p.workspace);
+    a.perm = reinterpret_cast<const int32_t*>(base + ws.sperm);
+    a.offsets = reinterpret_cast<const int32_t*>(base + ws.soffs);
+    a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
+    a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
+    a.direct = 0;
+    a.set_lut = set_mask_table(p.K);
+    return a;
+}
+
+hipError_t launch_attn_set_prepare(const AttnProblem& p, hipStream_t stream) {
+    const AttnArgs a = set_pass_args(p);
+    const AttnWorkspace ws = attn_workspace_layout(p);
+    char* base = static_cast<char*>(p.workspace);
+    int32_t* sid = reinterpret_cast<int32_t*>(base + ws.sid);
+    const int S = attn_membership_sets(p.K);
+    const int64_t ntok = (int64_t)p.B * p.n;
+    hipLaunchKernelGGL(attn_set_id_kernel, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0,
+                       stream, p.ids, ntok, p.K, S, sid);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_group_sort(sid, p.B, p.n, S, const_cast<int32_t*>(a.perm),
+                          const_cast<int32_t*>(a.offsets), base + ws.shist, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_set_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0,
+                       stream, a.perm, a.offsets, p.ids, p.n, p.K, S, p.w, a.TT, a.ntiles,
+                       attn_tile_keys(p.d, kLongSets), a.set_lut, const_cast<int32_t*>(a.plan));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_order_kernel, dim3(p.B), dim3(256), 0, stream, a.plan, a.ntiles,
+                       const_cast<int32_t*>(a.order));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // set-sorted K and V (the gather also writes plain positions into spos,
+    // which the next kernel replaces by the (position, group mask) words)
+    const int64_t chunks = (int64_t)(p.n + KPOS_PAD) * (p.d / 8);
+    hipLaunchKernelGGL(attn_gather_kernel, dim3((unsigned)((chunks + 255) / 256), p.B * p.Hkv),
+                       dim3(256), 0, stream, p.k, p.v, a.perm, p.ids, p.n, p.n, 1, p.K, p.Hkv,
+                       p.d, const_cast<uint16_t*>(a.k), const_cast<uint16_t*>(a.v), a.spos);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_set_spos_kernel, dim3((p.n + KPOS_PAD + 255) / 256, p.B), dim3(256),
+                       0, stream, a.perm, p.ids, p.n, p.K, a.spos);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
+    if (attn_uses_sets(p.n, p.d, p.m, p.K)) return launch_attn_set_prepare(p, stream);
     const AttnArgs a = long_range_args(p);
     hipError_t e = hipSuccess;
     if (!a.direct) {
@@ -1490,6 +1654,13 @@ hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stre
 hipError_t launch_attn_long_range_apply(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
+    if (attn_uses_sets(p.n, p.d, p.m, p.K)) {
+        // one pass over the set-sorted tokens, merged with the window partial
+        AttnArgs a = set_pass_args(p);
+        a.merge = 1;
+        a.partial = 0;
+        return launch<kLongSets>(a, p.d, stream);
+    }
     AttnArgs a = long_range_args(p);
     if (p.m == 1) {
         a.merge = 1;     // start from the window partial, write the final output

@@ -82,11 +82,21 @@ constexpr int attn_long_range_tile_keys(int d) { return d == 32 ? 64 : 32; }
 // 256 bytes.
 inline int attn_pack_ints(int TT, int BN) { return (64 + 2 * TT + BN + 63) / 64 * 64; }
 
-// Whether the long-range pass reads group-sorted copies of K and V (made by
-// its prepare step) rather than key rows in place: always with two groups
-// per token; with one, when a kv head's K rows span 2^31 bytes or more (the
-// reach of a buffer resource), or when the caller asks for the copies.
-inline bool attn_sorted_copies(int n, int d, int m, bool force) {
+// Two groups per token with few groups (K <= 4, so at most 6 membership
+// sets): the long-range pass runs over tokens sorted by membership set.
+inline int attn_membership_sets(int K) { return K * (K - 1) / 2; }
+inline bool attn_uses_sets(int n, int d, int m, int K) {
+    (void)n;
+    (void)d;
+    return m == 2 && K <= 4;
+}
+// Whether the long-range pass reads sorted copies of K and V (made by its
+// prepare step) rather than key rows in place: always with two groups per
+// token (copies in membership-entry or membership-set order); with one, when
+// a kv head's K rows span 2^31 bytes or more (the reach of a buffer
+// resource), or when the caller asks for them.
+inline bool attn_sorted_copies(int n, int d, int m, int K, bool force) {
+    (void)K;
     return force || m > 1 || (int64_t)n * d * 2 >= ((int64_t)1 << 31);
 }
 
@@ -100,17 +110,24 @@ inline bool attn_sorted_copies(int n, int d, int m, bool force) {
 // and V (bf16 [B][Hkv][n*m][d]) and the sorted slots' positions (int32
 // [B][n*m + pad]). With m groups per token (m > 1) the sorted order lists
 // n*m membership entries, and the long-range pass writes one partial per
-// entry (fp16 [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge.
+// entry (fp16 [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge;
+// except on the set pass (attn_uses_sets), whose sorted order lists the n
+// tokens by membership set: then the set id per token, the set-sorted
+// positions and set offsets, the sort's per-block counts and the sorted
+// slots' (position, group mask) words, and no copies or per-entry partials.
 // The first two regions lead every layout, so the window pass, which uses
 // only them, takes the same offsets for every m.
 struct AttnWorkspace {
-    size_t og, lseg, plan, order, pack, ks, vs, spos, oge, lsege, total;
+    size_t og, lseg, plan, order, pack, ks, vs, spos, oge, lsege, sid, sperm, soffs, shist, total;
 };
-inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m,
-                                           bool copies) {
+inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m, int K,
+                                           bool force_copies) {
     AttnWorkspace w{};
+    const bool sets = attn_uses_sets(n, d, m, K);
+    const bool copies = attn_sorted_copies(n, d, m, K, force_copies);
+    const int S = attn_membership_sets(K);
     const int TT = attn_tokens_per_tile(Hq, Hkv);
-    const size_t ne = (size_t)n * m;
+    const size_t ne = sets ? (size_t)n : (size_t)n * m;
     const size_t ntiles = (ne + TT - 1) / TT;
     size_t off = 0;
     w.og = off;   off += align_up((size_t)B * Hq * n * d * 2);
@@ -122,21 +139,30 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d,
                   : 0;
     w.ks = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
     w.vs = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
-    w.spos = off; off += copies ? align_up((size_t)B * (ne + KPOS_PAD) * 4) : 0;
-    w.oge = off;  off += m > 1 ? align_up((size_t)B * Hq * ne * d * 2) : 0;
-    w.lsege = off; off += m > 1 ? align_up((size_t)B * Hq * ne * 8) : 0;
+    w.spos = off; off += (copies || sets) ? align_up((size_t)B * (ne + KPOS_PAD) * 4) : 0;
+    w.oge = off;  off += (m > 1 && !sets) ? align_up((size_t)B * Hq * ne * d * 2) : 0;
+    w.lsege = off; off += (m > 1 && !sets) ? align_up((size_t)B * Hq * ne * 8) : 0;
+    w.sid = off;  off += sets ? align_up((size_t)B * n * 4) : 0;
+    w.sperm = off; off += sets ? align_up((size_t)B * n * 4) : 0;
+    w.soffs = off; off += sets ? align_up((size_t)B * (S + 1) * 4) : 0;
+    w.shist = off; off += sets ? align_up(group_sort_workspace(B, n, S)) : 0;
     w.total = off;
     return w;
 }
 inline AttnWorkspace attn_workspace_layout(const AttnProblem& p) {
-    return attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m,
-                                 attn_sorted_copies(p.n, p.d, p.m, p.force_copies != 0));
+    return attn_workspace_layout(p.B, p.Hq, p.Hkv, p.n, p.d, p.m, p.K, p.force_copies != 0);
 }
-inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w, int m = 1,
+// The window pass alone uses only the leading two regions (partial, L/e),
+// which every layout above shares.
+inline size_t attn_window_workspace(int B, int Hq, int Hkv, int n, int d, int w) {
+    if (!attn_has_long_range(n, w)) return 0;
+    const AttnWorkspace l = attn_workspace_layout(B, Hq, Hkv, n, d, 1, 1, false);
+    return l.plan;
+}
+inline size_t attn_workspace(int B, int Hq, int Hkv, int n, int d, int w, int K, int m = 1,
                              bool force_copies = false) {
     if (!attn_has_long_range(n, w)) return 0;
-    return attn_workspace_layout(B, Hq, Hkv, n, d, m, attn_sorted_copies(n, d, m, force_copies))
-        .total;
+    return attn_workspace_layout(B, Hq, Hkv, n, d, m, K, force_copies).total;
 }
 
 // The long-range pass: prepare (sorted K/V copies, tile plan and order, row

@@ -139,12 +139,19 @@ def test_workspace_sizes():
     # top-k, m = 1: the same layout
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 1, 32) == \
         lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32)
-    # m = 2: plan over 512 entries (8 tiles), sorted K, V and positions over 512 entries, then
-    # per-entry fp16 partials [B][Hq][512][d] and their pairs [B][Hq][512] (no row ends: the
-    # two-group pass masks by key position)
+    # m = 2, K = 5 (membership entries): plan over 512 entries (8 tiles), tile order, sorted K, V
+    # and positions over 512 entries, then per-entry fp16 partials [B][Hq][512][d] and their
+    # pairs [B][Hq][512] (no row ends: the two-group pass masks by key position)
+    assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 5, 2, 32) == (
+        256 * 2 * 32 * 2 + 4096 + 8 * 128 + 256 + 2 * (512 * 32 * 2) + 768 * 4
+        + 512 * 2 * 32 * 2 + 512 * 2 * 8)
+    # m = 2, K = 4 (six membership sets, the set pass): plan and order over the 256 tokens
+    # (4 tiles), set-sorted K and V [B][Hkv][n][d], the slots' (position, group mask) words
+    # [B][n + 256], then the set id per token, the set-sorted positions, the 7 set offsets and
+    # the sort's per-block counts
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 2, 32) == (
-        256 * 2 * 32 * 2 + 4096 + 8 * 128 + 2 * (512 * 32 * 2) + 768 * 4
-        + 512 * 2 * 32 * 2 + 512 * 2 * 8 + 256)
+        256 * 2 * 32 * 2 + 4096 + 4 * 128 + 256 + 2 * (256 * 32 * 2) + 512 * 4 + 256 * 4
+        + 256 * 4 + 256 + 256)
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 3, 32) == 0
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 2, 255) == 0
 
@@ -249,14 +256,18 @@ def _attn_topk(fn="focus_attn_topk_fwd", m=2, **kw):
     (2, dict(d=48), UNSUPPORTED, "d_head"),
     (2, dict(scale=0.0), INVALID, "scale"),
     (2, dict(ws=None), WORKSPACE, "workspace"),
-    # enough for m = 1 but not for the per-entry partials of m = 2
-    (2, dict(wsb=400000), WORKSPACE, "too small"),
+    # enough for m = 1 but not for the per-entry partials of m = 2 (K = 5: membership entries)
+    (2, dict(wsb=400000, K=5), WORKSPACE, "too small"),
+    # K = 4 (the set pass): one byte short of its own size
+    (2, dict(wsb=275711), WORKSPACE, "too small"),
 ])
 def test_attn_topk_rejects(fn, m, kw, code, msg):
     if kw.get("wsb") == 400000:
-        need1 = focus.lib().focus_attn_workspace_bytes(1, 4, 2, 256, 64, 4, 16)
-        need2 = focus.lib().focus_attn_topk_workspace_bytes(1, 4, 2, 256, 64, 4, 2, 16)
+        need1 = focus.lib().focus_attn_workspace_bytes(1, 4, 2, 256, 64, 5, 16)
+        need2 = focus.lib().focus_attn_topk_workspace_bytes(1, 4, 2, 256, 64, 5, 2, 16)
         assert need1 <= 400000 < need2
+    if kw.get("wsb") == 275711:
+        assert focus.lib().focus_attn_topk_workspace_bytes(1, 4, 2, 256, 64, 4, 2, 16) == 275712
     assert _attn_topk(fn, m, **kw) == code
     assert msg in _err()
 
