@@ -531,6 +531,8 @@ def main():
         lr_visited = lr
     else:
         win, lr, lr_visited = metrics.pair_counts_multi(gids, w)
+        if metrics.uses_set_pass(K, m):
+            lr_visited = lr   # the set pass meets each kept pair once
     pairs = win + lr
     flops = metrics.attn_flops(pairs, Hq, d)
     # the two attention passes; the tile plan (prepare) runs beside the window
@@ -541,8 +543,11 @@ def main():
     tt = 128 // metrics.heads_per_workgroup(Hq, Hkv)
     bn = metrics.tile_keys(d)
     cwin = B * metrics.window_computed_pairs(n, w, tt, bn)
-    clr = metrics.long_range_computed_pairs(gids.reshape(B, n * m), perm.cpu().numpy(),
-                                            offs.cpu().numpy(), w, tt, bn, m)
+    if metrics.uses_set_pass(K, m):
+        clr = metrics.set_long_range_computed_pairs(gids, K, w, tt, bn)
+    else:
+        clr = metrics.long_range_computed_pairs(gids.reshape(B, n * m), perm.cpu().numpy(),
+                                                offs.cpu().numpy(), w, tt, bn, m)
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -590,7 +595,8 @@ def main():
     kern = max(("long_range_apply", "window"), key=lambda nm: phase[nm])
     kflops = metrics.attn_flops(lr if kern == "long_range_apply" else win, Hq, d)
     ach = kflops / (phase[kern] * 1e-3) / 1e12
-    kname = (f"attn_kernel<{d},{1 if m == 1 else 3}>" if kern == "long_range_apply"
+    lr_phase = 1 if m == 1 else (7 if metrics.uses_set_pass(K, m) else 3)
+    kname = (f"attn_kernel<{d},{lr_phase}>" if kern == "long_range_apply"
              else f"attn_kernel<{d},0>")
     res["roofline"] = {"kernel": kname + (" (long-range pass + merge)" if kern == "long_range_apply"
                                           else " (window pass)"),

@@ -132,3 +132,40 @@ def long_range_computed_pairs(ids: np.ndarray, perm: np.ndarray, offsets: np.nda
                 kend = ob + int(np.searchsorted(pb[ob:qhi], m * (maxpos - w), side="left"))
                 total += (kend - ob + BN - 1) // BN
     return total * BN * TT
+
+
+def uses_set_pass(K: int, m: int) -> bool:
+    """Two groups per token with K <= 4: the long-range pass runs over the
+    tokens sorted by membership set (each kept pair visited once)."""
+    return m == 2 and K <= 4
+
+
+def set_long_range_computed_pairs(ids: np.ndarray, K: int, w: int, TT: int, BN: int) -> int:
+    """Per query head, summed over the batch, for the set pass (ids
+    [B][n][2]): tokens stably sorted by the index of their group pair; for
+    each tile of TT sorted tokens and each set sharing a group with some
+    token of the tile, the key tiles of that set's segment below the first
+    slot whose position is >= (largest position in the tile) - w, times TT."""
+    B, n, _ = ids.shape
+    pairs = [(a, b) for a in range(K) for b in range(a + 1, K)]
+    code = {p: i for i, p in enumerate(pairs)}
+    masks = np.array([(1 << a) | (1 << b) for a, b in pairs], dtype=np.int64)
+    total = 0
+    for bb in range(B):
+        lo = np.minimum(ids[bb, :, 0], ids[bb, :, 1])
+        hi = np.maximum(ids[bb, :, 0], ids[bb, :, 1])
+        sid = np.array([code[(int(x), int(y))] for x, y in zip(lo, hi)], dtype=np.int64)
+        perm = np.argsort(sid, kind="stable")
+        offs = np.concatenate([[0], np.cumsum(np.bincount(sid, minlength=len(pairs)))])
+        tmask = masks[sid]
+        for s0 in range(0, n, TT):
+            rows = perm[s0:s0 + TT]
+            umask = int(np.bitwise_or.reduce(tmask[rows]))
+            maxpos = int(rows.max())
+            for t in range(len(pairs)):
+                if not masks[t] & umask:
+                    continue
+                seg = perm[offs[t]:offs[t + 1]]
+                keys = int(np.searchsorted(seg, maxpos - w, side="left"))
+                total += (keys + BN - 1) // BN
+    return total * BN * TT

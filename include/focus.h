@@ -304,12 +304,20 @@ focus_status focus_attn_long_range_apply(const uint16_t* q, const uint16_t* k, c
  *   A_i = { j : 0 <= i - j <= window }  U  { j : j < i - window,
  *           groups(i) and groups(j) intersect },  groups(t) = group_ids[b][t][*]
  *
- * with out and lse as for focus_attn_fwd. Each kept pair is counted once: a
- * pair sharing two groups meets in both groups' segments and is kept in the
- * segment of the lower group only. The long-range pass visits every group
- * segment of both tokens, writes one partial result per membership entry,
- * and a final kernel merges the window partial and the m entry partials by
- * log-sum-exp.
+ * with out and lse as for focus_attn_fwd. Each kept pair is counted once.
+ * The long-range pass takes one of two forms, chosen by K:
+ *   - m = 2 and K <= 4 (at most 6 membership sets; the pages' runs use
+ *     K = 4, k = 2): the prepare call sorts the tokens by their set of two
+ *     groups (a counting sort into the workspace; perm and group_offsets are
+ *     checked but not read) and gathers set-sorted copies of K and V; a query
+ *     tile of set S visits the key segments of every set sharing a group
+ *     with S, so each kept pair meets exactly once, and the pass merges the
+ *     window partial and writes out and lse itself.
+ *   - otherwise (membership entries): a pair sharing two groups meets in
+ *     both groups' segments and is kept in the segment of the lower group
+ *     only; the pass visits every group segment of both tokens, writes one
+ *     partial result per membership entry, and a final kernel merges the
+ *     window partial and the m entry partials by log-sum-exp.
  *
  * group_ids [B][n][m] (distinct groups per token, as from focus_assign_topk),
  * perm [B][n*m] and group_offsets [B][K+1] from focus_group_sort over the
@@ -321,7 +329,7 @@ focus_status focus_attn_long_range_apply(const uint16_t* q, const uint16_t* k, c
  * focus_attn_topk_fwd == focus_attn_window then
  * focus_attn_topk_long_range_merge on one stream, with the workspace of
  * focus_attn_topk_workspace_bytes() passed to both (the window pass uses its
- * leading part, laid out as for m = 1).
+ * leading part, the window partial, laid out the same for every m).
  * ---------------------------------------------------------------------- */
 size_t focus_attn_topk_workspace_bytes(int B, int Hq, int Hkv, int n, int d_head, int K, int m,
                                        int window);
@@ -341,8 +349,10 @@ focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t*
                                               void* workspace, size_t workspace_bytes,
                                               focus_stream_t stream);
 /* focus_attn_topk_long_range_merge in two calls, as for m = 1 above:
- * prepare (sorted K/V over the n*m entries, plan and order; may run beside
- * the window pass) then apply (the per-entry partials and the final merge). */
+ * prepare (sorted K/V over the n*m entries, or over the tokens in
+ * membership-set order when K <= 4, plan and order; may run beside the window
+ * pass) then apply (the per-entry partials and the final merge, or the set
+ * pass with its merge). */
 focus_status focus_attn_topk_long_range_prepare(const uint16_t* q, const uint16_t* k,
                                                 const uint16_t* v, const int32_t* group_ids,
                                                 const int32_t* perm,

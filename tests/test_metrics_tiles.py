@@ -94,3 +94,40 @@ def test_heads_per_workgroup_and_tile_keys():
     assert metrics.heads_per_workgroup(24, 2) == 4
     assert metrics.heads_per_workgroup(12, 2) == 2
     assert metrics.tile_keys(32) == 64 and metrics.tile_keys(64) == 32 and metrics.tile_keys(128) == 32
+
+
+def brute_set_long_range(ids, K, w, TT, BN):
+    """The set pass's key tiles by direct enumeration: sort tokens by their
+    pair of groups (lexicographic pair index, stable), then per tile of TT
+    tokens and per set sharing a group with any of them, count that set's
+    tokens (in position order) whose position is below (largest position in
+    the tile) - w one by one."""
+    total = 0
+    pairs = [(a, b) for a in range(K) for b in range(a + 1, K)]
+    for b in range(ids.shape[0]):
+        n = ids.shape[1]
+        key = [pairs.index(tuple(sorted((int(ids[b, t, 0]), int(ids[b, t, 1]))))) for t in range(n)]
+        order = sorted(range(n), key=lambda t: (key[t], t))
+        for s0 in range(0, n, TT):
+            rows = order[s0:s0 + TT]
+            groups = set()
+            for t in rows:
+                groups |= {int(ids[b, t, 0]), int(ids[b, t, 1])}
+            maxpos = max(rows)
+            for si, (x, y) in enumerate(pairs):
+                if x not in groups and y not in groups:
+                    continue
+                keys = sum(1 for t in range(n) if key[t] == si and t < maxpos - w)
+                total += -(-keys // BN)
+    return total * BN * TT
+
+
+@pytest.mark.parametrize("n,K,w,TT,BN", [(1, 2, 0, 16, 32), (90, 4, 5, 16, 32), (300, 3, 20, 32, 64),
+                                         (500, 4, 40, 16, 32)])
+def test_set_long_range_matches_enumeration(n, K, w, TT, BN):
+    rng = np.random.default_rng(n + K)
+    ids = np.stack([np.stack([rng.choice(K, size=2, replace=False) for _ in range(n)])])
+    got = metrics.set_long_range_computed_pairs(ids, K, w, TT, BN)
+    assert got == brute_set_long_range(ids, K, w, TT, BN)
+    kept, _ = metrics.long_range_pairs_multi(ids[0], w)
+    assert got >= kept
