@@ -4,11 +4,11 @@
                     [--skip-cpu-baseline] [--skip-dense] [--cold-mall] [--graph]
 
 One step = the whole hot path on one batch of seeded synthetic input already
-resident in HBM, all through the C ABI: focus_attn_window (the window pass,
-which needs no group data) on a second stream, while focus_assign ->
-focus_group_sort -> focus_attn_long_range_prepare (group-sorted K/V copies
-and the tile plan) run on the main stream; then, once both are done,
-focus_attn_long_range_apply on the main stream (together the calls are
+resident in HBM, all through the C ABI: focus_assign -> focus_group_sort ->
+focus_attn_long_range_prepare (the tile plan) on the main stream, with
+focus_attn_window (the window pass, which needs no group data) enqueued on a
+second stream right after focus_assign, so that both run together; then,
+once both are done, focus_attn_long_range_apply on the main stream (together the calls are
 focus_attn_fwd). --no-overlap runs all five calls in order on one stream.
 Workloads with m = 2 groups per token use focus_assign_topk, the sort of the
 n*m membership entries and the focus_attn_topk_long_range_* calls instead.
@@ -451,6 +451,11 @@ def main():
         mark(0, stream)
         if overlap:
             side.wait_stream(stream)   # the previous apply has consumed the workspace
+            # the assignment is enqueued ahead of the window pass, so its short
+            # workgroups are dispatched first instead of waiting for the window
+            # pass's to retire one by one
+            assign()
+            mark(1, stream)
         else:
             assign()
             mark(1, stream)
@@ -462,8 +467,6 @@ def main():
         focus.focus_attn_window(q, k, v, K, w, scale, workspace=ws_t, out=out, stream=ws_stream)
         mark(6, ws_stream)
         if overlap:
-            assign()
-            mark(1, stream)
             focus.focus_group_sort(ids, K, perm=perm, group_offsets=offs, workspace=ws_s)
             mark(2, stream)
             prepare()
