@@ -17,11 +17,13 @@
 // bf16(x - hi) for both h and W, and hi*hi + hi*lo + lo*hi accumulated in
 // fp32 (the dropped lo*lo term is ~2^-16 of each product).
 //
-// Memory layout for coalescing: the hidden slice of a step (32 tokens x 64
-// columns, 8 KB) is copied HBM -> LDS with global_load_lds_dwordx4, each copy
-// one contiguous 1 KB (4 token rows); the W^T operand is stored by the
-// prologue in MFMA fragment order, so every fragment load is also one
-// contiguous 1 KB.
+// Memory layout for coalescing: the hidden slice of a stage (32 tokens x 256
+// columns, 32 KB) is copied HBM -> LDS with global_load_lds_dwordx4, each
+// copy one contiguous 1 KB of one token row (shorter runs per row, e.g. 256
+// bytes, measured about 15 % slower on gfx950); the four waves share the
+// stage and each multiplies its own 64 of the 256 columns. The W^T operand
+// is stored by the prologue in MFMA fragment order, so every fragment load is
+// also one contiguous 1 KB.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -106,11 +108,11 @@ __device__ __forceinline__ int other_half_i(int x) {
 
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Per-wave LDS slice of one step: 32 token rows x 64 fp32 columns (256 B per
-// row); 16-byte chunk c of row r sits in slot c ^ (r & 15), so the 16 rows
-// read by one quarter-wave hit 16 distinct chunk slots.
-constexpr int HROWB = 256;
-constexpr int HSTEPB = 32 * HROWB;  // 8 KB
+// LDS stage: 32 token rows x 256 fp32 columns (1 KB per row); 16-byte chunk
+// c of row r sits in slot c ^ (r & 15), so the 16 rows read by one
+// quarter-wave at the same logical chunk hit 16 distinct bank groups.
+constexpr int HROWB = 1024;
+constexpr int HSTAGEB = 32 * HROWB;  // 32 KB
 
 template <int NB>
 struct WRegs {
@@ -148,33 +150,33 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
     const float* __restrict__ hidden, const __bf16* __restrict__ wfrag,
     const float* __restrict__ bias, int64_t ntok, int d_model, int dpad, int K,
     int32_t* __restrict__ ids, float* __restrict__ margin, float* __restrict__ scores) {
-    // [wave][buffer][8 KB]; reused for the cross-wave reduction at the end.
-    __shared__ __attribute__((aligned(1024))) unsigned char hbuf[4 * 2 * HSTEPB];
+    // Two 32 KB stages; reused for the cross-wave reduction at the end.
+    __shared__ __attribute__((aligned(1024))) unsigned char hbuf[2 * HSTAGEB];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int rl = lane & 31, hh = lane >> 5;
     const int64_t t0 = (int64_t)blockIdx.x * 32;
     const int64_t tok = t0 + rl;
     const bool tvalid = tok < ntok;
 
-    // The 4 waves split the 64-column steps into quarters.
+    // Stage st holds columns [256 st, 256 st + 256); wave w multiplies its
+    // 64-column step s = 4 st + w (when s < NS, the 64-column steps of dpad).
     const int NS = dpad / 64;
-    const int s_beg = (NS * wave) / 4, s_end = (NS * (wave + 1)) / 4;
-    unsigned char* mybuf = hbuf + wave * 2 * HSTEPB;
+    const int NSTG = (NS + 3) / 4;
 
-    // This lane's copy share: for copy i (1 KB) row 4*i + lane/16, slot lane%16.
-    const int crow0 = lane >> 4, cslot = lane & 15;
-
-    auto issue = [&](int s, unsigned char* dst, WRegs<NB>& wr) {
+    // Copies of a stage: wave w copies rows 8w .. 8w+7, one 1 KB run each;
+    // lane l fills slot l of the row, i.e. logical chunk l ^ (row & 15).
+    auto issue = [&](int st, unsigned char* dst, WRegs<NB>& wr) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = 4 * i + crow0;
-            const int c = cslot ^ (r & 15);
+            const int r = 8 * wave + i;
+            const int c = lane ^ (r & 15);
             const int64_t trow = min(t0 + r, ntok - 1);
-            const int d = min(64 * s + 4 * c, d_model - 4);  // past d_model: W^T is zero there
+            const int d = min(256 * st + 4 * c, d_model - 4);  // past d_model: W^T is zero there
             __builtin_amdgcn_global_load_lds(hidden + trow * d_model + d,
-                                             (__attribute__((address_space(3))) void*)(dst + i * 1024),
+                                             (__attribute__((address_space(3))) void*)(dst + r * HROWB),
                                              16, 0, 0);
         }
+        const int s = min(4 * st + wave, NS - 1);
 #pragma unroll
         for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
@@ -194,8 +196,8 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
     auto compute = [&](const unsigned char* src, const WRegs<NB>& wr) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // columns 32*hh + 8*e .. +8 of token rl: logical chunks c, c+1
-            const int c = 8 * hh + 2 * e;
+            // columns 64*wave + 32*hh + 8*e .. +8 of token rl: logical chunks c, c+1
+            const int c = 16 * wave + 8 * hh + 2 * e;
             const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + rl * HROWB + ((c ^ (rl & 15)) << 4));
             const f32x4 x1 =
                 *reinterpret_cast<const f32x4*>(src + rl * HROWB + (((c + 1) ^ (rl & 15)) << 4));
@@ -215,18 +217,21 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
         }
     };
 
-    // Two buffers per wave; the copy of step s+1 is in flight while step s
-    // computes. Each wave reads only its own slice: no barrier needed.
+    // Two stages; the copy of stage st+1 is in flight while stage st
+    // computes. The barrier after each stage's copies have landed also
+    // tells every wave that the other buffer's previous stage is done.
     WRegs<NB> wa, wb;
-    if (s_beg < s_end) issue(s_beg, mybuf, wa);
-    for (int s = s_beg; s < s_end; s += 2) {
+    issue(0, hbuf, wa);
+    for (int st = 0; st < NSTG; st += 2) {
         wait_vm();
-        if (s + 1 < s_end) issue(s + 1, mybuf + HSTEPB, wb);
-        compute(mybuf, wa);
-        if (s + 1 >= s_end) break;
+        __syncthreads();
+        if (st + 1 < NSTG) issue(st + 1, hbuf + HSTAGEB, wb);
+        if (4 * st + wave < NS) compute(hbuf, wa);
+        if (st + 1 >= NSTG) break;
         wait_vm();
-        if (s + 2 < s_end) issue(s + 2, mybuf, wa);
-        compute(mybuf + HSTEPB, wb);
+        __syncthreads();
+        if (st + 2 < NSTG) issue(st + 2, hbuf, wa);
+        if (4 * (st + 1) + wave < NS) compute(hbuf + HSTAGEB, wb);
     }
 
     // Cross-wave sum in a fixed order (deterministic), through LDS.
