@@ -376,11 +376,12 @@ def focus_attn_long_range_prepare(q, k, v, group_ids, perm, group_offsets, K: in
                                   scale: float, *, workspace, out, out_dtype=torch.bfloat16,
                                   lse=None, stream=None):
     """First half of focus_attn_long_range_merge: the tile plan and order,
-    the row ends and (with two groups per token, or key rows of one head
-    spanning 2^31 bytes or more) group-sorted K/V copies, written into
-    workspace. It
-    reads only k, v and the group data (pass the out and lse that the apply
-    call will get), so it may run beside focus_attn_window."""
+    one packed record per ordered tile (plan record, tile index, each row's
+    entry and key-slot end, the first key tile's positions) and, when key
+    rows of one head span 2^31 bytes or more, group-sorted K/V copies,
+    written into workspace. It reads only k, v and the group data (pass the
+    out and lse that the apply call will get), so it may run beside
+    focus_attn_window."""
     _attn_call("focus_attn_long_range_prepare", q, k, v, group_ids, perm, group_offsets, K,
                window, scale, out, out_dtype, lse, False, workspace, stream)
 
