@@ -79,16 +79,17 @@ def parse():
 
 TRAFFIC_SOURCES = ("group_gated_sparse_amd/csrc/attn.hip", "group_gated_sparse_amd/csrc/focus_internal.h",
                    "group_gated_sparse_amd/csrc/assign.hip", "group_gated_sparse_amd/csrc/sort.hip",
-                   "group_gated_sparse_amd/build.py")
+                   "group_gated_sparse_amd/csrc/sinkhorn.hip", "group_gated_sparse_amd/build.py")
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(key, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic_<workload>.txt: FETCH_SIZE and WRITE_SIZE
+    summary (profiles/hbm_traffic_<key>.txt, key = the workload's name, or
+    "<op>_<workload>" for the training-time ops: FETCH_SIZE and WRITE_SIZE
     scaled by a plain-copy calibration), or None when there is none or it was
     taken on kernel sources other than the ones in this tree."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{key}.txt")
     if not os.path.exists(path):
         return None
     h = hashlib.sha256()
@@ -102,6 +103,19 @@ def measured_traffic(workload, kernel):
         elif line.startswith(f"kernel {kernel}:"):
             value = float(line.split("hbm_bytes")[1].split()[0])
     return value if sha == h.hexdigest() else None
+
+
+def copy_probe(torch, res):
+    """One plain 1 GiB device-to-device copy after the timed work: a dispatch
+    of known size for calibrating the HBM byte counters of a profiled run."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    res["copy_probe_bytes"] = src.numel() * 4
+    del src, dst
 
 
 def device_info(torch):
@@ -229,6 +243,9 @@ def bench_sinkhorn(args, wl):
     # algorithmic bytes of one Sinkhorn call: every pass reads the scores once,
     # the last also writes G
     sk_bytes = (T + 1) * B * n * K * 4 + B * n * K * 4
+    # the scores kernel: one 32-group block of the split W^T per workgroup
+    # pass up to 32 groups, two beyond
+    sc_kernel = f"assign_argmax_kernel<{1 if K <= 32 else 2},0>"
     res = {
         "metric": "Sinkhorn soft assignment (scores + rounds), tokens/s, 1 GPU",
         "value": B * n / (ms * 1e-3),
@@ -239,17 +256,21 @@ def bench_sinkhorn(args, wl):
         "config": {"workload": wl.name, "op": "sinkhorn", "B": B, "n": n, "K": K,
                    "d_model": wl.d_model, "d_proj": wl.d_proj, "iters": T, "tau": args.tau},
         "phase_ms": {"scores": sc_ms, "sinkhorn": sk_ms},
-        "roofline": {"kernel": "assign_argmax_kernel (scores)", "bound": "hbm",
+        "roofline": {"kernel": f"{sc_kernel} (scores)", "bound": "hbm",
                      "achieved": B * n * wl.d_model * 4 / (sc_ms * 1e-3) / 1e9,
                      "peak": metrics.MI355X_HBM_GBPS, "unit": "GB/s",
                      "frac": B * n * wl.d_model * 4 / (sc_ms * 1e-3) / 1e9 / metrics.MI355X_HBM_GBPS,
-                     "traffic": None},
+                     "traffic": measured_traffic(f"sinkhorn_{wl.name}", sc_kernel),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)"},
         "sinkhorn_roofline": {"kernel": "sinkhorn_pass_kernel x (iters + 1)", "bound": "hbm",
                               "achieved": sk_bytes / (sk_ms * 1e-3) / 1e9,
                               "peak": metrics.MI355X_HBM_GBPS, "unit": "GB/s",
                               "frac": sk_bytes / (sk_ms * 1e-3) / 1e9 / metrics.MI355X_HBM_GBPS,
                               "bytes_per_call": sk_bytes},
     }
+    if args.copy_probe:
+        copy_probe(torch, res)
     if not args.skip_cpu_baseline:
         import oracle
         t0 = time.perf_counter()
@@ -261,7 +282,8 @@ def bench_sinkhorn(args, wl):
         oracle.assign_scores(x["hidden"][:, :rows], x["P"], x["C"], x["bias"])
         t_a = (time.perf_counter() - t0) * n / rows
         res["cpu_baseline"] = {"value": B * n / (t_s + t_a), "unit": "tokens/s",
-                               "cores": oracle.max_threads(), "kind": "oracle",
+                               "cores": oracle.max_threads(), "host_cpu": host_cpu(),
+                               "kind": "oracle",
                                "sample": f"oracle scores and Sinkhorn ({T} rounds) on the first "
                                          f"{rows} tokens of each sequence, scaled by n / {rows}"}
     print(json.dumps(res), flush=True)
@@ -330,7 +352,11 @@ def bench_soft_gate(args, wl):
                      "bound": "mfma", "achieved": flops / (ms * 1e-3) / 1e12,
                      "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                      "frac": flops / (ms * 1e-3) / 1e12 / metrics.MI355X_BF16_DENSE_TFLOPS,
-                     "traffic": None, "flops_per_launch": flops, "avg_launch_ms": ev_ms},
+                     "traffic": measured_traffic(f"soft_gate_{wl.name}",
+                                                 f"attn_kernel<{d},{4 + (KG // 32)}>"),
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "flops_per_launch": flops, "avg_launch_ms": ev_ms},
     }
     if not args.skip_dense:
         focus.dense_causal_attn_fwd(q, k, v, wl.softmax_scale, out=out)
@@ -343,6 +369,8 @@ def bench_soft_gate(args, wl):
         res["dense_ms"] = e0.elapsed_time(e1) / args.dense_iters
         res["gate_overhead_vs_dense"] = ms / res["dense_ms"]
         log(f"dense {res['dense_ms']:.3f} ms")
+    if args.copy_probe:
+        copy_probe(torch, res)
     if not args.skip_cpu_baseline:
         import oracle
         rng = np.random.default_rng(7)
@@ -355,7 +383,8 @@ def bench_soft_gate(args, wl):
         i = rows % n
         done = int((i + 1).sum())
         res["cpu_baseline"] = {"value": metrics.attn_flops(done, 1, d) / t / 1e12,
-                               "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+                               "unit": "TFLOP/s", "cores": oracle.max_threads(), "host_cpu": host_cpu(),
+                               "kind": "oracle",
                                "sample": f"fp64 oracle on 4096 random query rows ({done} causal "
                                          f"pairs, {t:.1f} s)"}
     print(json.dumps(res), flush=True)
@@ -630,14 +659,7 @@ def main():
         log(f"dense {dense_ms:.3f} ms ({res['dense_tflops']:.1f} TFLOP/s)")
 
     if args.copy_probe:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dv)
-        dst = torch.empty_like(src)
-        src.fill_(1.0)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        res["copy_probe_bytes"] = src.numel() * 4
-        del src, dst
+        copy_probe(torch, res)
 
     del hidden, q, k, v, out, ws_t
     torch.cuda.empty_cache()
