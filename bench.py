@@ -577,9 +577,12 @@ def main():
     cwin = B * metrics.window_computed_pairs(n, w, tt, bn)
     if metrics.uses_set_pass(K, m):
         clr = metrics.set_long_range_computed_pairs(gids, K, w, tt, bn)
+    elif m == 2:
+        clr = metrics.entry_long_range_computed_pairs(gids.reshape(B, n * m), perm.cpu().numpy(),
+                                                      offs.cpu().numpy(), w, tt, bn)
     else:
-        clr = metrics.long_range_computed_pairs(gids.reshape(B, n * m), perm.cpu().numpy(),
-                                                offs.cpu().numpy(), w, tt, bn, m)
+        clr = metrics.long_range_computed_pairs(gids.reshape(B, n), perm.cpu().numpy(),
+                                                offs.cpu().numpy(), w, tt, bn)
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -630,15 +633,21 @@ def main():
     lr_phase = 1 if m == 1 else (7 if metrics.uses_set_pass(K, m) else 3)
     kname = (f"attn_kernel<{d},{lr_phase}>" if kern == "long_range_apply"
              else f"attn_kernel<{d},0>")
-    res["roofline"] = {"kernel": kname + (" (long-range pass + merge)" if kern == "long_range_apply"
-                                          else " (window pass)"),
+    # the entry passes (two groups per token, K >= 5) launch their kernel
+    # twice per step, once per membership index
+    launches = 2 if kern == "long_range_apply" and lr_phase == 3 else 1
+    what = {0: " (window pass)", 1: " (long-range pass + merge)", 7: " (set pass + merge)",
+            3: " (two entry passes, merged in place)"}
+    res["roofline"] = {"kernel": kname + what[lr_phase if kern == "long_range_apply" else 0],
                        "bound": "mfma", "achieved": ach,
                        "peak": metrics.MI355X_BF16_DENSE_TFLOPS, "unit": "TFLOP/s",
                        "frac": ach / metrics.MI355X_BF16_DENSE_TFLOPS,
                        "traffic": measured_traffic(wl.name, kname),
                        "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                        "copy-calibrated)",
-                       "flops_per_launch": kflops, "avg_launch_ms": phase[kern]}
+                       "launches_per_step": launches,
+                       "flops_per_launch": kflops / launches,
+                       "avg_launch_ms": phase[kern] / launches}
 
     if not args.skip_dense:
         log(f"dense causal baseline x{args.dense_iters}")

@@ -77,7 +77,9 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kProbSumCap = 256.0f;  // a lane's probability sum that triggers a rescale
 constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 
-// kLongMulti: the long-range pass over membership entries, two groups per token.
+// kLongMulti: the long-range pass over membership entries, two groups per
+// token (K >= 5): launched once per membership index, over the tokens' first
+// then second group.
 // kLongSets: the long-range pass with two groups per token and few groups
 // (K <= 4), over tokens sorted by their membership set.
 // kSoftGate + s (s = 0, 1, 2): the training-time soft-gated pass over every
@@ -90,9 +92,12 @@ struct AttnArgs {
     const uint16_t* k;      // sequence order (window / dense) or sorted copy (long-range)
     const uint16_t* v;
     const int32_t* ids;
-    const int32_t* perm;
+    const int32_t* perm;    // sorted key order (long-range passes)
     const int32_t* offsets;
-    const int32_t* plan;    // long-range tile plan [B][ntiles][PLAN_INTS]
+    const int32_t* qperm;   // entry passes: the query order's entries [B][2n]
+    int half;               // entry passes: membership index of this launch's query rows
+    const int32_t* plan;    // long-range tile plan [B][tiles][PLAN_INTS] (entry passes:
+                            // [B][2][ntiles][PLAN_INTS], one half per membership index)
     const int32_t* order;   // long-range pass: sorted query tiles, most work first [B][ntiles]
     const int32_t* pack;    // long-range pass (one group per token): a record per ordered tile
     int pack_ints;          // ints per packed record
@@ -100,16 +105,18 @@ struct AttnArgs {
     int set_lut;            // set pass: group mask of membership set s in bits 4s .. 4s+3
     _Float16* og;           // window partial [B][Hq][n][D]: O * 2^-e in fp16 (|.| < 1)
     f32x2* lseg;            // per row (log2-sum-exp L or -inf: no key, e)
+    _Float16* og_dst;       // where a partial is written (og, except in the first entry
+    f32x2* lseg_dst;        // pass, which must not overwrite the partial it merges)
     void* out;
     float* lse;
     int B, Hq, Hkv, n, K, w;
-    int ne;        // slots of the tiled order: n, or n*m entries in the multi pass
+    int ne;        // slots of the sorted key order: n, or n*2 entries in the entry passes
     int hpk;       // Hq / Hkv
     int G;         // query heads packed per workgroup
     int TT;        // tokens per workgroup tile (ROWS / G, a power of two)
     int tt_log;    // log2(TT)
     int nslices;   // hpk / G
-    int ntiles;    // ceil(n / TT)
+    int ntiles;    // ceil(n / TT): query tiles (of one launch)
     int total;     // workgroups
     float sl2;     // scale * log2(e)
     const uint16_t* gs;   // soft-gated pass: bf16 hi/lo split of the soft assignments,
@@ -263,8 +270,7 @@ __global__ __launch_bounds__(256) void attn_gather_kernel(const uint16_t* __rest
 // tile) - w. Positions increase inside a segment, so that cut is a binary
 // search, and no later slot of the segment can pair with any query of g here.
 // kfull: slots below it pair with every query of g in the tile (position
-// below (smallest query position) - w). Slots hold entries e of position
-// e / m, and e / m < bound exactly when e < m * bound.
+// below (smallest query position) - w).
 __device__ __forceinline__ int first_slot_at_or_above(const int32_t* perm_b, int lo, int hi,
                                                       int bound) {
     while (lo < hi) {
@@ -274,19 +280,113 @@ __device__ __forceinline__ int first_slot_at_or_above(const int32_t* perm_b, int
     return lo;
 }
 __device__ __forceinline__ void segment_range(const int32_t* perm_b, const int32_t* offb, int ne,
-                                              int m, int w, int s0, int s1, int g, int& ob,
-                                              int& kend, int& kfull) {
+                                              int w, int s0, int s1, int g, int& ob, int& kend,
+                                              int& kfull) {
     ob = clampi(offb[g], 0, ne);
     const int oe = clampi(offb[g + 1], ob, ne);
     const int qlo = max(s0, ob), qhi = min(s1, oe);
     kend = ob;
     kfull = ob;
     if (qlo < qhi) {
-        const int maxpos = clampi(perm_b[qhi - 1], 0, ne - 1) / m;
-        const int minpos = clampi(perm_b[qlo], 0, ne - 1) / m;
-        kend = first_slot_at_or_above(perm_b, ob, qhi, m * (maxpos - w));
-        kfull = first_slot_at_or_above(perm_b, ob, kend, m * (minpos - w));
+        const int maxpos = clampi(perm_b[qhi - 1], 0, ne - 1);
+        const int minpos = clampi(perm_b[qlo], 0, ne - 1);
+        kend = first_slot_at_or_above(perm_b, ob, qhi, maxpos - w);
+        kfull = first_slot_at_or_above(perm_b, ob, kend, minpos - w);
     }
+}
+
+// Entry passes (two groups per token, K >= 5). The key order is the sort
+// of the n*2 membership entries e = t*2 + c by group (position t = e / 2,
+// increasing inside a group's segment); the query rows of a tile are
+// entries of one membership index c, taken in key order, so the rows of
+// one group are consecutive there too. Group g's key slots for the tile's
+// rows of g, at positions minpos .. maxpos: [ob, kend), kend the first slot
+// of the segment at a position >= maxpos - w; kfull: the slots below
+// position minpos - w, kept by every such row (up to the pair rule). An
+// entry is below 2 * bound exactly when its position is below bound.
+__device__ __forceinline__ void entry_segment(const int32_t* perm_b, const int32_t* offb, int ne,
+                                              int w, int g, bool rows, int minpos, int maxpos,
+                                              int& ob, int& kend, int& kfull) {
+    ob = clampi(offb[g], 0, ne);
+    const int oe = clampi(offb[g + 1], ob, ne);
+    kend = ob;
+    kfull = ob;
+    if (rows) {
+        kend = first_slot_at_or_above(perm_b, ob, oe, 2 * (maxpos - w));
+        kfull = first_slot_at_or_above(perm_b, ob, kend, 2 * (minpos - w));
+    }
+}
+
+// Entry passes: the membership index of each key slot (okey[b][s] = the
+// entry's c), to sort the key slots stably by it into the query order.
+__global__ __launch_bounds__(256) void attn_entry_index_kernel(const int32_t* __restrict__ perm,
+                                                               int64_t slots,
+                                                               int32_t* __restrict__ okey) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x < slots) okey[x] = perm[x] & 1;
+}
+
+// Entry passes: the query order's entries, qent[b][u] = perm[b][operm[b][u]]
+// (operm: the key slots stably sorted by membership index).
+__global__ __launch_bounds__(256) void attn_entry_query_kernel(const int32_t* __restrict__ perm,
+                                                               const int32_t* __restrict__ operm,
+                                                               int ne, int64_t slots,
+                                                               int32_t* __restrict__ qent) {
+    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= slots) return;
+    const int64_t b = x / ne;
+    qent[x] = perm[b * ne + clampi(operm[x], 0, ne - 1)];
+}
+
+// Entry passes: one plan record per query tile of each half (tile j of
+// half c holds query slots c*n + j*TT .. c*n + min(n, (j+1)*TT) - 1),
+// shared by every kv head, laid out as attn_plan_kernel's records over
+// [B][2][T] tiles: the groups gf .. gl of the tile's rows, each with its key
+// slots (entry_segment), its first tile index and kfull.
+__global__ __launch_bounds__(256) void attn_entry_plan_kernel(
+    const int32_t* __restrict__ ids, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ qent, int n, int K, int w,
+    int TT, int T, int bn_keys, int32_t* __restrict__ plan) {
+    const int b = blockIdx.y;
+    const int u = blockIdx.x * 256 + threadIdx.x;
+    if (u >= 2 * T) return;
+    const int c = u / T, j = u % T;
+    const int ne = 2 * n;
+    const int64_t bne = (int64_t)b * ne;
+    const int32_t* perm_b = perm + bne;
+    const int32_t* qb = qent + bne;
+    const int32_t* offb = offsets + (int64_t)b * (K + 1);
+    const int s0 = c * n + j * TT, s1 = c * n + min(n, (j + 1) * TT);
+    auto entry = [&](int s) { return clampi(qb[s], 0, ne - 1); };
+    auto group = [&](int e) { return clampi(ids[bne + e], 0, K - 1); };
+    const int gf = group(entry(s0));
+    const int gl = max(gf, group(entry(s1 - 1)));
+    const int nseg = gl - gf + 1;
+    int32_t* rec = plan + ((int64_t)b * 2 * T + u) * PLAN_INTS;
+    int run = 0;
+    int s = s0;   // first row of the current group
+    for (int t = 0; t < nseg; ++t) {
+        const int g = gf + t;
+        int se = s;
+        while (se < s1 && group(entry(se)) == g) ++se;
+        const bool rows = se > s;
+        int ob, kend, kfull;
+        entry_segment(perm_b, offb, ne, w, g, rows, rows ? entry(s) >> 1 : 0,
+                      rows ? entry(se - 1) >> 1 : 0, ob, kend, kfull);
+        if (nseg <= SEGCAP) {
+            rec[4 + 4 * t] = ob;
+            rec[5 + 4 * t] = kend;
+            rec[6 + 4 * t] = run;
+            rec[7 + 4 * t] = kfull;
+        }
+        run += (kend - ob + bn_keys - 1) / bn_keys;
+        s = se;
+    }
+    // more groups than a record holds: the attention kernel derives them
+    rec[0] = nseg <= SEGCAP ? nseg : -1;
+    rec[1] = gf;
+    rec[2] = gf == gl ? 1 : 0;
+    rec[3] = run;
 }
 
 // Long-range pass with one group per token: one record per ordered query
@@ -436,15 +536,15 @@ __global__ __launch_bounds__(256) void attn_set_plan_kernel(
     rec[3] = run;
 }
 
-// Tile plan of the long-range pass, once per (batch, sorted query tile) and
-// shared by every kv head: record = {nseg (-1: more than SEGCAP groups, the
-// attention kernel then derives its segments itself), first group, all query
-// rows in one group, key tiles in total, then per group (ob, kend, first
-// tile index, kfull)}.
+// Tile plan of the long-range pass with one group per token, once per
+// (batch, sorted query tile) and shared by every kv head: record = {nseg
+// (-1: more than SEGCAP groups, the attention kernel then derives its
+// segments itself), first group, all query rows in one group, key tiles in
+// total, then per group (ob, kend, first tile index, kfull)}.
 __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restrict__ ids,
                                                         const int32_t* __restrict__ perm,
                                                         const int32_t* __restrict__ offsets,
-                                                        int ne, int m, int K, int w, int TT,
+                                                        int ne, int K, int w, int TT,
                                                         int ntiles, int bn_keys,
                                                         int32_t* __restrict__ plan) {
     const int b = blockIdx.y;
@@ -454,7 +554,6 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
     const int32_t* perm_b = perm + bne;
     const int32_t* offb = offsets + (int64_t)b * (K + 1);
     const int s0 = tile * TT, s1 = min(ne, s0 + TT);
-    // ids [B][n][m] read flat: entry e of batch b is ids[b * ne + e]
     const int gf = clampi(ids[bne + clampi(perm_b[s0], 0, ne - 1)], 0, K - 1);
     const int gl = clampi(ids[bne + clampi(perm_b[s1 - 1], 0, ne - 1)], gf, K - 1);
     const int nseg = gl - gf + 1;
@@ -465,7 +564,7 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
         int run = 0;
         for (int t = 0; t < nseg; ++t) {
             int ob, kend, kfull;
-            segment_range(perm_b, offb, ne, m, w, s0, s1, gf + t, ob, kend, kfull);
+            segment_range(perm_b, offb, ne, w, s0, s1, gf + t, ob, kend, kfull);
             run += (kend - ob + bn_keys - 1) / bn_keys;
         }
         rec[0] = -1;
@@ -475,7 +574,7 @@ __global__ __launch_bounds__(256) void attn_plan_kernel(const int32_t* __restric
     int run = 0;
     for (int t = 0; t < nseg; ++t) {
         int ob, kend, kfull;
-        segment_range(perm_b, offb, ne, m, w, s0, s1, gf + t, ob, kend, kfull);
+        segment_range(perm_b, offb, ne, w, s0, s1, gf + t, ob, kend, kfull);
         rec[4 + 4 * t] = ob;
         rec[5 + 4 * t] = kend;
         rec[6 + 4 * t] = run;
@@ -560,7 +659,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     constexpr int GROWB = 4 * KG;
     constexpr int GNCH = GROWB / 16;
     constexpr int GNC = BN * GROWB / 1024;
-    // slots of the tiled order (n except in the multi pass)
+    // slots of the sorted key order (n except in the entry passes: n*2)
     const int ne = MULTI ? a.ne : a.n;
     // Two K/V buffers, [K tile | V tile] each. In the sorted passes they are
     // two LDS variables: the compiler then sees that reads of one buffer
@@ -598,6 +697,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     slice = __builtin_amdgcn_readfirstlane(slice);
     kvh = __builtin_amdgcn_readfirstlane(kvh);
     b = __builtin_amdgcn_readfirstlane(b);
+    // plan and order rows of this launch: per batch element, or per (batch
+    // element, half) in the entry passes
+    const int pbi = MULTI ? 2 * b + a.half : b;
     const int R = wave * 32 + rl;
     const int hslot = R >> a.tt_log, tok = R & (a.TT - 1);
     // Packed pass: every load the prologue needs before the first key tile
@@ -619,20 +721,25 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             pos0_pk[i] = rec[64 + 2 * a.TT + ((wave * G::NI + i) * 1024 + 16 * lane) / G::ROWB];
         tile = clampi(__builtin_amdgcn_readlane(prec[0], 8), 0, a.ntiles - 1);
     } else if (SORTED) {
-        tile = clampi(a.order[(int64_t)b * a.ntiles + tile], 0, a.ntiles - 1);
+        tile = clampi(a.order[(int64_t)pbi * a.ntiles + tile], 0, a.ntiles - 1);
     }
     tile = __builtin_amdgcn_readfirstlane(tile);
 
     const int h = kvh * a.hpk + slice * a.G + hslot;
     const int64_t bne = (int64_t)b * ne;
-    const int s_row = tile * a.TT + tok;
-    const bool rvalid = s_row < ne;
+    // the tile's query slots [qs0, qs1) (entry passes: in the half of this
+    // launch's membership index)
+    const int qs0 = (MULTI ? a.half * a.n : 0) + tile * a.TT;
+    const int qs1 = MULTI ? a.half * a.n + min(a.n, (tile + 1) * a.TT) : min(ne, qs0 + a.TT);
+    const int s_row = qs0 + tok;
+    const bool rvalid = s_row < qs1;
     // entry of the row (sorted passes: perm holds entries t*m + c; m = 1
     // makes the entry the position) and its sequence position
     int ent_i = rvalid ? s_row : 0;
     // Sorted passes: every row has an entry (rows past the end take the last
     // slot's, a valid position they never store to).
     if (PACKED) ent_i = clampi(ent_pk, 0, ne - 1);
+    else if (MULTI) ent_i = clampi(a.qperm[bne + min(s_row, qs1 - 1)], 0, ne - 1);
     else if (SORTED) ent_i = clampi(a.perm[bne + min(s_row, ne - 1)], 0, ne - 1);
     // long-range pass: the end of the row's key slots (a partial tile is
     // masked by slot index)
@@ -642,7 +749,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // entry so that the two round trips overlap. Lane l < 8 of every wave
     // holds ints 4l .. 4l+3: lane 0 the header, lane t + 1 segment t.
     if (MULTI || SETS)
-        prec = *reinterpret_cast<const i32x4*>(a.plan + ((int64_t)b * a.ntiles + tile) * PLAN_INTS +
+        prec = *reinterpret_cast<const i32x4*>(a.plan + ((int64_t)pbi * a.ntiles + tile) * PLAN_INTS +
                                               4 * (lane & 7));
     const int pos_i = MULTI ? (ent_i >> 1) : ent_i;
     // multi pass: the row token's other group
@@ -668,8 +775,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         kend0 = qlast + 1;
         ntl = (kend0 - kstart + BN - 1) / BN;
     } else {
-        const int s0 = tile * a.TT;
-        const int s1 = min(ne, s0 + a.TT);
+        const int s0 = qs0, s1 = qs1;
         if (hh == 0) rowpos[R] = ent_i;  // published by the barrier below
         if (MULTI && tid == 0) excl_any = 0;
         // the header is uniform: readlane keeps it in scalar registers
@@ -693,15 +799,32 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             // More groups in this tile than a plan record holds: derive the
             // segments here (every tile of them is treated as partial).
             const int32_t* offb = a.offsets + (int64_t)b * (a.K + 1);
+            const int32_t* qord = MULTI ? a.qperm : a.perm;
             gfirst = __builtin_amdgcn_readfirstlane(
-                clampi(a.ids[bne + clampi(a.perm[bne + s0], 0, ne - 1)], 0, a.K - 1));
+                clampi(a.ids[bne + clampi(qord[bne + s0], 0, ne - 1)], 0, a.K - 1));
             const int glast = __builtin_amdgcn_readfirstlane(
-                clampi(a.ids[bne + clampi(a.perm[bne + s1 - 1], 0, ne - 1)], gfirst, a.K - 1));
+                clampi(a.ids[bne + clampi(qord[bne + s1 - 1], 0, ne - 1)], gfirst, a.K - 1));
             nseg = glast - gfirst + 1;
+            if (MULTI) __syncthreads();   // rowpos: the rows' entries
             if (tid < nseg) {
                 int ob, kend, kfull;
-                segment_range(a.perm + bne, offb, ne, MULTI ? 2 : 1, a.w, s0, s1, gfirst + tid,
-                              ob, kend, kfull);
+                if (MULTI) {
+                    // this group's rows (consecutive) and their position range
+                    const int g = gfirst + tid;
+                    int lo = -1, hi = -1;
+                    for (int r = 0; r < s1 - s0; ++r) {
+                        const int e = rowpos[r];
+                        if (clampi(a.ids[bne + e], 0, a.K - 1) == g) {
+                            if (lo < 0) lo = e >> 1;
+                            hi = e >> 1;
+                        }
+                    }
+                    entry_segment(a.perm + bne, offb, ne, a.w, g, lo >= 0, lo, hi, ob, kend,
+                                  kfull);
+                } else {
+                    segment_range(a.perm + bne, offb, ne, a.w, s0, s1, gfirst + tid, ob, kend,
+                                  kfull);
+                }
                 seg_ob[tid] = ob;
                 seg_kend[tid] = kend;
                 seg_kfull[tid] = ob;
@@ -724,11 +847,17 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         nseg_tile = __builtin_amdgcn_readfirstlane(nseg);
         ntl = __builtin_amdgcn_readfirstlane(
             clampi(seg_t0[nseg], 0, nseg * ((ne + BN - 1) / BN)));
-        // the row's group: segments are consecutive in sorted order
+        // the row's group: its own (entry passes: the entry's group; else
+        // the segment holding its slot, segments being consecutive in sorted
+        // order), within the tile's segments
         if (rvalid) {
-            int t = 0;
-            while (t + 1 < nseg && seg_ob[t + 1] <= s_row) ++t;
-            g_i = gfirst + t;
+            if (MULTI) {
+                g_i = clampi(a.ids[bne + ent_i], gfirst, gfirst + nseg - 1);
+            } else {
+                int t = 0;
+                while (t + 1 < nseg && seg_ob[t + 1] <= s_row) ++t;
+                g_i = gfirst + t;
+            }
         }
         if (MULTI) {
             // A pair of tokens sharing both their groups meets in both
@@ -1301,7 +1430,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // kind has its own straight-line path (sizes known at compile time).
     const float l_tot = l_run + other_half(l_run);
     const float l_pv_tot = l_pv + other_half(l_pv);
-    const int64_t row = ((int64_t)b * a.Hq + h) * ne + ent_i;   // output row
+    const int64_t row = ((int64_t)b * a.Hq + h) * a.n + pos_i;   // output row
     const float inv_l = l_pv_tot > 0.0f ? __builtin_amdgcn_rcpf(l_pv_tot) : 0.0f;
     // kind 0: fp16 partial O * 2^-e; 1: bf16 output; 2: fp32 output
     auto epilogue = [&](auto kind_tag) {
@@ -1327,7 +1456,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             scale_o = __builtin_ldexpf(scale_o, -ex);
             if (rvalid && hh == 0) {
                 const f32x2 le = {l_tot > 0.0f ? m_ref + __log2f(l_tot) : kNegInf, (float)ex};
-                a.lseg[row] = le;
+                a.lseg_dst[row] = le;
             }
         } else {
             if (rvalid && hh == 0 && a.lse) a.lse[row] = (m_ref + __log2f(l_tot)) * kLn2;
@@ -1335,7 +1464,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         auto stage = [&](int rs) -> unsigned char* {
             return rs < HROWS ? buf0 + rs * RB : buf1 + (rs - HROWS) * RB;
         };
-        char* dst = KIND == 0 ? reinterpret_cast<char*>(a.og) : static_cast<char*>(a.out);
+        char* dst = KIND == 0 ? reinterpret_cast<char*>(a.og_dst) : static_cast<char*>(a.out);
 #pragma unroll
         for (int r0 = 0; r0 < ROWS; r0 += RPP) {
             // K/V buffers (or the previous pass) are free
@@ -1375,85 +1504,26 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 const int rs = idx / NCHK, c = idx % NCHK;
                 const int r = r0 + rs;
                 const int tk = r & (a.TT - 1);
-                if (tile * a.TT + tk >= ne) continue;   // rows past the sequence end
+                if (qs0 + tk >= qs1) continue;   // rows past the sequence end
                 int hr, pr;
                 row_of(r, hr, pr);
                 u32x4 val = *reinterpret_cast<const u32x4*>(stage(rs) + ((c ^ (rs & CMASK)) << 4));
                 if (ESZ == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
-                *reinterpret_cast<u32x4*>(dst + ((((int64_t)b * a.Hq + hr) * ne + pr) * RB) +
-                                          c * 16) = val;
+                // the row's token (entry passes: entry / 2)
+                const int64_t orow = ((int64_t)b * a.Hq + hr) * a.n + (MULTI ? pr >> 1 : pr);
+                *reinterpret_cast<u32x4*>(dst + orow * RB + c * 16) = val;
             }
         }
     };
-    // partials: the window pass ahead of a long-range pass, the multi pass
-    if (MULTI || (PHASE == kWindow && a.partial)) {
+    // partials: the window pass ahead of a long-range pass, the first entry
+    // pass
+    if ((MULTI || PHASE == kWindow) && a.partial) {
         epilogue(std::integral_constant<int, 0>{});
     } else if (a.out_f32) {
         epilogue(std::integral_constant<int, 2>{});
     } else {
         epilogue(std::integral_constant<int, 1>{});
     }
-}
-
-// Final merge of the multi pass: per row (b, h, i), the window partial and
-// the row's m entry partials (each O~ = O * 2^-e in fp16 with (L, e), L the
-// log2-sum-exp of its keys, -inf for none) are combined by log-sum-exp:
-// out = sum_c 2^(L_c - L) O_c, L = log2 sum_c 2^(L_c). The parts cover
-// disjoint key sets whose union is the row's pattern, so this is exact.
-// D/8 threads per row, one 8-element chunk each.
-template <int D, int MM>
-__global__ __launch_bounds__(256) void attn_merge_entries_kernel(
-    const _Float16* __restrict__ og, const f32x2* __restrict__ lseg,
-    const _Float16* __restrict__ oge, const f32x2* __restrict__ lsege, int64_t rows, int n,
-    void* __restrict__ out, int out_f32, float* __restrict__ lse) {
-    constexpr int TPR = D / 8;
-    const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t row = x / TPR;
-    const int c = (int)(x % TPR);
-    if (row >= rows) return;
-    const int64_t bh = row / n;
-    const int pos = (int)(row % n);
-    f32x2 le[MM + 1];
-    const _Float16* src[MM + 1];
-    le[0] = lseg[row];
-    src[0] = og + row * D + c * 8;
-#pragma unroll
-    for (int e = 0; e < MM; ++e) {
-        const int64_t er = (bh * n + pos) * MM + e;   // entry row: [b][h][t * MM + e]
-        le[e + 1] = lsege[er];
-        src[e + 1] = oge + er * D + c * 8;
-    }
-    float lmax = kNegInf;
-#pragma unroll
-    for (int p = 0; p <= MM; ++p) lmax = fmaxf(lmax, le[p][0]);
-    float o[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float tot = 0.0f;
-    if (lmax != kNegInf) {
-#pragma unroll
-        for (int p = 0; p <= MM; ++p) {
-            if (le[p][0] == kNegInf) continue;
-            const float wgt = __builtin_amdgcn_exp2f(le[p][0] - lmax);
-            tot += wgt;
-            const float f = __builtin_ldexpf(wgt, (int)le[p][1]);
-            const f16x8 hv = *reinterpret_cast<const f16x8*>(src[p]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = __builtin_fmaf(f, (float)hv[j], o[j]);
-        }
-    }
-    const float inv = tot > 0.0f ? 1.0f / tot : 0.0f;
-    if (out_f32) {
-        float* dst = static_cast<float*>(out) + row * D + c * 8;
-        const f32x4 a0 = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
-        const f32x4 a1 = {o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
-        *reinterpret_cast<f32x4*>(dst) = a0;
-        *reinterpret_cast<f32x4*>(dst + 4) = a1;
-    } else {
-        bf16x8 ob;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ob[j] = (__bf16)(o[j] * inv);
-        *reinterpret_cast<bf16x8*>(static_cast<uint16_t*>(out) + row * D + c * 8) = ob;
-    }
-    if (c == 0 && lse) lse[row] = tot > 0.0f ? (lmax + __log2f(tot)) * kLn2 : kNegInf;
 }
 
 // Soft-gated pass operand: gs[t][0][k] = bf16(G[t][k]) (round to nearest
@@ -1504,6 +1574,8 @@ AttnArgs make_args(const AttnProblem& p) {
         char* base = static_cast<char*>(p.workspace);
         a.og = reinterpret_cast<_Float16*>(base + ws.og);
         a.lseg = reinterpret_cast<f32x2*>(base + ws.lseg);
+        a.og_dst = a.og;
+        a.lseg_dst = a.lseg;
         a.plan = reinterpret_cast<const int32_t*>(base + ws.plan);
         a.order = reinterpret_cast<const int32_t*>(base + ws.order);
         a.spos = reinterpret_cast<int32_t*>(base + ws.spos);
@@ -1525,23 +1597,24 @@ hipError_t launch(const AttnArgs& a, int d, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// Long-range pass arguments: the sorted order lists n*m entries. K and V
-// rows are read in place at the positions perm gives, or from group-sorted
+// Long-range pass arguments: the sorted key order lists n*m entries. K and
+// V rows are read in place at the positions perm gives, or from sorted
 // copies made by the prepare call (attn_sorted_copies: two groups per token,
 // a head's rows beyond a buffer resource's 2^31-byte reach, or asked for).
-// The choice depends only on the problem, so prepare and apply agree.
+// The choice depends only on the problem, so prepare and apply agree. With
+// two groups per token each of the two entry passes takes ceil(n / TT)
+// query tiles of its half of the query order.
 AttnArgs long_range_args(const AttnProblem& p) {
     AttnArgs a = make_args(p);
     a.ne = p.n * p.m;
-    a.ntiles = (a.ne + a.TT - 1) / a.TT;
-    a.total = p.B * p.Hkv * a.nslices * a.ntiles;
     a.direct = attn_sorted_copies(p.n, p.d, p.m, p.K, p.force_copies != 0) ? 0 : 1;
+    const AttnWorkspace ws = attn_workspace_layout(p);
+    char* base = static_cast<char*>(p.workspace);
     if (!a.direct) {
-        const AttnWorkspace ws = attn_workspace_layout(p);
-        char* base = static_cast<char*>(p.workspace);
         a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
         a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
     }
+    if (p.m == 2) a.qperm = reinterpret_cast<const int32_t*>(base + ws.qent);
     return a;
 }
 
@@ -1571,8 +1644,8 @@ AttnArgs set_pass_args(const AttnProblem& p) {
     AttnArgs a = make_args(p);
     const AttnWorkspace ws = attn_workspace_layout(p);
     char* base = static_cast<char*>(p.workspace);
-    a.perm = reinterpret_cast<const int32_t*>(base + ws.sperm);
-    a.offsets = reinterpret_cast<const int32_t*>(base + ws.soffs);
+    a.perm = reinterpret_cast<const int32_t*>(base + ws.operm);
+    a.offsets = reinterpret_cast<const int32_t*>(base + ws.ooffs);
     a.k = reinterpret_cast<const uint16_t*>(base + ws.ks);
     a.v = reinterpret_cast<const uint16_t*>(base + ws.vs);
     a.direct = 0;
@@ -1584,7 +1657,7 @@ hipError_t launch_attn_set_prepare(const AttnProblem& p, hipStream_t stream) {
     const AttnArgs a = set_pass_args(p);
     const AttnWorkspace ws = attn_workspace_layout(p);
     char* base = static_cast<char*>(p.workspace);
-    int32_t* sid = reinterpret_cast<int32_t*>(base + ws.sid);
+    int32_t* sid = reinterpret_cast<int32_t*>(base + ws.okey);
     const int S = attn_membership_sets(p.K);
     const int64_t ntok = (int64_t)p.B * p.n;
     hipLaunchKernelGGL(attn_set_id_kernel, dim3((unsigned)((ntok + 255) / 256)), dim3(256), 0,
@@ -1592,7 +1665,7 @@ hipError_t launch_attn_set_prepare(const AttnProblem& p, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = launch_group_sort(sid, p.B, p.n, S, const_cast<int32_t*>(a.perm),
-                          const_cast<int32_t*>(a.offsets), base + ws.shist, stream);
+                          const_cast<int32_t*>(a.offsets), base + ws.ohist, stream);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_set_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0,
                        stream, a.perm, a.offsets, p.ids, p.n, p.K, S, p.w, a.TT, a.ntiles,
@@ -1616,6 +1689,41 @@ hipError_t launch_attn_set_prepare(const AttnProblem& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Entry passes (two groups per token, K >= 5): the query order (the key
+// slots stably sorted by membership index: first-group entries, then
+// second-group entries, each half in key order), its plan over [B][2][T]
+// tiles and the LPT order of each half.
+hipError_t launch_attn_entry_prepare(const AttnProblem& p, const AttnArgs& a,
+                                     hipStream_t stream) {
+    const AttnWorkspace ws = attn_workspace_layout(p);
+    char* base = static_cast<char*>(p.workspace);
+    int32_t* okey = reinterpret_cast<int32_t*>(base + ws.okey);
+    int32_t* operm = reinterpret_cast<int32_t*>(base + ws.operm);
+    int32_t* ooffs = reinterpret_cast<int32_t*>(base + ws.ooffs);
+    int32_t* qent = const_cast<int32_t*>(a.qperm);
+    const int64_t slots = (int64_t)p.B * a.ne;
+    const dim3 sgrid((unsigned)((slots + 255) / 256));
+    hipLaunchKernelGGL(attn_entry_index_kernel, sgrid, dim3(256), 0, stream, p.perm, slots, okey);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_group_sort(okey, p.B, a.ne, 2, operm, ooffs, base + ws.ohist, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attn_entry_query_kernel, sgrid, dim3(256), 0, stream, p.perm, operm, a.ne,
+                       slots, qent);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int T = a.ntiles;
+    hipLaunchKernelGGL(attn_entry_plan_kernel, dim3((2 * T + 255) / 256, p.B), dim3(256), 0, stream,
+                       p.ids, p.perm, p.offsets, qent, p.n, p.K, p.w, a.TT, T,
+                       attn_tile_keys(p.d, kLongMulti), const_cast<int32_t*>(a.plan));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // one order row per (batch element, half)
+    hipLaunchKernelGGL(attn_order_kernel, dim3(2 * p.B), dim3(256), 0, stream, a.plan, T,
+                       const_cast<int32_t*>(a.order));
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stream) {
     if (!attn_has_long_range(p.n, p.w)) return hipSuccess;
     if (p.m != 1 && p.m != 2) return hipErrorInvalidValue;
@@ -1631,24 +1739,21 @@ hipError_t launch_attn_long_range_prepare(const AttnProblem& p, hipStream_t stre
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    if (p.m == 2) return launch_attn_entry_prepare(p, a, stream);
     hipLaunchKernelGGL(attn_plan_kernel, dim3((a.ntiles + 255) / 256, p.B), dim3(256), 0, stream,
-                       p.ids, p.perm, p.offsets, a.ne, p.m, p.K, p.w, a.TT, a.ntiles,
-                       attn_tile_keys(p.d, kLongRange),
-                       const_cast<int32_t*>(a.plan));
+                       p.ids, p.perm, p.offsets, a.ne, p.K, p.w, a.TT, a.ntiles,
+                       attn_tile_keys(p.d, kLongRange), const_cast<int32_t*>(a.plan));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_order_kernel, dim3(p.B), dim3(256), 0, stream, a.plan, a.ntiles,
                        const_cast<int32_t*>(a.order));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.m == 1) {
-        hipLaunchKernelGGL(attn_pack_kernel, dim3(a.ntiles, p.B), dim3(256), 0, stream, a.plan,
-                           a.order, p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT,
-                           attn_long_range_tile_keys(p.d), a.ntiles, a.pack_ints,
-                           const_cast<int32_t*>(a.pack));
-        e = hipGetLastError();
-    }
-    return e;
+    hipLaunchKernelGGL(attn_pack_kernel, dim3(a.ntiles, p.B), dim3(256), 0, stream, a.plan,
+                       a.order, p.ids, p.perm, p.offsets, p.n, p.K, p.w, a.TT,
+                       attn_long_range_tile_keys(p.d), a.ntiles, a.pack_ints,
+                       const_cast<int32_t*>(a.pack));
+    return hipGetLastError();
 }
 
 hipError_t launch_attn_long_range_apply(const AttnProblem& p, hipStream_t stream) {
@@ -1662,43 +1767,31 @@ hipError_t launch_attn_long_range_apply(const AttnProblem& p, hipStream_t stream
         return launch<kLongSets>(a, p.d, stream);
     }
     AttnArgs a = long_range_args(p);
+    a.merge = 1;     // start from the window partial
     if (p.m == 1) {
-        a.merge = 1;     // start from the window partial, write the final output
-        a.partial = 0;
+        a.partial = 0;   // write the final output
         return launch<kLongRange>(a, p.d, stream);
     }
-    // Two groups per token: one partial per entry, then the merge.
+    // Two groups per token: the first-group entries merge their keys into
+    // the window partial and write the result as a second partial, then the
+    // second-group entries merge theirs into that and write the final
+    // output. A pair of tokens sharing both groups is kept only where the
+    // query row's group is the lower of the two.
     const AttnWorkspace ws = attn_workspace_layout(p);
     char* base = static_cast<char*>(p.workspace);
-    _Float16* oge = reinterpret_cast<_Float16*>(base + ws.oge);
-    f32x2* lsege = reinterpret_cast<f32x2*>(base + ws.lsege);
-    const _Float16* og = a.og;
-    const f32x2* lseg = a.lseg;
-    a.og = oge;
-    a.lseg = lsege;
-    a.merge = 0;
+    _Float16* og1 = reinterpret_cast<_Float16*>(base + ws.og1);
+    f32x2* lseg1 = reinterpret_cast<f32x2*>(base + ws.lseg1);
+    a.half = 0;
     a.partial = 1;
+    a.og_dst = og1;
+    a.lseg_dst = lseg1;
     hipError_t e = launch<kLongMulti>(a, p.d, stream);
     if (e != hipSuccess) return e;
-    const int64_t rows = (int64_t)p.B * p.Hq * p.n;
-    const int64_t threads = rows * (p.d / 8);
-    const dim3 grid((unsigned)((threads + 255) / 256));
-    switch (p.d) {
-        case 32:
-            hipLaunchKernelGGL((attn_merge_entries_kernel<32, 2>), grid, dim3(256), 0, stream, og,
-                               lseg, oge, lsege, rows, p.n, p.out, p.out_f32, p.lse);
-            break;
-        case 64:
-            hipLaunchKernelGGL((attn_merge_entries_kernel<64, 2>), grid, dim3(256), 0, stream, og,
-                               lseg, oge, lsege, rows, p.n, p.out, p.out_f32, p.lse);
-            break;
-        case 128:
-            hipLaunchKernelGGL((attn_merge_entries_kernel<128, 2>), grid, dim3(256), 0, stream, og,
-                               lseg, oge, lsege, rows, p.n, p.out, p.out_f32, p.lse);
-            break;
-        default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    a.half = 1;
+    a.partial = 0;
+    a.og = og1;
+    a.lseg = lseg1;
+    return launch<kLongMulti>(a, p.d, stream);
 }
 
 hipError_t launch_attn_long_range(const AttnProblem& p, hipStream_t stream) {

@@ -100,25 +100,42 @@ inline bool attn_sorted_copies(int n, int d, int m, int K, bool force) {
     return force || m > 1 || (int64_t)n * d * 2 >= ((int64_t)1 << 31);
 }
 
+// Query tiles of the long-range pass. One group per token, and the set
+// pass: ceil(n / TT) tiles over the sorted tokens. Two groups per token
+// otherwise (the entry passes): ceil(n / TT) tiles over each half of the
+// query order (first-group entries, then second-group entries).
+inline int attn_long_range_tiles(int n, int TT, int m, bool sets) {
+    const int t = (n + TT - 1) / TT;
+    return (m == 2 && !sets) ? 2 * t : t;
+}
+
 // Attention workspace, byte offsets: the window partial output (fp16
 // [B][Hq][n][d], scaled per row), its log2-sum-exp and scale exponent (fp32
 // pairs [B][Hq][n]), the tile plan, the order in which the long-range pass
 // takes the sorted query tiles (int32 [B][tiles], most work first) and, with
 // one group per token, one packed record per ordered tile (int32
 // [B][tiles][attn_pack_ints]: plan record, tile index, each row's entry and
-// key-slot end, the first key tile's positions). With sorted copies (attn_sorted_copies) also the group-sorted K
-// and V (bf16 [B][Hkv][n*m][d]) and the sorted slots' positions (int32
-// [B][n*m + pad]). With m groups per token (m > 1) the sorted order lists
-// n*m membership entries, and the long-range pass writes one partial per
-// entry (fp16 [B][Hq][n*m][d] and pairs [B][Hq][n*m]) for a final merge;
-// except on the set pass (attn_uses_sets), whose sorted order lists the n
-// tokens by membership set: then the set id per token, the set-sorted
-// positions and set offsets, the sort's per-block counts and the sorted
-// slots' (position, group mask) words, and no copies or per-entry partials.
+// key-slot end, the first key tile's positions). With sorted copies
+// (attn_sorted_copies) also the sorted K and V (bf16 [B][Hkv][slots][d])
+// and the sorted slots' positions or (position, group) words (int32
+// [B][slots + pad]). Two groups per token:
+//  - the set pass (attn_uses_sets) sorts the n tokens by membership set:
+//    the set id per token (okey), the set-sorted positions (operm), set
+//    offsets (ooffs), the sort's per-block counts (ohist);
+//  - the entry passes key on the caller's sort of the n*2 membership
+//    entries by group and take their query rows in a second order, the
+//    first-group entries then the second-group entries, each half in key
+//    order: the stable sort by membership index of the key order (okey:
+//    index per key slot, operm: the sorted key slots, ooffs, ohist), the
+//    query order's entries (qent, int32 [B][2n]) and the first entry pass's
+//    partial (og1, lseg1: laid out as og, lseg), from which the second pass
+//    starts; the window partial is only read, so apply can be repeated on
+//    it, and there is no partial per entry.
 // The first two regions lead every layout, so the window pass, which uses
 // only them, takes the same offsets for every m.
 struct AttnWorkspace {
-    size_t og, lseg, plan, order, pack, ks, vs, spos, oge, lsege, sid, sperm, soffs, shist, total;
+    size_t og, lseg, plan, order, pack, ks, vs, spos, okey, operm, ooffs, ohist, qent, og1, lseg1,
+        total;
 };
 inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d, int m, int K,
                                            bool force_copies) {
@@ -127,8 +144,9 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d,
     const bool copies = attn_sorted_copies(n, d, m, K, force_copies);
     const int S = attn_membership_sets(K);
     const int TT = attn_tokens_per_tile(Hq, Hkv);
+    const bool entries = m == 2 && !sets;
     const size_t ne = sets ? (size_t)n : (size_t)n * m;
-    const size_t ntiles = (ne + TT - 1) / TT;
+    const size_t ntiles = attn_long_range_tiles(n, TT, m, sets);
     size_t off = 0;
     w.og = off;   off += align_up((size_t)B * Hq * n * d * 2);
     w.lseg = off; off += align_up((size_t)B * Hq * n * 8);
@@ -140,12 +158,16 @@ inline AttnWorkspace attn_workspace_layout(int B, int Hq, int Hkv, int n, int d,
     w.ks = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
     w.vs = off;   off += copies ? align_up((size_t)B * Hkv * ne * d * 2) : 0;
     w.spos = off; off += (copies || sets) ? align_up((size_t)B * (ne + KPOS_PAD) * 4) : 0;
-    w.oge = off;  off += (m > 1 && !sets) ? align_up((size_t)B * Hq * ne * d * 2) : 0;
-    w.lsege = off; off += (m > 1 && !sets) ? align_up((size_t)B * Hq * ne * 8) : 0;
-    w.sid = off;  off += sets ? align_up((size_t)B * n * 4) : 0;
-    w.sperm = off; off += sets ? align_up((size_t)B * n * 4) : 0;
-    w.soffs = off; off += sets ? align_up((size_t)B * (S + 1) * 4) : 0;
-    w.shist = off; off += sets ? align_up(group_sort_workspace(B, n, S)) : 0;
+    // the order sort: S sets over n tokens, or 2 halves over 2n key slots
+    const bool osort = sets || entries;
+    const int okeys = sets ? S : 2;
+    w.okey = off;  off += osort ? align_up((size_t)B * ne * 4) : 0;
+    w.operm = off; off += osort ? align_up((size_t)B * ne * 4) : 0;
+    w.ooffs = off; off += osort ? align_up((size_t)B * (okeys + 1) * 4) : 0;
+    w.ohist = off; off += osort ? align_up(group_sort_workspace(B, (int)ne, okeys)) : 0;
+    w.qent = off;  off += entries ? align_up((size_t)B * ne * 4) : 0;
+    w.og1 = off;   off += entries ? align_up((size_t)B * Hq * n * d * 2) : 0;
+    w.lseg1 = off; off += entries ? align_up((size_t)B * Hq * n * 8) : 0;
     w.total = off;
     return w;
 }

@@ -110,12 +110,12 @@ def window_computed_pairs(n: int, w: int, TT: int, BN: int) -> int:
 
 
 def long_range_computed_pairs(ids: np.ndarray, perm: np.ndarray, offsets: np.ndarray, w: int,
-                              TT: int, BN: int, m: int = 1) -> int:
-    """Per query head, summed over the batch: for each tile of TT sorted
-    slots and each group g among them, the key tiles of g's segment below
-    the first slot whose position is >= (largest query position of g in the
-    tile) - w, times TT rows. ids is [B][n*m] flat, perm [B][n*m] entries
-    (position = entry // m), offsets [B][K+1]."""
+                              TT: int, BN: int) -> int:
+    """One group per token. Per query head, summed over the batch: for each
+    tile of TT sorted tokens and each group g among them, the key tiles of
+    g's segment below the first slot whose position is >= (largest query
+    position of g in the tile) - w, times TT rows. ids [B][n], perm [B][n]
+    positions, offsets [B][K+1]."""
     B, ne = perm.shape
     total = 0
     for b in range(B):
@@ -128,9 +128,38 @@ def long_range_computed_pairs(ids: np.ndarray, perm: np.ndarray, offsets: np.nda
                 qlo, qhi = max(s0, ob), min(s1, oe)
                 if qlo >= qhi:
                     continue
-                maxpos = int(pb[qhi - 1]) // m
-                kend = ob + int(np.searchsorted(pb[ob:qhi], m * (maxpos - w), side="left"))
+                maxpos = int(pb[qhi - 1])
+                kend = ob + int(np.searchsorted(pb[ob:qhi], maxpos - w, side="left"))
                 total += (kend - ob + BN - 1) // BN
+    return total * BN * TT
+
+
+def entry_long_range_computed_pairs(ids: np.ndarray, perm: np.ndarray, offsets: np.ndarray,
+                                    w: int, TT: int, BN: int) -> int:
+    """Two groups per token, the entry passes (K >= 5). Keys: the n*2
+    membership entries e = t*2 + c sorted by group (perm [B][2n], offsets
+    [B][K+1]; ids [B][2n] flat). Queries: for c = 0, 1 the entries of
+    membership index c in key order, cut into tiles of TT; for each tile and
+    each group g among its rows, the key tiles of g's segment below the first
+    slot whose position is >= (largest position of the tile's rows of g) - w.
+    Per query head, summed over the batch, times TT rows."""
+    B, ne = perm.shape
+    total = 0
+    for b in range(B):
+        pb, ob_, ib = perm[b].astype(np.int64), offsets[b].astype(np.int64), ids[b]
+        for c in (0, 1):
+            q = pb[(pb & 1) == c]
+            for s0 in range(0, len(q), TT):
+                rows = q[s0:s0 + TT]
+                grp = ib[rows]
+                for g in range(int(grp[0]), int(grp[-1]) + 1):
+                    mine = rows[grp == g]
+                    if len(mine) == 0:
+                        continue
+                    ob, oe = int(ob_[g]), int(ob_[g + 1])
+                    bound = 2 * (int(mine[-1]) // 2 - w)
+                    kend = ob + int(np.searchsorted(pb[ob:oe], bound, side="left"))
+                    total += (kend - ob + BN - 1) // BN
     return total * BN * TT
 
 

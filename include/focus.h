@@ -313,11 +313,13 @@ focus_status focus_attn_long_range_apply(const uint16_t* q, const uint16_t* k, c
  *     tile of set S visits the key segments of every set sharing a group
  *     with S, so each kept pair meets exactly once, and the pass merges the
  *     window partial and writes out and lse itself.
- *   - otherwise (membership entries): a pair sharing two groups meets in
- *     both groups' segments and is kept in the segment of the lower group
- *     only; the pass visits every group segment of both tokens, writes one
- *     partial result per membership entry, and a final kernel merges the
- *     window partial and the m entry partials by log-sum-exp.
+ *   - otherwise (membership entries, m = 2): keys are the n*2 entries in
+ *     the caller's group order; the query rows are taken in two passes, the
+ *     tokens' first-group entries then their second-group entries (each in
+ *     group order). The first pass merges its keys into the window partial
+ *     in place, the second merges its keys into that and writes out and
+ *     lse. A pair sharing two groups meets in both groups' segments and is
+ *     kept only where the query row's group is the lower of the two.
  *
  * group_ids [B][n][m] (distinct groups per token, as from focus_assign_topk),
  * perm [B][n*m] and group_offsets [B][K+1] from focus_group_sort over the
@@ -349,10 +351,10 @@ focus_status focus_attn_topk_long_range_merge(const uint16_t* q, const uint16_t*
                                               void* workspace, size_t workspace_bytes,
                                               focus_stream_t stream);
 /* focus_attn_topk_long_range_merge in two calls, as for m = 1 above:
- * prepare (sorted K/V over the n*m entries, or over the tokens in
- * membership-set order when K <= 4, plan and order; may run beside the window
- * pass) then apply (the per-entry partials and the final merge, or the set
- * pass with its merge). */
+ * prepare (sorted K/V over the n*m entries and the query order of the two
+ * entry passes, or over the tokens in membership-set order when K <= 4; plan
+ * and order; may run beside the window pass) then apply (the two entry
+ * passes, or the set pass; either merges the window partial itself). */
 focus_status focus_attn_topk_long_range_prepare(const uint16_t* q, const uint16_t* k,
                                                 const uint16_t* v, const int32_t* group_ids,
                                                 const int32_t* perm,

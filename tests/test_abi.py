@@ -139,12 +139,15 @@ def test_workspace_sizes():
     # top-k, m = 1: the same layout
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 4, 1, 32) == \
         lib.focus_attn_workspace_bytes(1, 2, 1, 256, 32, 4, 32)
-    # m = 2, K = 5 (membership entries): plan over 512 entries (8 tiles), tile order, sorted K, V
-    # and positions over 512 entries, then per-entry fp16 partials [B][Hq][512][d] and their
-    # pairs [B][Hq][512] (no row ends: the two-group pass masks by key position)
+    # m = 2, K = 5 (the entry passes): plan and order over the two halves of the query order
+    # (4 tiles of 64 entries each), sorted K and V and the slots' (position, other group) words
+    # over the 512 membership entries, then the query-order sort (membership index per key
+    # slot, the sorted slots, 3 offsets, the sort's per-block counts), the query order's
+    # entries and the first pass's partial (fp16 [B][Hq][n][d] and its pairs [B][Hq][n]); no
+    # partial per entry
     assert lib.focus_attn_topk_workspace_bytes(1, 2, 1, 256, 32, 5, 2, 32) == (
         256 * 2 * 32 * 2 + 4096 + 8 * 128 + 256 + 2 * (512 * 32 * 2) + 768 * 4
-        + 512 * 2 * 32 * 2 + 512 * 2 * 8)
+        + 512 * 4 + 512 * 4 + 256 + 256 + 512 * 4 + 256 * 2 * 32 * 2 + 4096)
     # m = 2, K = 4 (six membership sets, the set pass): plan and order over the 256 tokens
     # (4 tiles), set-sorted K and V [B][Hkv][n][d], the slots' (position, group mask) words
     # [B][n + 256], then the set id per token, the set-sorted positions, the 7 set offsets and
@@ -256,7 +259,7 @@ def _attn_topk(fn="focus_attn_topk_fwd", m=2, **kw):
     (2, dict(d=48), UNSUPPORTED, "d_head"),
     (2, dict(scale=0.0), INVALID, "scale"),
     (2, dict(ws=None), WORKSPACE, "workspace"),
-    # enough for m = 1 but not for the per-entry partials of m = 2 (K = 5: membership entries)
+    # enough for m = 1 but not for the sorted K/V of m = 2 (K = 5: the entry passes)
     (2, dict(wsb=400000, K=5), WORKSPACE, "too small"),
     # K = 4 (the set pass): one byte short of its own size
     (2, dict(wsb=275711), WORKSPACE, "too small"),

@@ -14,7 +14,7 @@ def brute_window(n, w, TT, BN):
     return total * BN * TT
 
 
-def brute_long_range(ids_flat, perm, offsets, w, TT, BN, m):
+def brute_long_range(ids_flat, perm, offsets, w, TT, BN):
     """Per sorted tile and group present: count the segment's slots whose
     position is below (largest query position of the group in the tile) - w
     by scanning them one by one."""
@@ -29,14 +29,41 @@ def brute_long_range(ids_flat, perm, offsets, w, TT, BN, m):
                 mine = [s for s in rows if ob <= s < oe]
                 if not mine:
                     continue
-                maxpos = max(int(perm[b][s]) // m for s in mine)
+                maxpos = max(int(perm[b][s]) for s in mine)
                 keys = 0
                 for s in range(ob, max(mine) + 1):
-                    if int(perm[b][s]) // m < maxpos - w:
+                    if int(perm[b][s]) < maxpos - w:
                         keys += 1
                     else:
                         break
                 total += -(-keys // BN)
+    return total * BN * TT
+
+
+def brute_entry_long_range(ids, w, TT, BN):
+    """The entry passes' key tiles by direct enumeration, ids [B][n][2]: for
+    membership index c, the tokens ordered by (their c-th group, position)
+    are cut into tiles of TT; for each tile and each group g of its tokens,
+    count the tokens having g as either group (in position order) whose
+    position is below (largest position of the tile's tokens of g) - w, one by
+    one."""
+    total = 0
+    B, n, _ = ids.shape
+    for b in range(B):
+        for c in (0, 1):
+            order = sorted(range(n), key=lambda t: (int(ids[b, t, c]), t))
+            for s0 in range(0, n, TT):
+                rows = order[s0:s0 + TT]
+                for g in sorted({int(ids[b, t, c]) for t in rows}):
+                    maxpos = max(t for t in rows if ids[b, t, c] == g)
+                    keys = 0
+                    for t in range(n):
+                        if g in (int(ids[b, t, 0]), int(ids[b, t, 1])):
+                            if t < maxpos - w:
+                                keys += 1
+                            else:
+                                break
+                    total += -(-keys // BN)
     return total * BN * TT
 
 
@@ -59,26 +86,31 @@ def test_window_matches_enumeration(n, w, TT, BN):
     assert got >= metrics.window_pairs(n, w)
 
 
-@pytest.mark.parametrize("seed,B,n,K,w,TT,m", [(1, 1, 200, 4, 10, 16, 1), (2, 2, 333, 8, 30, 16, 1),
-                                                (3, 1, 256, 3, 0, 32, 1), (4, 1, 180, 6, 20, 16, 2),
-                                                (5, 1, 97, 64, 5, 16, 1)])
-def test_long_range_matches_enumeration(seed, B, n, K, w, TT, m):
+@pytest.mark.parametrize("seed,B,n,K,w,TT", [(1, 1, 200, 4, 10, 16), (2, 2, 333, 8, 30, 16),
+                                              (3, 1, 256, 3, 0, 32), (5, 1, 97, 64, 5, 16)])
+def test_long_range_matches_enumeration(seed, B, n, K, w, TT):
     rng = np.random.default_rng(seed)
-    if m == 1:
-        ids = rng.integers(0, K, (B, n)).astype(np.int32)
-        flat = ids
-    else:
-        ids = np.stack([np.stack([rng.choice(K, 2, replace=False) for _ in range(n)])
-                        for _ in range(B)]).astype(np.int32)
-        flat = ids.reshape(B, n * m)
-    perm, offs = sort_entries(flat, K)
+    ids = rng.integers(0, K, (B, n)).astype(np.int32)
+    perm, offs = sort_entries(ids, K)
     BN = 32
-    got = metrics.long_range_computed_pairs(flat, perm, offs, w, TT, BN, m)
-    assert got == brute_long_range(flat, perm, offs, w, TT, BN, m)
-    if m == 1:
-        assert got >= metrics.pair_counts(ids, w)[1]
-    else:
-        assert got >= metrics.pair_counts_multi(ids, w)[2]
+    got = metrics.long_range_computed_pairs(ids, perm, offs, w, TT, BN)
+    assert got == brute_long_range(ids, perm, offs, w, TT, BN)
+    assert got >= metrics.pair_counts(ids, w)[1]
+
+
+@pytest.mark.parametrize("seed,B,n,K,w,TT,BN", [(4, 1, 180, 6, 20, 16, 32), (6, 2, 300, 5, 0, 16, 32),
+                                                 (7, 1, 257, 32, 12, 64, 64),
+                                                 (8, 1, 130, 9, 3, 32, 32)])
+def test_entry_long_range_matches_enumeration(seed, B, n, K, w, TT, BN):
+    rng = np.random.default_rng(seed)
+    ids = np.stack([np.stack([rng.choice(K, 2, replace=False) for _ in range(n)])
+                    for _ in range(B)]).astype(np.int32)
+    flat = ids.reshape(B, 2 * n)
+    perm, offs = sort_entries(flat, K)
+    got = metrics.entry_long_range_computed_pairs(flat, perm, offs, w, TT, BN)
+    assert got == brute_entry_long_range(ids, w, TT, BN)
+    # every far pair inside a group's segment is computed
+    assert got >= metrics.pair_counts_multi(ids, w)[2]
 
 
 def test_long_range_empty_when_window_covers_all():
