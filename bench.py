@@ -10,6 +10,13 @@ focus_attn_window (the window pass, which needs no group data) enqueued on a
 second stream right after focus_assign, so that both run together; then,
 once both are done, focus_attn_long_range_apply on the main stream (together the calls are
 focus_attn_fwd). --no-overlap runs all five calls in order on one stream.
+The window pass either starts at once beside the assignment (schedule
+"beside") or waits for the assignment to finish and then runs beside the sort
+and prepare calls (schedule "after_assign"): where the assignment is short
+next to the window pass, sharing the GPU with it stretches the assignment
+so far that the chain assign -> sort -> prepare outlasts the window pass.
+--schedule auto (the default) times a few steps of each after the warm-up
+and keeps the faster; the timed steps then all use it.
 Workloads with m = 2 groups per token use focus_assign_topk, the sort of the
 n*m membership entries and the focus_attn_topk_long_range_* calls instead.
 W untimed warm-up steps, then K timed steps between two device
@@ -56,6 +63,9 @@ def parse():
                     help="target CPU time of the oracle attention sample")
     ap.add_argument("--no-overlap", action="store_true",
                     help="run the window pass on the main stream, after the sort")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "beside", "after_assign"],
+                    help="when the window pass starts on its stream: beside the assignment, "
+                         "or after it; auto picks the faster after the warm-up")
     ap.add_argument("--op", default="attn", choices=["attn", "sinkhorn", "soft_gate"],
                     help="attn: the inference forward step (default); sinkhorn: the "
                          "training-time soft assignment (scores + Sinkhorn rounds); "
@@ -471,6 +481,8 @@ def main():
             focus.focus_attn_topk_long_range_apply(q, k, v, ids, perm, offs, K, m, w, scale,
                                                    workspace=ws_t, out=out)
 
+    schedule = "beside" if args.schedule == "auto" else args.schedule
+
     def step(evs=None):
         stream = torch.cuda.current_stream()   # the capture stream under --graph
         def mark(i, st):
@@ -485,6 +497,8 @@ def main():
             # pass's to retire one by one
             assign()
             mark(1, stream)
+            if schedule == "after_assign":
+                side.wait_stream(stream)
         else:
             assign()
             mark(1, stream)
@@ -509,6 +523,23 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    probe = None
+    if overlap and args.schedule == "auto":
+        # part of the warm-up: a few steps of each schedule, the faster is kept
+        probe = {}
+        for sc in ("beside", "after_assign", "beside", "after_assign"):
+            schedule = sc
+            ts = []
+            for _ in range(5):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                step()
+                torch.cuda.synchronize()
+                ts.append((time.perf_counter() - t0) * 1e3)
+            probe.setdefault(sc, []).extend(ts)
+        probe = {sc: float(np.median(ts)) for sc, ts in probe.items()}
+        schedule = min(probe, key=probe.get)
+        log(f"schedule {schedule} (median ms of 10 steps each: {probe})")
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(NEV)] for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
@@ -603,12 +634,14 @@ def main():
                    else "warm",
                    "launch": "HIP graph of the whole step, replayed" if args.graph else "eager",
                    "streams": "window pass overlapped with assign+sort" if overlap
-                   else "one stream"},
+                   else "one stream",
+                   "schedule": schedule if overlap else None},
         "visited_pairs_per_head": pairs,
         "window_pairs_per_head": win,
         "long_range_pairs_per_head": lr,
         "long_range_pairs_visited_per_head": lr_visited,
         "phase_ms": phase,
+        "schedule_probe_ms": probe,
         "eager_ms_per_step": eager_ms,
         "step_ms_stats": {"median": float(np.median(per_step)), "min": per_step[0],
                           "max": per_step[-1]},
