@@ -688,7 +688,11 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // Work item of this workgroup. The indices are uniform; readfirstlane
     // keeps them (and every address derived from them) in scalar registers.
     const int L = xcd_remap(blockIdx.x, a.total);
+    // Sequence-order passes take their query tiles last to first: the later
+    // tiles have the most keys (causal passes) or the full window, so the
+    // grid's last round is made of the short first tiles (longest first).
     int tile = L % a.ntiles;
+    if (!SORTED) tile = a.ntiles - 1 - tile;
     int rest = L / a.ntiles;
     int slice = rest % a.nslices;
     rest /= a.nslices;
