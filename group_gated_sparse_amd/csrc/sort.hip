@@ -17,7 +17,9 @@
 //                     (exclusive), and every thread replays its tokens in
 //                     order, writing perm[start + rank] = token.
 // Blocks, threads and the tokens of a thread are all visited in token order,
-// so the result is the stable sort, and it is deterministic.
+// so the result is the stable sort, and it is deterministic. A sequence of
+// one block (n <= 2048) needs no counts from other blocks: the scatter pass
+// alone runs, taking the group totals from its own scan.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -66,8 +68,8 @@ __global__ __launch_bounds__(SORT_T) void sort_scatter_kernel(const int32_t* __r
     const int stride = K + 1;
 
     // Group totals of the batch element and the tokens of each group in
-    // earlier blocks.
-    if (t < K) {
+    // earlier blocks (one block: taken from the scan below).
+    if (nblk > 1 && t < K) {
         int all = 0, pre = 0;
         for (int u = 0; u < nblk; ++u) {
             const int c = hb[(int64_t)u * K + t];
@@ -89,6 +91,19 @@ __global__ __launch_bounds__(SORT_T) void sort_scatter_kernel(const int32_t* __r
         if (gid[i] >= 0) my[gid[i]] += 1;
     }
     __syncthreads();
+    if (t < K) {   // exclusive scan down the thread index, per group
+        int run = 0;
+        for (int u = 0; u < SORT_T; ++u) {
+            const int c = cnt[u * stride + t];
+            cnt[u * stride + t] = run;
+            run += c;
+        }
+        if (nblk == 1) {
+            tot[t] = run;
+            before[t] = 0;
+        }
+    }
+    if (nblk == 1) __syncthreads();
     if (t == 0) {  // exclusive scan of the group totals -> group offsets
         int run = 0;
         for (int k = 0; k < K; ++k) {
@@ -97,14 +112,6 @@ __global__ __launch_bounds__(SORT_T) void sort_scatter_kernel(const int32_t* __r
             run += c;
         }
         tot[K] = run;
-    }
-    if (t < K) {   // exclusive scan down the thread index, per group
-        int run = 0;
-        for (int u = 0; u < SORT_T; ++u) {
-            const int c = cnt[u * stride + t];
-            cnt[u * stride + t] = run;
-            run += c;
-        }
     }
     __syncthreads();
     if (blk == 0 && t <= K) offsets[(int64_t)b * (K + 1) + t] = tot[t];
@@ -161,9 +168,11 @@ hipError_t launch_group_sort(const int32_t* ids, int B, int n, int K, int32_t* p
     const int nblk = (n + SORT_BLOCK_TOKENS - 1) / SORT_BLOCK_TOKENS;
     int32_t* hist = static_cast<int32_t*>(workspace);
     const dim3 grid(nblk, B);
-    hipLaunchKernelGGL(sort_hist_kernel, grid, dim3(SORT_T), 0, stream, ids, n, K, nblk, hist);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (nblk > 1) {
+        hipLaunchKernelGGL(sort_hist_kernel, grid, dim3(SORT_T), 0, stream, ids, n, K, nblk, hist);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(sort_scatter_kernel, grid, dim3(SORT_T), 0, stream, ids, n, K, nblk, hist,
                        perm, offsets);
     return hipGetLastError();
