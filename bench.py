@@ -16,7 +16,8 @@ and prepare calls (schedule "after_assign"): where the assignment is short
 next to the window pass, sharing the GPU with it stretches the assignment
 so far that the chain assign -> sort -> prepare outlasts the window pass.
 --schedule auto (the default) times a few steps of each after the warm-up
-and keeps the faster; the timed steps then all use it.
+and keeps the faster; the timed steps then all use it (with --graph the
+replayed graph is chosen the same way, from replays of each).
 Workloads with m = 2 groups per token use focus_assign_topk, the sort of the
 n*m membership entries and the focus_attn_topk_long_range_* calls instead.
 W untimed warm-up steps, then K timed steps between two device
@@ -567,14 +568,38 @@ def main():
         if args.cold_mall:
             raise SystemExit("--graph and --cold-mall are exclusive")
         ref_out = out.clone()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(max(args.warmup, 1)):
-            g.replay()
-        torch.cuda.synchronize()
-        if not torch.equal(out, ref_out):
-            raise RuntimeError("the replayed step differs from the eager step")
+        eager_schedule = schedule
+
+        def capture():
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step()
+            for _ in range(max(args.warmup, 1)):
+                gr.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(out, ref_out):
+                raise RuntimeError("the replayed step differs from the eager step")
+            return gr
+
+        graph_probe = None
+        if overlap and args.schedule == "auto":
+            # the replayed graph may favour another schedule than eager launches:
+            # time a few replays of each and keep the faster
+            graph_probe = {}
+            for sc in ("beside", "after_assign"):
+                schedule = sc
+                gr = capture()
+                pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                pe0.record(stream)
+                for _ in range(10):
+                    gr.replay()
+                pe1.record(stream)
+                torch.cuda.synchronize()
+                graph_probe[sc] = pe0.elapsed_time(pe1) / 10
+                del gr
+            schedule = min(graph_probe, key=graph_probe.get)
+            log(f"graph schedule {schedule} (ms per replay: {graph_probe})")
+        g = capture()
         ge0, ge1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ge0.record(stream)
@@ -586,6 +611,8 @@ def main():
         ms_step = max(g_wall, ge0.elapsed_time(ge1) / args.steps)
         log(f"graph replay: {ms_step:.4f} ms per step (eager {eager_ms:.4f})")
         del g, ref_out
+        graph_schedule = schedule
+        schedule = eager_schedule
     log(f"step {ms_step:.3f} ms (events {ev_step:.3f}, wall {wall_ms:.3f}); phases {phase}")
 
     gids = ids.cpu().numpy()
@@ -635,13 +662,15 @@ def main():
                    "launch": "HIP graph of the whole step, replayed" if args.graph else "eager",
                    "streams": "window pass overlapped with assign+sort" if overlap
                    else "one stream",
-                   "schedule": schedule if overlap else None},
+                   "schedule": schedule if overlap else None,
+                   "graph_schedule": graph_schedule if (overlap and args.graph) else None},
         "visited_pairs_per_head": pairs,
         "window_pairs_per_head": win,
         "long_range_pairs_per_head": lr,
         "long_range_pairs_visited_per_head": lr_visited,
         "phase_ms": phase,
         "schedule_probe_ms": probe,
+        "graph_schedule_probe_ms": graph_probe if args.graph else None,
         "eager_ms_per_step": eager_ms,
         "step_ms_stats": {"median": float(np.median(per_step)), "min": per_step[0],
                           "max": per_step[-1]},
