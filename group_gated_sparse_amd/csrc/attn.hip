@@ -87,6 +87,29 @@ constexpr int kNoPos = 0x7fffffff;      // position of a padding key slot
 enum { kWindow = 0, kLongRange = 1, kDense = 2, kLongMulti = 3, kSoftGate = 4, kLongSets = 7 };
 constexpr bool attn_gated(int PHASE) { return PHASE >= kSoftGate && PHASE < kLongSets; }
 
+// Division by a divisor fixed for the launch (the work decode's tile, slice
+// and head counts): floor(x / d) for any 32-bit x as a multiply-high, an add
+// and two shifts, with the multiplier m = floor(2^32 (2^l - d) / d) + 1,
+// l = ceil(log2 d), computed on the host (division by invariant integers,
+// Granlund and Montgomery, PLDI 1994). d = 1 takes x itself.
+struct FastDiv {
+    uint32_t mul, shr, d;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    FastDiv f{0u, 0u, d};
+    if (d <= 1) return f;
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    f.mul = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+    f.shr = l;
+    return f;
+}
+__device__ __forceinline__ uint32_t fast_div(uint32_t x, const FastDiv& f) {
+    if (f.d <= 1) return x;
+    const uint32_t t = __umulhi(x, f.mul);
+    return (t + ((x - t) >> 1)) >> (f.shr - 1);
+}
+
 struct AttnArgs {
     const uint16_t* q;
     const uint16_t* k;      // sequence order (window / dense) or sorted copy (long-range)
@@ -117,6 +140,7 @@ struct AttnArgs {
     int tt_log;    // log2(TT)
     int nslices;   // hpk / G
     int ntiles;    // ceil(n / TT): query tiles (of one launch)
+    FastDiv fd_ntiles, fd_nslices, fd_hkv;   // the work decode's divisors
     int total;     // workgroups
     float sl2;     // scale * log2(e)
     const uint16_t* gs;   // soft-gated pass: bf16 hi/lo split of the soft assignments,
@@ -691,13 +715,14 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // Sequence-order passes take their query tiles last to first: the later
     // tiles have the most keys (causal passes) or the full window, so the
     // grid's last round is made of the short first tiles (longest first).
-    int tile = L % a.ntiles;
+    const uint32_t q1 = fast_div((uint32_t)L, a.fd_ntiles);
+    const uint32_t q2 = fast_div(q1, a.fd_nslices);
+    const uint32_t q3 = fast_div(q2, a.fd_hkv);
+    int tile = (int)((uint32_t)L - q1 * (uint32_t)a.ntiles);
     if (!SORTED) tile = a.ntiles - 1 - tile;
-    int rest = L / a.ntiles;
-    int slice = rest % a.nslices;
-    rest /= a.nslices;
-    int kvh = rest % a.Hkv;
-    int b = rest / a.Hkv;
+    int slice = (int)(q1 - q2 * (uint32_t)a.nslices);
+    int kvh = (int)(q2 - q3 * (uint32_t)a.Hkv);
+    int b = (int)q3;
     slice = __builtin_amdgcn_readfirstlane(slice);
     kvh = __builtin_amdgcn_readfirstlane(kvh);
     b = __builtin_amdgcn_readfirstlane(b);
@@ -1469,6 +1494,15 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             return rs < HROWS ? buf0 + rs * RB : buf1 + (rs - HROWS) * RB;
         };
         char* dst = KIND == 0 ? reinterpret_cast<char*>(a.og_dst) : static_cast<char*>(a.out);
+        // Stores: each thread writes one fixed 16-byte chunk c of every
+        // RSTEP-th staged row. Row r of the tile is token (or entry) slot
+        // r & (TT-1) of head slot r >> tt_log; the head's rows start at
+        // dbase + (r >> tt_log) * n * RB.
+        constexpr int RSTEP = NT / NCHK;
+        const int c_t = tid % NCHK, rs_t = tid / NCHK;
+        const int64_t hstride = (int64_t)a.n * RB;
+        char* const dbase =
+            dst + ((int64_t)b * a.Hq + kvh * a.hpk + slice * a.G) * hstride + c_t * 16;
 #pragma unroll
         for (int r0 = 0; r0 < ROWS; r0 += RPP) {
             // K/V buffers (or the previous pass) are free
@@ -1501,21 +1535,21 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     }
             }
             __syncthreads();
+            static_assert(RPP % RSTEP == 0, "whole store rounds");
 #pragma unroll
-            for (int idx0 = 0; idx0 < RPP * NCHK; idx0 += NT) {
-                const int idx = idx0 + tid;
-                if (RPP * NCHK % NT != 0 && idx >= RPP * NCHK) break;
-                const int rs = idx / NCHK, c = idx % NCHK;
+            for (int k = 0; k < RPP / RSTEP; ++k) {
+                const int rs = rs_t + k * RSTEP;
                 const int r = r0 + rs;
                 const int tk = r & (a.TT - 1);
                 if (qs0 + tk >= qs1) continue;   // rows past the sequence end
-                int hr, pr;
-                row_of(r, hr, pr);
-                u32x4 val = *reinterpret_cast<const u32x4*>(stage(rs) + ((c ^ (rs & CMASK)) << 4));
+                // the row's position (sorted passes: from its entry; entry passes: entry / 2)
+                int pr = qs0 + tk;
+                if (SORTED) pr = MULTI ? rowpos[r] >> 1 : rowpos[r];
+                u32x4 val =
+                    *reinterpret_cast<const u32x4*>(stage(rs) + ((c_t ^ (rs & CMASK)) << 4));
                 if (ESZ == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
-                // the row's token (entry passes: entry / 2)
-                const int64_t orow = ((int64_t)b * a.Hq + hr) * a.n + (MULTI ? pr >> 1 : pr);
-                *reinterpret_cast<u32x4*>(dst + orow * RB + c * 16) = val;
+                *reinterpret_cast<u32x4*>(dbase + (int64_t)(r >> a.tt_log) * hstride +
+                                          (int64_t)pr * RB) = val;
             }
         }
     };
@@ -1571,6 +1605,9 @@ AttnArgs make_args(const AttnProblem& p) {
     a.ne = p.n;
     a.ntiles = (p.n + a.TT - 1) / a.TT;
     a.total = p.B * p.Hkv * a.nslices * a.ntiles;
+    a.fd_ntiles = make_fastdiv((uint32_t)a.ntiles);
+    a.fd_nslices = make_fastdiv((uint32_t)a.nslices);
+    a.fd_hkv = make_fastdiv((uint32_t)p.Hkv);
     a.sl2 = p.scale * 1.44269504088896340736f;
     a.out_f32 = p.out_f32;
     if (p.workspace) {
