@@ -164,7 +164,9 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
     const int NSTG = (NS + 3) / 4;
 
     // Copies of a stage: wave w copies rows 8w .. 8w+7, one 1 KB run each;
-    // lane l fills slot l of the row, i.e. logical chunk l ^ (row & 15).
+    // lane l fills slot l of the row, i.e. logical chunk l ^ (row & 15). The
+    // hidden states are read once, so the copies are non-temporal (cache
+    // policy nt), which leaves the caches to W and lifts the read rate.
     auto issue = [&](int st, unsigned char* dst, WRegs<NB>& wr) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void assign_argmax_kernel(
             const int d = min(256 * st + 4 * c, d_model - 4);  // past d_model: W^T is zero there
             __builtin_amdgcn_global_load_lds(hidden + trow * d_model + d,
                                              (__attribute__((address_space(3))) void*)(dst + r * HROWB),
-                                             16, 0, 0);
+                                             16, 0, 2);
         }
         const int s = min(4 * st + wave, NS - 1);
 #pragma unroll
