@@ -1080,11 +1080,13 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         for (int part = 0; part < 2; ++part)
             goff[ks][part] = rl * GROWB + (((part * KG / 8) + 2 * ks + hh) ^ gswz<GNCH>(rl)) * 16;
 
-    f32x16 acc[G::DB];
+    f32x16 acc[G::DB];   // the sorted passes set it from the partial they merge
+    if constexpr (!SORTED) {
 #pragma unroll
-    for (int db = 0; db < G::DB; ++db)
+        for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
+            for (int e = 0; e < 16; ++e) acc[db][e] = 0.0f;
+    }
     // l_run: sum of the fp32 probabilities (log-sum-exp); l_pv: sum of the
     // bf16-rounded probabilities the PV MFMAs multiply (output normaliser)
     float m_ref = kNegInf, l_run = 0.0f, l_pv = 0.0f;
@@ -1333,13 +1335,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     // log2-sum-exp L and e; (acc = O~, l = 2^-e, reference max = L + e) is
     // exactly the state that result stands for, so this pass's keys
     // accumulate on top of it and the final normalisation merges both parts.
-    // The sorted passes load the partial rows whatever (L, e) holds (the
-    // window pass writes every row), so their round trip overlaps that of
-    // (L, e), the Q rows and the first K/V tile, and take them into the
-    // state once the loads are back. (The window pass never merges, but
-    // keeping the plain form of this code in it gives it a far better
-    // register allocation at three workgroups per CU.)
-    const bool merging = !CAUSAL_ALL && a.merge && rvalid;
+    // The sorted passes always merge (every row; rows past the end take a
+    // valid row's partial, never stored): they load the partial rows whatever
+    // (L, e) holds (the window pass writes every row, zeros with L = -inf for
+    // a row without keys, which is then the empty state), so their round trip
+    // overlaps that of (L, e), the Q rows and the first K/V tile, and they
+    // take them into the state once the loads are back; their accumulator
+    // needs no zeroing. (The window pass never merges, but keeping the plain
+    // form of this code in it gives it a far better register allocation at
+    // three workgroups per CU.)
+    const bool merging = SORTED || (!CAUSAL_ALL && a.merge && rvalid);
     f32x2 le_in = {kNegInf, 0.0f};
     f16x4 part_in[G::DB][4];
     auto set_state = [&](int db, int i, f16x4 gv) {
@@ -1373,7 +1378,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         }
     }
     auto take_partial = [&]() {
-        if (SORTED && merging && le_in[0] != kNegInf) {
+        if constexpr (SORTED) {
 #pragma unroll
             for (int db = 0; db < G::DB; ++db)
 #pragma unroll
