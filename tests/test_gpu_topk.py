@@ -129,6 +129,9 @@ TOPK_CASES = [
     ("many_tiles", 2, 3, 3, 1100, 64, 9, 2, 100),
     ("k4_long_d128", 1, 8, 8, 2000, 128, 4, 2, 64),
     ("m1", 1, 4, 2, 300, 64, 5, 1, 20),
+    # the entry passes (K >= 5) at d = 32 (64-key tiles) with a ragged second half, and at w = 0
+    ("entries_d32_ragged", 1, 4, 2, 150, 32, 6, 2, 9),
+    ("entries_w0_b2", 2, 4, 4, 260, 64, 12, 2, 0),
 ]
 
 
@@ -210,6 +213,33 @@ def test_topk_two_calls_equal_one():
                                            workspace=ws, out=two, lse=lse2, stream=main)
     torch.cuda.synchronize()
     assert torch.equal(one, two) and torch.equal(lse1, lse2)
+
+
+@pytest.mark.parametrize("K", [4, 6], ids=["set_pass", "entry_passes"])
+def test_topk_apply_repeats_on_one_window_partial(K):
+    """The long-range calls only read the window partial: merging twice from
+    one window pass gives the same result twice, equal to focus_attn_topk_fwd
+    (both long-range forms)."""
+    say(f"[attn top-k] apply twice, K={K}")
+    rng = np.random.default_rng(40 + K)
+    B, Hq, Hkv, n, d, m, w = 1, 4, 2, 700, 64, 2, 30
+    q, k, v = _qkv(rng, B, Hq, Hkv, n, d)
+    ids = _member_ids(rng, B, n, K, m)
+    tq, tk, tv, tid = dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(ids)
+    perm, offs = focus.focus_group_sort(tid, K)
+    one, lse1 = focus.focus_attn_topk_fwd(tq, tk, tv, tid, perm, offs, K, m, w, 0.125,
+                                          out_dtype=torch.float32, want_lse=True)
+    ws = torch.empty(focus.focus_attn_topk_workspace_bytes(B, Hq, Hkv, n, d, K, m, w),
+                     dtype=torch.uint8, device="cuda")
+    outs = [torch.empty_like(one) for _ in range(2)]
+    lses = [torch.empty_like(lse1) for _ in range(2)]
+    focus.focus_attn_window(tq, tk, tv, K, w, 0.125, workspace=ws, out=outs[0], lse=lses[0])
+    for o, l in zip(outs, lses):
+        focus.focus_attn_topk_long_range_merge(tq, tk, tv, tid, perm, offs, K, m, w, 0.125,
+                                               workspace=ws, out=o, lse=l)
+    torch.cuda.synchronize()
+    for o, l in zip(outs, lses):
+        assert torch.equal(o, one) and torch.equal(l, lse1)
 
 
 def test_topk_three_calls_equal_one():
