@@ -961,6 +961,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         make_rsrc(kbase, direct ? (uint32_t)a.n * G::ROWB : 0u);
     const __amdgpu_buffer_rsrc_t vrs_head =
         make_rsrc(vbase, direct ? (uint32_t)a.n * G::ROWB : 0u);
+    // The positions come through a buffer resource over the batch element's
+    // perm row (scalar base; a read past its size returns 0, a valid row).
+    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.perm + bne, direct ? (uint32_t)ne * 4 : 0u);
     auto prefetch = [&](int tau) {
         int kt0, kend;
         bool full;
@@ -969,7 +972,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         for (int i = 0; i < G::NI; ++i) {
             // rows past the segment's valid slots take its last valid slot (masked)
             const int slot = min(kt0 + (int)(lane_off[i] / G::ROWB), kend - 1);
-            pnext[i] = a.perm[bne + clampi(slot, 0, ne - 1)];
+            pnext[i] = __builtin_amdgcn_raw_buffer_load_b32(prs, (uint32_t)slot * 4u, 0, 0);
         }
     };
     // the first key tile's positions: from the packed record when the plan
