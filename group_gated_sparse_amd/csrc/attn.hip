@@ -1150,7 +1150,22 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         // 8*(e>>2) + 4*hh + (e&3) of its row, i.e. key kt0 + 4*hh + c with a
         // compile-time c; each test is one subtraction or compare against c.
         // (branch-free: every condition is evaluated, combined with &)
-        if (!full) {
+        // Entry passes: a tile whose keys every row keeps by position (below
+        // the segment's kfull, rows of one group) needs only the pair rule,
+        // one compare per key against the row's excluded group.
+        const bool excl_only = MULTI && rows_one_group && (kt0 + BN <= seg_cur.kfull);
+        if (!full && excl_only) {
+#pragma unroll
+            for (int kb = 0; kb < G::KB; ++kb)
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const int4 kp = *reinterpret_cast<const int4*>(kposp + kb * 32 + 8 * e4 + 4 * hh);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        st[kb][4 * e4 + j] =
+                            (kp[j] & 63) != x_i ? st[kb][4 * e4 + j] : kNegInf;
+                }
+        } else if (!full) {
             const bool row_ok = !SORTED || SETS || g_i == gfirst + seg_cur.seg;
             // sequence-order passes: kept keys are those with 0 <= pos_i - key
             // <= w (keys past the last row then fail too: pos_i < kend for
