@@ -1232,13 +1232,22 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                         at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ghi, gq[ks][1], at, 0, 0, 0);
                         at = __builtin_amdgcn_mfma_f32_32x32x16_bf16(glo, gq[ks][0], at, 0, 0, 0);
                     }
+                    if (all_far) {   // the common case: every pair of the tile is far
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int key = kt0 + kb * 32 + 8 * (e >> 2) + 4 * hh + (e & 3);
-                        const bool far = all_far || (pos_i - key > a.w);
-                        gate[kb][e] = far ? __builtin_amdgcn_rcpf(
-                                                1.0f + __builtin_amdgcn_exp2f(at[e] * a.nl2))
-                                          : 1.0f;
+                        for (int e = 0; e < 16; ++e)
+                            gate[kb][e] = __builtin_amdgcn_rcpf(
+                                1.0f + __builtin_amdgcn_exp2f(at[e] * a.nl2));
+                    } else {
+                        // pos_i - key = dpos - c with a compile-time c per slot
+                        const int dpos = pos_i - kt0 - kb * 32 - 4 * hh;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int c = 8 * (e >> 2) + (e & 3);
+                            gate[kb][e] = dpos - c > a.w
+                                              ? __builtin_amdgcn_rcpf(
+                                                    1.0f + __builtin_amdgcn_exp2f(at[e] * a.nl2))
+                                              : 1.0f;
+                        }
                     }
                 }
             }
