@@ -1207,7 +1207,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         // window, the group affinity a = g_key . g_row of every pair comes
         // from three MFMAs on the bf16 hi/lo split (hi*hi + hi*lo + lo*hi),
         // and far pairs get the gate sigmoid(lambda a) = 1 / (1 + 2^(-lambda
-        // log2(e) a)); pairs inside the window keep gate 1.
+        // log2(e) a)), the row side's fragments carrying the factor -lambda
+        // log2(e); pairs inside the window keep gate 1.
         float gate[G::KB][16];
         bool gated_tile = false;
         if constexpr (GATED) {
@@ -1235,8 +1236,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     if (all_far) {   // the common case: every pair of the tile is far
 #pragma unroll
                         for (int e = 0; e < 16; ++e)
-                            gate[kb][e] = __builtin_amdgcn_rcpf(
-                                1.0f + __builtin_amdgcn_exp2f(at[e] * a.nl2));
+                            gate[kb][e] = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(at[e]));
                     } else {
                         // pos_i - key = dpos - c with a compile-time c per slot
                         const int dpos = pos_i - kt0 - kb * 32 - 4 * hh;
@@ -1245,7 +1245,7 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                             const int c = 8 * (e >> 2) + (e & 3);
                             gate[kb][e] = dpos - c > a.w
                                               ? __builtin_amdgcn_rcpf(
-                                                    1.0f + __builtin_amdgcn_exp2f(at[e] * a.nl2))
+                                                    1.0f + __builtin_amdgcn_exp2f(at[e]))
                                               : 1.0f;
                         }
                     }
@@ -1453,14 +1453,23 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
     }
 
     if constexpr (GATED) {
-        // the row's assignment fragments: columns 16*ks + 8*hh .. +8 of hi and lo
+        // the row's assignment fragments: columns 16*ks + 8*hh .. +8 of hi and
+        // lo, scaled by -lambda log2(e) and split again (hi = bf16 of the
+        // scaled value, lo = bf16 of the rest), so the affinity MFMAs return
+        // the gate's exponent directly
         const uint16_t* gr = a.gs + ((int64_t)b * a.n + pos_i) * 2 * KG;
 #pragma unroll
-        for (int ks = 0; ks < KG / 16; ++ks)
+        for (int ks = 0; ks < KG / 16; ++ks) {
+            const bf16x8 hi = *reinterpret_cast<const bf16x8*>(gr + 16 * ks + 8 * hh);
+            const bf16x8 lo = *reinterpret_cast<const bf16x8*>(gr + KG + 16 * ks + 8 * hh);
 #pragma unroll
-            for (int part = 0; part < 2; ++part)
-                gq[ks][part] =
-                    *reinterpret_cast<const bf16x8*>(gr + part * KG + 16 * ks + 8 * hh);
+            for (int j = 0; j < 8; ++j) {
+                const float g = ((float)hi[j] + (float)lo[j]) * a.nl2;
+                const __bf16 gh = (__bf16)g;
+                gq[ks][0][j] = gh;
+                gq[ks][1][j] = (__bf16)(g - (float)gh);
+            }
+        }
     }
 
     take_partial();
