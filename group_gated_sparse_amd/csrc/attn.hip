@@ -781,6 +781,16 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         prec = *reinterpret_cast<const i32x4*>(a.plan + ((int64_t)pbi * a.ntiles + tile) * PLAN_INTS +
                                               4 * (lane & 7));
     const int pos_i = MULTI ? (ent_i >> 1) : ent_i;
+    // Sequence-order passes: the positions of the wave's valid rows form one
+    // run [wpmin, wpmax] (32 consecutive tokens of the tile, or all TT
+    // tokens when the wave spans several heads), so whether the wave keeps
+    // any key of a tile is a scalar test.
+    int wpmin = 0, wpmax = -1;
+    if constexpr (!SORTED) {
+        const int w0 = a.TT >= 32 ? ((__builtin_amdgcn_readfirstlane(wave) * 32) & (a.TT - 1)) : 0;
+        wpmin = qs0 + w0;
+        wpmax = min(qs1 - 1, qs0 + w0 + min(32, a.TT) - 1);
+    }
     // multi pass: the row token's other group
     const int oth_i = (MULTI && rvalid) ? clampi(a.ids[bne + (ent_i ^ 1)], 0, a.K - 1) : 0;
     // set pass: the row token's group mask (a key is kept when it shares one)
@@ -1109,7 +1119,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         {
             bool needs;
             if (!SORTED) {
-                needs = rvalid && kt0 <= pos_i && (CAUSAL_ALL || kt0 + BN - 1 >= pos_i - a.w);
+                if (!(wpmin <= wpmax && kt0 <= wpmax && (CAUSAL_ALL || kt0 + BN - 1 + a.w >= wpmin)))
+                    return;
+                needs = true;
             } else if (SETS) {
                 // the segment's set shares a group with the row's
                 needs = rvalid && (gmask_i & (a.set_lut >> (4 * seg_cur.seg))) != 0;
@@ -1275,17 +1287,22 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     if constexpr (GATED) {
                         if (gated_tile) p *= gate[kb][e];
                     }
-                    ps2[e & 1] += p;
+                    if (kb == 0 && e < 2) {
+                        ps2[e] = p;   // no add to zero (it is not folded: -0 + 0 = +0)
+                    } else {
+                        ps2[e & 1] += p;
+                    }
                     pf[kb][e >> 3][e & 7] = (__bf16)p;
                 }
             psum = ps2[0] + ps2[1];
         };
-        bool need = m_ref == kNegInf;
-        if (!__any(need)) {
+        // (the tests are wave-wide: the decision stays in scalar registers)
+        bool redo = __any(m_ref == kNegInf);
+        if (!redo) {
             probs(m_ref);
-            need = psum > kProbSumCap;
+            redo = __any(psum > kProbSumCap);
         }
-        if (__any(need)) {
+        if (redo) {
             float tmax = kNegInf;
 #pragma unroll
             for (int kb = 0; kb < G::KB; ++kb)
