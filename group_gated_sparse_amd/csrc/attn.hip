@@ -971,19 +971,20 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         make_rsrc(kbase, direct ? (uint32_t)a.n * G::ROWB : 0u);
     const __amdgpu_buffer_rsrc_t vrs_head =
         make_rsrc(vbase, direct ? (uint32_t)a.n * G::ROWB : 0u);
-    // The positions come through a buffer resource over the batch element's
-    // perm row (scalar base; a read past its size returns 0, a valid row).
-    const __amdgpu_buffer_rsrc_t prs = make_rsrc(a.perm + bne, direct ? (uint32_t)ne * 4 : 0u);
+    // The positions come through a buffer resource over the tile's valid
+    // slots of the batch element's perm row (scalar base and size, built per
+    // tile), so each lane's read is a fixed 32-bit offset; a slot past the
+    // segment's valid end reads 0, a valid row, which the mask drops.
     auto prefetch = [&](int tau) {
         int kt0, kend;
         bool full;
         locate(tau, seg_pref, kt0, kend, full);
+        const int s0 = min(max(kt0, 0), kend);
+        const __amdgpu_buffer_rsrc_t prs =
+            make_rsrc(a.perm + bne + s0, direct ? (uint32_t)(kend - s0) * 4u : 0u);
 #pragma unroll
-        for (int i = 0; i < G::NI; ++i) {
-            // rows past the segment's valid slots take its last valid slot (masked)
-            const int slot = min(kt0 + (int)(lane_off[i] / G::ROWB), kend - 1);
-            pnext[i] = __builtin_amdgcn_raw_buffer_load_b32(prs, (uint32_t)slot * 4u, 0, 0);
-        }
+        for (int i = 0; i < G::NI; ++i)
+            pnext[i] = __builtin_amdgcn_raw_buffer_load_b32(prs, (lane_off[i] / G::ROWB) * 4u, 0, 0);
     };
     // the first key tile's positions: from the packed record when the plan
     // record holds the segments (otherwise the kernel derived them itself)
@@ -1022,8 +1023,8 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         if (direct) {
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
-                const uint32_t vo = (uint32_t)clampi(pnext[i], 0, a.n - 1) * G::ROWB +
-                                    lane_off[i] % G::ROWB;
+                // a position outside [0, n) reads past the resource: zeros, no fault
+                const uint32_t vo = (uint32_t)pnext[i] * G::ROWB + lane_off[i] % G::ROWB;
                 copy16_buf(krs_head, vo, 0, dst + i * 1024);
                 copy16_buf(vrs_head, vo, 0, dst + G::TILEB + i * 1024);
             }
