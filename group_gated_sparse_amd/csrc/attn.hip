@@ -909,6 +909,15 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
             rows_excl = __builtin_amdgcn_readfirstlane(excl_any) != 0;
         }
     }
+    // Set pass: the groups the wave's valid rows hold, a scalar bit mask
+    // taken once per work item, so that the per-tile test of whether the
+    // wave keeps any key of a segment is scalar.
+    uint32_t wave_groups = 0;
+    if constexpr (SETS) {
+#pragma unroll
+        for (int bit = 0; bit < 4; ++bit)
+            if (__any(rvalid && ((gmask_i >> bit) & 1))) wave_groups |= 1u << bit;
+    }
 
     // Sorted passes: a cursor over the segments, with the current segment's
     // values held in scalar registers (first and end tile, first key slot,
@@ -1124,8 +1133,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                     return;
                 needs = true;
             } else if (SETS) {
-                // the segment's set shares a group with the row's
-                needs = rvalid && (gmask_i & (a.set_lut >> (4 * seg_cur.seg))) != 0;
+                // the segment's set shares a group with one of the wave's rows
+                if ((wave_groups & (uint32_t)(a.set_lut >> (4 * seg_cur.seg)) & 15u) == 0) return;
+                needs = true;
             } else if (!MULTI) {
                 needs = rvalid && g_i == gfirst + seg_cur.seg && kt0 < kend_row;
             } else {
