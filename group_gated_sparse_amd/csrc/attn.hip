@@ -1617,8 +1617,10 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
                 u32x4 val =
                     *reinterpret_cast<const u32x4*>(stage(rs) + ((c_t ^ (rs & CMASK)) << 4));
                 if (ESZ == 2 && ((rs >> 4) & 1)) val = __builtin_shufflevector(val, val, 2, 3, 0, 1);
-                *reinterpret_cast<u32x4*>(dbase + (int64_t)(r >> a.tt_log) * hstride +
-                                          (int64_t)pr * RB) = val;
+                // non-temporal: written once, read (if at all) by a later pass
+                __builtin_nontemporal_store(
+                    val, reinterpret_cast<u32x4*>(dbase + (int64_t)(r >> a.tt_log) * hstride +
+                                                  (int64_t)pr * RB));
             }
         }
     };
