@@ -1032,7 +1032,9 @@ __global__ __launch_bounds__(NT, attn_occupancy(D, PHASE)) void attn_kernel(Attn
         if (direct) {
 #pragma unroll
             for (int i = 0; i < G::NI; ++i) {
-                // a position outside [0, n) reads past the resource: zeros, no fault
+                // no clamp: the offset is 32-bit and the resource spans the
+                // head's n rows, so no position reads outside them (one
+                // outside [0, n) reads zeros, or another row if it wraps)
                 const uint32_t vo = (uint32_t)pnext[i] * G::ROWB + lane_off[i] % G::ROWB;
                 copy16_buf(krs_head, vo, 0, dst + i * 1024);
                 copy16_buf(vrs_head, vo, 0, dst + G::TILEB + i * 1024);
